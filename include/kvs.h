@@ -1,0 +1,214 @@
+/*
+ * kvs.h - C ABI of libkvs: the KV-sparsity prefill-and-compress path on MI355X (gfx950).
+ *
+ * Sources, cited by page title and section:
+ *   [KVS] Novita AI, "How KV Sparsity Achieves 1.5x Acceleration for vLLM" (blog post).
+ *   [PAG] Ultralytics glossary, "PagedAttention".
+ *
+ * The path, per layer and batch of prompts:
+ *   kvs_prefill_attn_lse  causal attention that also returns each row's log-sum-exp
+ *   kvs_window_score      the observation-window score S per KV head, rebuilt from that LSE
+ *   kvs_topk_select       the kept token indices per KV head
+ *   kvs_compact_paged     copy of the kept K/V rows into 16-token blocks through block tables
+ *   kvs_paged_decode      attention of one new token per sequence over the paged cache
+ * plus a host block allocator (free list, reference counts, copy-on-write) and the
+ * device block copy that copy-on-write needs.
+ *
+ * Conventions shared by every call
+ *   - Return value: KVS_OK (0) or a negative KVS_E_* code; kvs_last_error() gives a
+ *     message for the calling thread.  Scalar arguments are checked on the host before
+ *     anything is launched; a failed check launches nothing.
+ *   - Pointers named *_dev / the tensors below are DEVICE pointers, owned by the caller
+ *     (the library never allocates device memory and never frees a caller's buffer).
+ *     Device integer arrays (cu_seqlens, keep_offsets, keep_idx, block tables, ctx_lens,
+ *     slot offsets, copy pairs) are trusted: the host does not read them back.  Kernels
+ *     skip any pool access whose block id lies outside [0, num_blocks).
+ *   - bf16 tensors are passed as void* (IEEE bfloat16, 2 bytes); fp32 as float*; indices
+ *     and tables as int32_t*.
+ *   - Every device call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream).  No call synchronises the host with the device.
+ *   - Shapes: head_dim d in {64, 128}; hq % hkv == 0 and G = hq / hkv <= 16; query head h
+ *     reads KV head h / G.  The block size is fixed at KVS_BLOCK_SIZE = 16 tokens.
+ *   - Token-major ragged batches: prompt s owns tokens [cu_seqlens[s], cu_seqlens[s+1]) of
+ *     Q [total][hq][d] and K, V [total][hkv][d]; indices inside a prompt are 0-based.
+ *   - Thread safety: device calls may be made from any thread; an allocator object must
+ *     not be used by two threads at once.
+ */
+#ifndef KVS_H_
+#define KVS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVS_BLOCK_SIZE 16
+
+enum {
+  KVS_OK = 0,
+  KVS_E_INVAL = -1,    /* bad shape or argument; nothing launched            */
+  KVS_E_NOBLOCKS = -2, /* allocator: no free block                           */
+  KVS_E_STATE = -3,    /* allocator: reference count misuse                  */
+  KVS_E_HIP = -4       /* a HIP launch or runtime call failed                */
+};
+
+/* Message of the last failure on the calling thread ("" if none). */
+const char* kvs_last_error(void);
+/* Library version string. */
+const char* kvs_version(void);
+
+/*
+ * kvs_prefill_attn_lse - causal attention over every prompt, with the row statistics
+ * FlashAttention computes but does not return.
+ *   [KVS] Key techniques, 2. "Attention modification": FlashAttention2 (first Fig. 7)
+ *   walks Q in chunks over KV blocks, carrying O, P and the row maximum and dividing by
+ *   l at the end; rowmax and l are computed but not returned, and the modification
+ *   (second Fig. 7) outputs them at negligible cost.
+ * Computes, for every prompt s, query head h and row j < n_s, with s_ji = scale*<q_j,k_i>
+ * for i <= j:  m_j = max_i s_ji,  l_j = sum_i exp(s_ji - m_j),
+ *              O_j = sum_i exp(s_ji - m_j) v_i / l_j,  lse_j = m_j + ln(l_j).
+ * In:  q [total][hq][d], k, v [total][hkv][d] bf16; cu_seqlens [num_seqs+1] int32 (device).
+ *      max_seqlen >= every n_s; total_tokens = cu_seqlens[num_seqs]; scale > 0 (1/sqrt(d)).
+ * Out: o [total][hq][d] bf16 (round to nearest even); lse [hq][total_tokens] fp32 natural
+ *      log; rowmax_opt, ell_opt [hq][total_tokens] fp32 (m_j and l_j; NULL to skip).
+ * Errors: KVS_E_INVAL on a bad shape, KVS_E_HIP if the launch fails.
+ */
+int kvs_prefill_attn_lse(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                         int num_seqs, int total_tokens, int max_seqlen, int hq, int hkv, int d,
+                         float scale, void* o, float* lse, float* rowmax_opt, float* ell_opt,
+                         void* stream);
+
+/*
+ * kvs_window_score - the observation-window score, rebuilt from the saved LSE.
+ *   [KVS] Key techniques, 2. "Attention modification": the last alpha prompt tokens are
+ *   the window; a token's score is the sum of its softmax values over the window rows,
+ *   p = exp(qk - rowmax)/l from the saved statistics, summed row-wise; the loop order is
+ *   swapped to k.q so the sum stays in registers, and the causal mask plus the window
+ *   bound limit the work to the window rows (second Fig. 7).
+ * Computes, with a = min(alpha, n_s) and G = hq / hkv:
+ *   S[g][i] = sum_{h: h/G = g} sum_{j = max(i, n_s - a)}^{n_s - 1} exp(scale*<q_hj, k_gi> - lse[h][j])
+ * In:  q, k as in prefill (only the last a rows of q are read); lse [hq][total_tokens].
+ * Out: scores [hkv][total_tokens] fp32 (indexed by the prompt's global token position).
+ * Errors: KVS_E_INVAL if alpha < 1 or on a bad shape; KVS_E_HIP on launch failure.
+ */
+int kvs_window_score(const void* q, const void* k, const float* lse, const int32_t* cu_seqlens,
+                     int num_seqs, int total_tokens, int max_seqlen, int alpha, int hq, int hkv,
+                     int d, float scale, float* scores, void* stream);
+
+/*
+ * kvs_topk_select - the tokens each KV head keeps, per prompt.
+ *   [KVS] Key techniques, 2. "Attention modification": in every layer and head the k_l
+ *   highest-scoring tokens are kept and the rest dropped for the whole generation;
+ *   [KVS] System model: pairs with a high score and greater proximity are kept.
+ * Rule: with a = min(alpha, n_s): if k_budget >= n_s keep all n_s tokens; otherwise keep
+ * the window {n_s-a .. n_s-1} plus the k_budget - a highest S among tokens i < n_s - a,
+ * equal scores going to the lower index.  Indices are written in ascending order.
+ * In:  scores [hkv][total_tokens] fp32, every value >= +0 and not NaN (as the window score
+ *      produces); keep_offsets [num_seqs+1] int32 (device), keep_offsets[s] =
+ *      sum_{s'<s} min(k_budget, n_s').
+ * Out: keep_idx int32: prompt s, head g, rank t at keep_idx[hkv*keep_offsets[s] +
+ *      g*k_eff_s + t], k_eff_s = min(k_budget, n_s); values are prompt-local indices.
+ * Errors: KVS_E_INVAL if k_budget < alpha or alpha < 1; KVS_E_HIP on launch failure.
+ */
+int kvs_topk_select(const float* scores, const int32_t* cu_seqlens, int num_seqs, int total_tokens,
+                    int max_seqlen, int hkv, int alpha, int k_budget, const int32_t* keep_offsets,
+                    int32_t* keep_idx, void* stream);
+
+/*
+ * kvs_compact_paged - write kept K/V rows into 16-token blocks through block tables.
+ *   [PAG] "How paging works": the cache lives in fixed 16-token blocks anywhere in GPU
+ *   memory; a per-request block table records their order, and token p goes to block
+ *   table[p / 16], slot p % 16.  [KVS] Key techniques 1: the first layers keep a full
+ *   cache (keep_idx == NULL writes every token).
+ * For prompt s, head g, rank t < k_eff_s and p = dst_slot_offset[s] + t (0 if NULL):
+ *   k_pool[table_s[p/16]][g][p%16][:] = k_src[cu_seqlens[s] + keep(g, t)][g][:]
+ *   v_pool[table_s[p/16]][g][:][p%16] = v_src[cu_seqlens[s] + keep(g, t)][g][:]
+ * keep(g, t) = keep_idx as laid out by kvs_topk_select, or t when keep_idx is NULL (then
+ * k_eff_s = n_s and keep_offsets is ignored).  Slots outside [off, off + k_eff) are not
+ * written, so a partially filled first block keeps its earlier slots.
+ * Pool layouts: k_pool [num_blocks][hkv][16][d], v_pool [num_blocks][hkv][d][16] bf16.
+ * block_tables [num_seqs][max_blocks] int32; max_keep >= every k_eff_s.
+ * Errors: KVS_E_INVAL on a bad shape; KVS_E_HIP on launch failure.  Source and pools must
+ * not overlap.
+ */
+int kvs_compact_paged(const void* k_src, const void* v_src, const int32_t* cu_seqlens,
+                      int num_seqs, int hkv, int d, const int32_t* keep_idx,
+                      const int32_t* keep_offsets, int max_keep, void* k_pool, void* v_pool,
+                      int num_blocks, const int32_t* block_tables, int max_blocks,
+                      const int32_t* dst_slot_offset, void* stream);
+
+/*
+ * kvs_paged_decode - attention of one new token per sequence over its paged cache.
+ *   [PAG] "How paging works": the attention kernel follows the request's block table to
+ *   read keys and values block by block.  [KVS] Key techniques, 2: PagedAttention does
+ *   the decode side of the same computation over the compressed cache.
+ * For sequence b with L = ctx_lens[b] >= 1 (the new token included) and query head h:
+ *   o[b][h] = sum_{t<L} softmax_t(scale*<q_bh, K_t>) V_t,  K_t/V_t read through table_b.
+ * If new_k and new_v are not NULL, they are first stored at slot L-1 (block
+ * table_b[(L-1)/16] must already be allocated) and the token attends to itself.
+ * In:  q [batch][hq][d] bf16; new_k, new_v [batch][hkv][d] bf16 or NULL; pools and tables
+ *      as in kvs_compact_paged; max_ctx >= every L.
+ * Out: o [batch][hq][d] bf16; lse_opt [batch][hq] fp32 (natural log) or NULL.
+ * Workspace: a device buffer of at least kvs_paged_decode_workspace_size(batch, hq, hkv, d,
+ * max_ctx) bytes for split partial results (may be NULL when that size is 0).  The
+ * context is split so that about 2048 workgroups run; partial (max, sum, output) triples
+ * are merged by a second kernel.
+ * Errors: KVS_E_INVAL on a bad shape or a short workspace; KVS_E_HIP on launch failure.
+ */
+size_t kvs_paged_decode_workspace_size(int batch, int hq, int hkv, int d, int max_ctx);
+int kvs_paged_decode(const void* q, void* k_pool, void* v_pool, int num_blocks,
+                     const int32_t* block_tables, int max_blocks, const int32_t* ctx_lens,
+                     int batch, int max_ctx, int hq, int hkv, int d, float scale,
+                     const void* new_k, const void* new_v, void* o, float* lse_opt,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kvs_copy_blocks - device side of copy-on-write: whole-block copies in both pools.
+ *   [PAG] "Sharing blocks between sequences": a sequence that must write a block still
+ *   used by others copies it first.
+ * src_dst_pairs [n_pairs][2] int32 (device): block src is copied to block dst (K and V,
+ * every head).  Pairs must not chain (no dst is another pair's src).
+ * Errors: KVS_E_INVAL on a bad shape; KVS_E_HIP on launch failure.
+ */
+int kvs_copy_blocks(void* k_pool, void* v_pool, int num_blocks, int hkv, int d,
+                    const int32_t* src_dst_pairs, int n_pairs, void* stream);
+
+/*
+ * Host block allocator.  [PAG] "How paging works": a request gets a new block only when
+ * its last block is full, from any free block (the worked example pops from the front of
+ * the free list).  [PAG] "Sharing blocks between sequences": a reference count per block;
+ * copy-on-write.  [PAG] "Related techniques": a finished sequence's blocks return to the
+ * free pool at once.
+ * The free list is FIFO: allocation pops the front, a block whose count reaches 0 is
+ * appended at the back.  The object is owned by the caller (create / destroy).
+ */
+typedef struct kvs_alloc kvs_alloc;
+/* initial_free_order: host array of n_initial distinct ids in [0, num_blocks) forming the
+ * free list (NULL: 0..num_blocks-1, n_initial ignored).  Blocks not listed start in use
+ * with count 1. */
+int kvs_alloc_create(int num_blocks, const int32_t* initial_free_order, int n_initial,
+                     kvs_alloc** out);
+void kvs_alloc_destroy(kvs_alloc* a);
+/* Pop the front of the free list; its count becomes 1.  KVS_E_NOBLOCKS if empty. */
+int kvs_alloc_block(kvs_alloc* a, int32_t* out_block);
+/* Share a live block.  KVS_E_STATE if the block is free. */
+int kvs_alloc_incref(kvs_alloc* a, int32_t block);
+/* Drop one reference; at 0 the block is appended to the free list.  KVS_E_STATE if free. */
+int kvs_alloc_decref(kvs_alloc* a, int32_t block);
+/* Count of a block (0 = free), or KVS_E_INVAL for an id out of range. */
+int kvs_alloc_refcount(const kvs_alloc* a, int32_t block);
+int kvs_alloc_num_free(const kvs_alloc* a);
+/* Copy up to cap ids of the free list, front first; returns the number written. */
+int kvs_alloc_free_list(const kvs_alloc* a, int32_t* out, int cap);
+/* Copy-on-write: count > 1 -> a fresh block is allocated, the old one loses a reference,
+ * *out_block = new id and *copied = 1 (the caller copies the data if a live slot survives);
+ * count == 1 -> *out_block = block, *copied = 0.  KVS_E_NOBLOCKS / KVS_E_STATE as above. */
+int kvs_alloc_cow(kvs_alloc* a, int32_t block, int32_t* out_block, int* copied);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVS_H_ */

@@ -1,0 +1,20 @@
+"""KV-cache sparsification on MI355X: the prefill-and-compress path behind libkvs.
+
+    kvs_prefill_attn_lse -> kvs_window_score -> kvs_topk_select -> kvs_compact_paged -> kvs_paged_decode
+
+Every step runs in hand-written HIP kernels for gfx950 (libkvs.so, built in-tree with
+``python -m kv_cache_sparsification_amd.build``).  This package only marshals torch tensors
+into the C ABI declared in include/kvs.h; importing it fails if the library is not built.
+"""
+from ._lib import lib, KvsError, BLOCK_SIZE, LIB_PATH
+from .ops import (kvs_prefill_attn_lse, kvs_window_score, kvs_topk_select, kvs_compact_paged,
+                  kvs_paged_decode, kvs_paged_decode_workspace_size, kvs_copy_blocks, new_pools)
+from .allocator import BlockAllocator
+from .pipeline import layer_policy, keep_counts, prefill_compress_layer
+
+__all__ = [
+    "lib", "KvsError", "BLOCK_SIZE", "LIB_PATH",
+    "kvs_prefill_attn_lse", "kvs_window_score", "kvs_topk_select", "kvs_compact_paged",
+    "kvs_paged_decode", "kvs_paged_decode_workspace_size", "kvs_copy_blocks", "new_pools",
+    "BlockAllocator", "layer_policy", "keep_counts", "prefill_compress_layer",
+]

@@ -1,0 +1,166 @@
+// Gather-compaction of kept K/V rows into 16-token blocks, and the block copy of
+// copy-on-write.
+//
+// [PAG] Ultralytics glossary, "PagedAttention", "How paging works": the cache is stored in
+// fixed 16-token blocks anywhere in GPU memory and a per-request block table gives their
+// order; the worked example writes token p to block table[p // 16], slot p % 16.
+// [PAG] "Sharing blocks between sequences": a shared block is copied before it is written.
+// [KVS] Novita AI, "How KV Sparsity Achieves 1.5x Acceleration for vLLM", Key techniques 1:
+// the first three layers keep every token, the later layers only their budget.
+//
+// Pool layouts (bf16): K [num_blocks][hkv][16][d] (token rows), V [num_blocks][hkv][d][16]
+// (each channel's 16 slots contiguous, the operand order the decode kernel's P.V product
+// wants).  One wavefront fills one (destination block, head) pair: for K it moves whole
+// token rows with 16-byte lanes, for V each lane owns a pair of channels, reads them for all
+// 16 slots (every read instruction covers one contiguous source row) and writes two
+// contiguous 32-byte channel runs, so both sides stay coalesced with no LDS round trip.
+#include "kvs_common.h"
+
+namespace kvs {
+namespace {
+
+constexpr int kWavesPerWG = 4;
+
+template <int D>
+__global__ __launch_bounds__(kWavesPerWG * kWave) void compact_kernel(
+    const uint16_t* __restrict__ k_src, const uint16_t* __restrict__ v_src,
+    const int32_t* __restrict__ cu_seqlens, int hkv, const int32_t* __restrict__ keep_idx,
+    const int32_t* __restrict__ keep_offsets, uint16_t* __restrict__ k_pool,
+    uint16_t* __restrict__ v_pool, int num_blocks, const int32_t* __restrict__ block_tables,
+    int max_blocks, const int32_t* __restrict__ dst_slot_offset, int blocks_per_seq) {
+  const int lane = threadIdx.x % kWave;
+  const int unit = blockIdx.x * kWavesPerWG + threadIdx.x / kWave;   // (block index, head)
+  const int s = blockIdx.y;
+  if (unit >= blocks_per_seq * hkv) return;
+  const int bi = unit / hkv;
+  const int g = unit % hkv;
+
+  const int base = cu_seqlens[s];
+  const int n = cu_seqlens[s + 1] - base;
+  const bool keep_all = keep_idx == nullptr;
+  const int k_eff = keep_all ? n : keep_offsets[s + 1] - keep_offsets[s];
+  const int off = dst_slot_offset ? dst_slot_offset[s] : 0;
+  const int tbl_pos = off / kBlock + bi;          // table entry this unit fills
+  const int p0 = tbl_pos * kBlock;                 // slot position of its first slot
+  if (k_eff <= 0 || p0 >= off + k_eff || tbl_pos >= max_blocks) return;
+  const int blk = block_tables[(size_t)s * max_blocks + tbl_pos];
+  if (blk < 0 || blk >= num_blocks) return;
+
+  const int32_t* keep = keep_all ? nullptr : keep_idx + (size_t)hkv * keep_offsets[s] + (size_t)g * k_eff;
+  const int t0 = p0 - off;                         // rank written to slot 0 (may be negative)
+  const bool full = t0 >= 0 && t0 + kBlock <= k_eff;
+
+  // ---- K: row-major slots, 16-byte lanes
+  constexpr int kLanesPerRow = D * 2 / 16;         // 16 (d=128) or 8 (d=64)
+  constexpr int kRowsPerIter = kWave / kLanesPerRow;
+  uint16_t* kdst = k_pool + ((size_t)blk * hkv + g) * kBlock * D;
+  for (int j = lane / kLanesPerRow; j < kBlock; j += kRowsPerIter) {
+    const int t = t0 + j;
+    if (t < 0 || t >= k_eff) continue;
+    const int src = keep_all ? t : keep[t];
+    const int c = lane % kLanesPerRow;
+    const u32x4 val = *reinterpret_cast<const u32x4*>(k_src + ((size_t)(base + src) * hkv + g) * D + c * 8);
+    *reinterpret_cast<u32x4*>(kdst + j * D + c * 8) = val;
+  }
+
+  // ---- V: channel-major slots; lane owns channels 2*lane and 2*lane + 1
+  constexpr int kPairs = D / 2;
+  if (lane >= kPairs) return;
+  uint16_t* vdst = v_pool + ((size_t)blk * hkv + g) * D * kBlock;
+  if (full) {
+    uint32_t pair[kBlock];
+#pragma unroll
+    for (int j = 0; j < kBlock; ++j) {
+      const int src = keep_all ? t0 + j : keep[t0 + j];
+      pair[j] = *reinterpret_cast<const uint32_t*>(v_src + ((size_t)(base + src) * hkv + g) * D + 2 * lane);
+    }
+    u32x4 lo[2], hi[2];   // channel 2*lane (low halves) and 2*lane + 1 (high halves), 16 slots each
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      // slot 2q in the low half-word, slot 2q + 1 in the high one
+      lo[q / 4][q % 4] = (pair[2 * q] & 0xffffu) | (pair[2 * q + 1] << 16);
+      hi[q / 4][q % 4] = (pair[2 * q] >> 16) | (pair[2 * q + 1] & 0xffff0000u);
+    }
+    u32x4* d0 = reinterpret_cast<u32x4*>(vdst + (size_t)(2 * lane) * kBlock);
+    u32x4* d1 = reinterpret_cast<u32x4*>(vdst + (size_t)(2 * lane + 1) * kBlock);
+    d0[0] = lo[0]; d0[1] = lo[1];
+    d1[0] = hi[0]; d1[1] = hi[1];
+  } else {
+    for (int j = 0; j < kBlock; ++j) {
+      const int t = t0 + j;
+      if (t < 0 || t >= k_eff) continue;
+      const int src = keep_all ? t : keep[t];
+      const uint32_t x = *reinterpret_cast<const uint32_t*>(v_src + ((size_t)(base + src) * hkv + g) * D + 2 * lane);
+      vdst[(size_t)(2 * lane) * kBlock + j] = (uint16_t)(x & 0xffffu);
+      vdst[(size_t)(2 * lane + 1) * kBlock + j] = (uint16_t)(x >> 16);
+    }
+  }
+}
+
+// One workgroup copies one (src, dst) block pair in both pools.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(uint16_t* __restrict__ k_pool,
+                                                          uint16_t* __restrict__ v_pool, int num_blocks,
+                                                          size_t block_elems,
+                                                          const int32_t* __restrict__ pairs) {
+  const int src = pairs[2 * blockIdx.x];
+  const int dst = pairs[2 * blockIdx.x + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks || src == dst) return;
+  const size_t n16 = block_elems / 8;   // 16-byte chunks per block
+  const u32x4* ks = reinterpret_cast<const u32x4*>(k_pool + (size_t)src * block_elems);
+  u32x4* kd = reinterpret_cast<u32x4*>(k_pool + (size_t)dst * block_elems);
+  const u32x4* vs = reinterpret_cast<const u32x4*>(v_pool + (size_t)src * block_elems);
+  u32x4* vd = reinterpret_cast<u32x4*>(v_pool + (size_t)dst * block_elems);
+  for (size_t i = threadIdx.x; i < n16; i += blockDim.x) {
+    kd[i] = ks[i];
+    vd[i] = vs[i];
+  }
+}
+
+}  // namespace
+}  // namespace kvs
+
+using namespace kvs;
+
+extern "C" int kvs_compact_paged(const void* k_src, const void* v_src, const int32_t* cu_seqlens,
+                                 int num_seqs, int hkv, int d, const int32_t* keep_idx,
+                                 const int32_t* keep_offsets, int max_keep, void* k_pool, void* v_pool,
+                                 int num_blocks, const int32_t* block_tables, int max_blocks,
+                                 const int32_t* dst_slot_offset, void* stream) {
+  if (!k_src || !v_src || !cu_seqlens || !k_pool || !v_pool || !block_tables)
+    return fail(KVS_E_INVAL, "kvs_compact_paged: NULL tensor");
+  if (keep_idx && !keep_offsets) return fail(KVS_E_INVAL, "kvs_compact_paged: keep_offsets required with keep_idx");
+  if (num_seqs < 0 || hkv <= 0 || (d != 64 && d != 128) || max_keep < 0 || num_blocks <= 0 || max_blocks <= 0)
+    return fail(KVS_E_INVAL, "kvs_compact_paged: bad shape (num_seqs=%d hkv=%d d=%d max_keep=%d)", num_seqs, hkv,
+                d, max_keep);
+  if (num_seqs == 0 || max_keep == 0) return KVS_OK;
+  // A misaligned destination offset makes the kept rows straddle one extra block.
+  const int blocks_per_seq = (max_keep + kBlock - 1) / kBlock + (dst_slot_offset ? 1 : 0);
+  const int units = blocks_per_seq * hkv;
+  dim3 grid((units + kWavesPerWG - 1) / kWavesPerWG, num_seqs);
+  dim3 block(kWavesPerWG * kWave);
+  auto* ks = static_cast<const uint16_t*>(k_src);
+  auto* vs = static_cast<const uint16_t*>(v_src);
+  auto* kp = static_cast<uint16_t*>(k_pool);
+  auto* vp = static_cast<uint16_t*>(v_pool);
+  if (d == 128)
+    hipLaunchKernelGGL(compact_kernel<128>, grid, block, 0, as_stream(stream), ks, vs, cu_seqlens, hkv, keep_idx,
+                       keep_offsets, kp, vp, num_blocks, block_tables, max_blocks, dst_slot_offset, blocks_per_seq);
+  else
+    hipLaunchKernelGGL(compact_kernel<64>, grid, block, 0, as_stream(stream), ks, vs, cu_seqlens, hkv, keep_idx,
+                       keep_offsets, kp, vp, num_blocks, block_tables, max_blocks, dst_slot_offset, blocks_per_seq);
+  return launch_status("kvs_compact_paged");
+}
+
+extern "C" int kvs_copy_blocks(void* k_pool, void* v_pool, int num_blocks, int hkv, int d,
+                               const int32_t* src_dst_pairs, int n_pairs, void* stream) {
+  if (!k_pool || !v_pool || (n_pairs > 0 && !src_dst_pairs))
+    return fail(KVS_E_INVAL, "kvs_copy_blocks: NULL tensor");
+  if (num_blocks <= 0 || hkv <= 0 || (d != 64 && d != 128) || n_pairs < 0)
+    return fail(KVS_E_INVAL, "kvs_copy_blocks: bad shape");
+  if (n_pairs == 0) return KVS_OK;
+  const size_t block_elems = (size_t)hkv * kBlock * d;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(n_pairs), dim3(256), 0, as_stream(stream),
+                     static_cast<uint16_t*>(k_pool), static_cast<uint16_t*>(v_pool), num_blocks, block_elems,
+                     src_dst_pairs);
+  return launch_status("kvs_copy_blocks");
+}

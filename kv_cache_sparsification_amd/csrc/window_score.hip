@@ -1,0 +1,137 @@
+// Observation-window score S, rebuilt from the LSE the prefill saved.
+//
+// [KVS] Novita AI, "How KV Sparsity Achieves 1.5x Acceleration for vLLM", Key techniques,
+// 2. "Attention modification" (the PyramidKV-style score and the modified-FlashAttention
+// figure, second Fig. 7):
+//   * the last alpha prompt positions form the window; the score of token i is the sum of
+//     its softmax values over the window rows;
+//   * softmax values come back from the saved row statistics, p = exp(qk - rowmax) / l,
+//     which is exp(qk - LSE); a row-wise sum then gives S;
+//   * the loop order is swapped from q.k to k.q so that the sum over window rows is a
+//     register sum and no block has to talk to another;
+//   * causality and the window bound mean only window rows are visited (about n * alpha
+//     pairs instead of n * n).
+//
+// MI355X form.  A workgroup (4 wavefronts) owns 128 consecutive keys of one KV head; each
+// wavefront owns 32 keys, which are the N dimension of a bf16 32x32x16 MFMA, while the
+// G * a window rows of the group's query heads are the M dimension, staged through LDS in
+// chunks of 64 rows together with LSE * log2(e) and each row's causal limit.  Every lane
+// ends up holding 16 (row, key) products for one key, so the window sum is 16 adds in
+// registers per M tile plus a single cross-lane add at the end: the pages' "row sum in
+// registers".  The key fragment is read from HBM once and kept in registers; nothing but
+// the window rows is ever touched.
+#include "kvs_common.h"
+
+namespace kvs {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kKeysPerWave = 32;
+constexpr int kKeysPerWG = kWaves * kKeysPerWave;
+constexpr int kRowChunk = 64;   // window rows staged in LDS at a time (2 M tiles)
+
+template <int D>
+__global__ __launch_bounds__(kWaves * kWave) void window_score_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ lse,
+    const int32_t* __restrict__ cu_seqlens, int total_tokens, int alpha, int hq, int hkv, float c_log2,
+    float* __restrict__ S) {
+  constexpr int kStride = D + 8;                       // bf16 per LDS row (16-byte pad)
+  __shared__ __attribute__((aligned(16))) uint16_t qs[kRowChunk * kStride];
+  __shared__ float lse2[kRowChunk];
+  __shared__ int jlim[kRowChunk];
+
+  const int g = blockIdx.y, s = blockIdx.z;
+  const int base = cu_seqlens[s];
+  const int n = cu_seqlens[s + 1] - base;
+  const int kb_wg = blockIdx.x * kKeysPerWG;
+  if (kb_wg >= n) return;
+  const int G = hq / hkv;
+  const int a = alpha < n ? alpha : n;
+  const int rows = G * a;                               // window rows of this KV head's group
+
+  const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
+  const int half = lane / 32, col = lane % 32;
+  const int key = kb_wg + w * kKeysPerWave + col;       // this lane's key (N index)
+
+  // B operand: K^T[d][key] for every 16-wide d step, kept in registers.
+  bf16x8 kf[D / 16];
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (key < n) v = *reinterpret_cast<const u32x4*>(k + ((size_t)(base + key) * hkv + g) * D + st * 16 + half * 8);
+    kf[st] = __builtin_bit_cast(bf16x8, v);
+  }
+
+  float acc_sum = 0.f;
+  for (int r0 = 0; r0 < rows; r0 += kRowChunk) {
+    // Stage 64 window rows: row r = (local head r / a, window position r % a).
+    for (int e = tid; e < kRowChunk * (D / 8); e += kWaves * kWave) {
+      const int r = e / (D / 8), cc = e % (D / 8);
+      const int rr = r0 + r;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (rr < rows) {
+        const int h = g * G + rr / a, j = n - a + rr % a;
+        v = *reinterpret_cast<const u32x4*>(q + ((size_t)(base + j) * hq + h) * D + cc * 8);
+      }
+      *reinterpret_cast<u32x4*>(&qs[r * kStride + cc * 8]) = v;
+    }
+    if (tid < kRowChunk) {
+      const int rr = r0 + tid;
+      if (rr < rows) {
+        const int h = g * G + rr / a, j = n - a + rr % a;
+        lse2[tid] = lse[(size_t)h * total_tokens + base + j] * kLog2e;
+        jlim[tid] = j;
+      } else {
+        lse2[tid] = 0.f;
+        jlim[tid] = -1;                                 // padding row: masks every key
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int mt = 0; mt < kRowChunk / 32; ++mt) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st) {
+        const u32x4 av = *reinterpret_cast<const u32x4*>(&qs[(mt * 32 + col) * kStride + st * 16 + half * 8]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), kf[st], acc, 0, 0, 0);
+      }
+      // acc[i] is window row mt*32 + 8*(i/4) + 4*half + i%4 against this lane's key.
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = mt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+        const float p = __builtin_amdgcn_exp2f(acc[i] * c_log2 - lse2[r]);
+        acc_sum += key <= jlim[r] ? p : 0.f;
+      }
+    }
+    __syncthreads();
+  }
+  acc_sum += wave_xor(acc_sum, 32);
+  if (half == 0 && key < n) S[(size_t)g * total_tokens + base + key] = acc_sum;
+}
+
+}  // namespace
+}  // namespace kvs
+
+using namespace kvs;
+
+extern "C" int kvs_window_score(const void* q, const void* k, const float* lse, const int32_t* cu_seqlens,
+                                int num_seqs, int total_tokens, int max_seqlen, int alpha, int hq, int hkv, int d,
+                                float scale, float* scores, void* stream) {
+  if (!q || !k || !lse || !cu_seqlens || !scores) return fail(KVS_E_INVAL, "kvs_window_score: NULL tensor");
+  if (num_seqs < 0 || total_tokens < 0 || max_seqlen < 0 || hq <= 0 || hkv <= 0 || hq % hkv || hq / hkv > 16 ||
+      (d != 64 && d != 128) || !(scale > 0.f))
+    return fail(KVS_E_INVAL, "kvs_window_score: bad shape (hq=%d hkv=%d d=%d)", hq, hkv, d);
+  if (alpha < 1) return fail(KVS_E_INVAL, "kvs_window_score: alpha must be >= 1");
+  if (num_seqs == 0 || max_seqlen == 0) return KVS_OK;
+  dim3 grid((max_seqlen + kKeysPerWG - 1) / kKeysPerWG, hkv, num_seqs);
+  const float c = scale * kLog2e;
+  auto* qq = static_cast<const uint16_t*>(q);
+  auto* kk = static_cast<const uint16_t*>(k);
+  if (d == 128)
+    hipLaunchKernelGGL(window_score_kernel<128>, grid, dim3(kWaves * kWave), 0, as_stream(stream), qq, kk, lse,
+                       cu_seqlens, total_tokens, alpha, hq, hkv, c, scores);
+  else
+    hipLaunchKernelGGL(window_score_kernel<64>, grid, dim3(kWaves * kWave), 0, as_stream(stream), qq, kk, lse,
+                       cu_seqlens, total_tokens, alpha, hq, hkv, c, scores);
+  return launch_status("kvs_window_score");
+}

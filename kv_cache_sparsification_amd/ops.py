@@ -1,0 +1,151 @@
+"""Thin torch-facing binding of the libkvs device calls (argument marshalling only).
+
+Each function has the name of the C entry point it forwards to, checks that the tensors
+have the dtype, device and contiguity the C ABI expects, allocates missing outputs with
+torch (device memory is the only thing torch provides here), and launches on the current
+torch stream.  All arithmetic happens in the HIP kernels.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import torch
+
+from ._lib import lib, check, BLOCK_SIZE
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, dtype, name: str):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return t
+
+
+def _stream(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def kvs_prefill_attn_lse(q, k, v, cu_seqlens, max_seqlen: int, scale: Optional[float] = None, o=None, lse=None,
+                         rowmax=None, ell=None, stream=None):
+    """Causal attention + LSE.  q [T][Hq][d], k/v [T][Hkv][d] bf16; returns (o, lse [Hq][T])."""
+    _dev(q, torch.bfloat16, "q"); _dev(k, torch.bfloat16, "k"); _dev(v, torch.bfloat16, "v")
+    _dev(cu_seqlens, torch.int32, "cu_seqlens")
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if o is None else _dev(o, torch.bfloat16, "o")
+    lse = torch.empty(hq, T, device=q.device, dtype=torch.float32) if lse is None else _dev(lse, torch.float32, "lse")
+    for name, t in (("rowmax", rowmax), ("ell", ell)):
+        if t is not None:
+            _dev(t, torch.float32, name)
+    check(lib.kvs_prefill_attn_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(),
+                                   cu_seqlens.numel() - 1, T, int(max_seqlen), hq, hkv, d, float(scale),
+                                   o.data_ptr(), lse.data_ptr(), _ptr(rowmax), _ptr(ell), _stream(stream)))
+    return o, lse
+
+
+def kvs_window_score(q, k, lse, cu_seqlens, max_seqlen: int, alpha: int, scale: Optional[float] = None,
+                     scores=None, stream=None):
+    """Window score S [Hkv][T] from the saved LSE [Hq][T]."""
+    _dev(q, torch.bfloat16, "q"); _dev(k, torch.bfloat16, "k"); _dev(lse, torch.float32, "lse")
+    _dev(cu_seqlens, torch.int32, "cu_seqlens")
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    scores = torch.empty(hkv, T, device=q.device, dtype=torch.float32) if scores is None else \
+        _dev(scores, torch.float32, "scores")
+    check(lib.kvs_window_score(q.data_ptr(), k.data_ptr(), lse.data_ptr(), cu_seqlens.data_ptr(),
+                               cu_seqlens.numel() - 1, T, int(max_seqlen), int(alpha), hq, hkv, d, float(scale),
+                               scores.data_ptr(), _stream(stream)))
+    return scores
+
+
+def kvs_topk_select(scores, cu_seqlens, max_seqlen: int, alpha: int, k_budget: int, keep_offsets, keep_idx=None,
+                    total_keep: Optional[int] = None, stream=None):
+    """Kept indices; keep_offsets [S+1] int32 (device, prefix sums of min(k, n_s)); total_keep = its last value."""
+    _dev(scores, torch.float32, "scores"); _dev(cu_seqlens, torch.int32, "cu_seqlens")
+    _dev(keep_offsets, torch.int32, "keep_offsets")
+    hkv, T = scores.shape
+    if keep_idx is None:
+        if total_keep is None:
+            raise ValueError("total_keep (host value of keep_offsets[-1]) is needed to size keep_idx")
+        keep_idx = torch.empty(hkv * int(total_keep), device=scores.device, dtype=torch.int32)
+    _dev(keep_idx, torch.int32, "keep_idx")
+    check(lib.kvs_topk_select(scores.data_ptr(), cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, T, int(max_seqlen),
+                              hkv, int(alpha), int(k_budget), keep_offsets.data_ptr(), keep_idx.data_ptr(),
+                              _stream(stream)))
+    return keep_idx
+
+
+def kvs_compact_paged(k_src, v_src, cu_seqlens, keep_idx, keep_offsets, max_keep: int, k_pool, v_pool,
+                      block_tables, dst_slot_offset=None, stream=None):
+    """Write kept rows (keep_idx None = every row) into the pools through the block tables."""
+    _dev(k_src, torch.bfloat16, "k_src"); _dev(v_src, torch.bfloat16, "v_src")
+    _dev(cu_seqlens, torch.int32, "cu_seqlens"); _dev(block_tables, torch.int32, "block_tables")
+    _dev(k_pool, torch.bfloat16, "k_pool"); _dev(v_pool, torch.bfloat16, "v_pool")
+    if keep_idx is not None:
+        _dev(keep_idx, torch.int32, "keep_idx"); _dev(keep_offsets, torch.int32, "keep_offsets")
+    if dst_slot_offset is not None:
+        _dev(dst_slot_offset, torch.int32, "dst_slot_offset")
+    T, hkv, d = k_src.shape
+    check(lib.kvs_compact_paged(k_src.data_ptr(), v_src.data_ptr(), cu_seqlens.data_ptr(), cu_seqlens.numel() - 1,
+                                hkv, d, _ptr(keep_idx), _ptr(keep_offsets), int(max_keep), k_pool.data_ptr(),
+                                v_pool.data_ptr(), k_pool.shape[0], block_tables.data_ptr(), block_tables.shape[1],
+                                _ptr(dst_slot_offset), _stream(stream)))
+
+
+def kvs_paged_decode_workspace_size(batch: int, hq: int, hkv: int, d: int, max_ctx: int) -> int:
+    return int(lib.kvs_paged_decode_workspace_size(batch, hq, hkv, d, max_ctx))
+
+
+def kvs_paged_decode(q, k_pool, v_pool, block_tables, ctx_lens, max_ctx: int, scale: Optional[float] = None,
+                     new_k=None, new_v=None, o=None, lse=None, workspace=None, stream=None):
+    """One decode step: q [B][Hq][d] over the paged cache (new_k/new_v appended at slot L-1 first)."""
+    _dev(q, torch.bfloat16, "q"); _dev(k_pool, torch.bfloat16, "k_pool"); _dev(v_pool, torch.bfloat16, "v_pool")
+    _dev(block_tables, torch.int32, "block_tables"); _dev(ctx_lens, torch.int32, "ctx_lens")
+    B, hq, d = q.shape
+    hkv = k_pool.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if new_k is not None:
+        _dev(new_k, torch.bfloat16, "new_k"); _dev(new_v, torch.bfloat16, "new_v")
+    o = torch.empty_like(q) if o is None else _dev(o, torch.bfloat16, "o")
+    if lse is not None:
+        _dev(lse, torch.float32, "lse")
+    need = kvs_paged_decode_workspace_size(B, hq, hkv, d, int(max_ctx))
+    if need and workspace is None:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(lib.kvs_paged_decode(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), k_pool.shape[0],
+                               block_tables.data_ptr(), block_tables.shape[1], ctx_lens.data_ptr(), B, int(max_ctx),
+                               hq, hkv, d, float(scale), _ptr(new_k), _ptr(new_v), o.data_ptr(), _ptr(lse),
+                               _ptr(workspace), ws_bytes, _stream(stream)))
+    return o
+
+
+def kvs_copy_blocks(k_pool, v_pool, src_dst_pairs, stream=None):
+    """Copy whole blocks (both pools): src_dst_pairs [n][2] int32 device."""
+    _dev(k_pool, torch.bfloat16, "k_pool"); _dev(v_pool, torch.bfloat16, "v_pool")
+    _dev(src_dst_pairs, torch.int32, "src_dst_pairs")
+    nb, hkv = k_pool.shape[0], k_pool.shape[1]
+    d = k_pool.shape[3]
+    check(lib.kvs_copy_blocks(k_pool.data_ptr(), v_pool.data_ptr(), nb, hkv, d, src_dst_pairs.data_ptr(),
+                              src_dst_pairs.shape[0], _stream(stream)))
+
+
+def new_pools(num_blocks: int, hkv: int, d: int, device="cuda"):
+    """Empty K [num_blocks][hkv][16][d] and V [num_blocks][hkv][d][16] bf16 pools."""
+    k_pool = torch.empty(num_blocks, hkv, BLOCK_SIZE, d, device=device, dtype=torch.bfloat16)
+    v_pool = torch.empty(num_blocks, hkv, d, BLOCK_SIZE, device=device, dtype=torch.bfloat16)
+    return k_pool, v_pool

@@ -1,0 +1,79 @@
+"""Host orchestration of one layer's prefill-and-compress step (no device readback).
+
+[KVS] Novita AI, "How KV Sparsity Achieves 1.5x Acceleration for vLLM", Key techniques 1
+(step preparation): the first three layers keep a full cache, later layers keep a budget
+k_l per head; [KVS] Key techniques 2: rowmax/l from the attention feed the window score,
+whose top-k_l tokens are kept.  [PAG] Ultralytics glossary, "PagedAttention", "How paging
+works": blocks come from the allocator's free list and a table records their order.
+
+Every size the kernels need (k_eff = min(k_l, n) per prompt, the keep offsets, the number
+of blocks) follows from the prompt lengths, the budget and the window on the host, so the
+host never waits for the device.
+"""
+from __future__ import annotations
+
+import math
+from typing import List, Optional, Sequence
+
+import torch
+
+from ._lib import BLOCK_SIZE
+from . import ops
+
+FULL_CACHE_LAYERS = 3   # [KVS] Key techniques 1: the first three layers store every KV
+
+
+def layer_policy(layer: int, k_budget: Optional[int], full_layers: int = FULL_CACHE_LAYERS) -> Optional[int]:
+    """The budget a layer compresses to, or None for a full-cache layer."""
+    return None if layer < full_layers else k_budget
+
+
+def keep_counts(lengths: Sequence[int], k_budget: Optional[int]) -> List[int]:
+    """Tokens each prompt keeps per KV head: n for a full layer, else min(k_l, n)."""
+    return [n if (k_budget is None or k_budget >= n) else k_budget for n in lengths]
+
+
+def blocks_needed(tokens: int) -> int:
+    return -(-tokens // BLOCK_SIZE)
+
+
+def prefill_compress_layer(q, k, v, cu_seqlens, lengths: Sequence[int], alpha: int, k_budget: Optional[int],
+                           allocator, k_pool, v_pool, max_blocks: int, scale: Optional[float] = None,
+                           tables: Optional[List[List[int]]] = None, stream=None):
+    """Run prefill attention + (window score + top-k when compressing) + compaction for one layer.
+
+    lengths are the host copies of the prompt lengths; tables (host lists) may be given to
+    reuse blocks, else ceil(k_eff / 16) blocks per prompt are taken from the allocator.
+    Returns a dict with o, lse, scores, keep_idx, keep_offsets, tables and the device tables.
+    """
+    dev = q.device
+    max_n = max(lengths)
+    o, lse = ops.kvs_prefill_attn_lse(q, k, v, cu_seqlens, max_n, scale=scale, stream=stream)
+    kept = keep_counts(lengths, k_budget)
+    if tables is None:
+        tables = [allocator.alloc_n(blocks_needed(c)) for c in kept]
+    tbl = torch.full((len(lengths), max_blocks), -1, dtype=torch.int32)
+    for i, t in enumerate(tables):
+        if len(t) > max_blocks:
+            raise ValueError("block table longer than max_blocks")
+        tbl[i, :len(t)] = torch.tensor(t, dtype=torch.int32)
+    tbl_dev = tbl.to(dev, non_blocking=False)
+    scores = keep_idx = keep_off_dev = None
+    if k_budget is None:
+        ops.kvs_compact_paged(k, v, cu_seqlens, None, None, max(kept), k_pool, v_pool, tbl_dev, stream=stream)
+    else:
+        scores = ops.kvs_window_score(q, k, lse, cu_seqlens, max_n, alpha, scale=scale, stream=stream)
+        keep_off = [0]
+        for c in kept:
+            keep_off.append(keep_off[-1] + c)
+        keep_off_dev = torch.tensor(keep_off, dtype=torch.int32).to(dev)
+        keep_idx = ops.kvs_topk_select(scores, cu_seqlens, max_n, alpha, k_budget, keep_off_dev,
+                                       total_keep=keep_off[-1], stream=stream)
+        ops.kvs_compact_paged(k, v, cu_seqlens, keep_idx, keep_off_dev, max(kept), k_pool, v_pool, tbl_dev,
+                              stream=stream)
+    return dict(o=o, lse=lse, scores=scores, keep_idx=keep_idx, keep_offsets=keep_off_dev, kept=kept,
+                tables=tables, tables_dev=tbl_dev)
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)

@@ -54,7 +54,10 @@ class BlockAllocator:
         if len(set(order)) != len(order) or any(b < 0 or b >= num_blocks for b in order):
             raise ValueError("initial free order must be distinct ids in [0, num_blocks)")
         self.free = collections.deque(order)
-        self.ref = [0] * num_blocks
+        # Blocks missing from the initial free list belong to other requests (the page's
+        # example has a 64-block pool with five free blocks): they start with count 1.
+        listed = set(order)
+        self.ref = [0 if b in listed else 1 for b in range(num_blocks)]
         self.log: List[tuple] = []
 
     def _valid(self, b: int):

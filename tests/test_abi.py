@@ -1,0 +1,139 @@
+"""CPU checks of the C ABI: every declared symbol is exported, host-side argument checks
+fail before any launch, and the native allocator matches the oracle's allocator op for op."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle.paged import NoBlocksError, RefcountError
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvs.h")
+
+kvs = pytest.importorskip("kv_cache_sparsification_amd")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvs_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 18
+    lib = ctypes.CDLL(kvs.LIB_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    # and the binding declares a signature for each
+    from kv_cache_sparsification_amd._lib import SIGNATURES
+    assert sorted(SIGNATURES) == names
+
+
+def test_version():
+    assert b"gfx950" in kvs.lib.kvs_version()
+
+
+def test_host_validation_rejects_before_launch():
+    L = kvs.lib
+    fake = 0x1000   # never dereferenced: the checks fail first
+    rc = L.kvs_prefill_attn_lse(fake, fake, fake, fake, 1, 10, 10, 8, 3, 128, 0.1, fake, fake, None, None, None)
+    assert rc == kvs._lib.KVS_E_INVAL and b"bad shape" in L.kvs_last_error()
+    assert L.kvs_prefill_attn_lse(fake, fake, fake, fake, 1, 10, 10, 8, 2, 96, 0.1, fake, fake, None, None, None) == -1
+    assert L.kvs_window_score(fake, fake, fake, fake, 1, 10, 10, 0, 8, 2, 128, 0.1, fake, None) == -1
+    assert L.kvs_topk_select(fake, fake, 1, 10, 10, 2, 8, 4, fake, fake, None) == -1      # k < alpha
+    assert b"alpha" in L.kvs_last_error()
+    assert L.kvs_compact_paged(fake, fake, fake, 1, 2, 100, None, None, 8, fake, fake, 4, fake, 4, None, None) == -1
+    assert L.kvs_copy_blocks(fake, fake, 4, 2, 128, None, 3, None) == -1
+    ws = L.kvs_paged_decode_workspace_size(1, 32, 8, 128, 4000)
+    assert ws > 0
+    assert L.kvs_paged_decode(fake, fake, fake, 64, fake, 300, fake, 1, 4000, 32, 8, 128, 0.1, None, None, fake,
+                              None, fake, ws - 1, None) == -1
+    assert b"workspace" in L.kvs_last_error()
+    assert L.kvs_paged_decode(fake, fake, fake, 64, fake, 10, fake, 1, 4000, 32, 8, 128, 0.1, None, None, fake,
+                              None, None, 0, None) == -1                                       # 10 blocks < 4000 tokens
+    # empty work is a no-op that launches nothing
+    assert L.kvs_prefill_attn_lse(fake, fake, fake, fake, 0, 0, 0, 8, 2, 128, 0.1, fake, fake, None, None, None) == 0
+    assert L.kvs_copy_blocks(fake, fake, 4, 2, 128, fake, 0, None) == 0
+
+
+def test_workspace_size_policy():
+    L = kvs.lib
+    # short contexts at large batch need no split; long single-sequence contexts do
+    assert L.kvs_paged_decode_workspace_size(64, 32, 8, 128, 64) == 0
+    assert L.kvs_paged_decode_workspace_size(1, 32, 8, 128, 900) > 0
+    assert L.kvs_paged_decode_workspace_size(0, 32, 8, 128, 900) == 0
+
+
+def test_allocator_worked_example():
+    a = kvs.BlockAllocator(64, [41, 7, 19, 2, 33])
+    assert a.alloc_n(3) == [41, 7, 19]
+    assert a.free_list() == [2, 33]
+    assert a.refcount(5) == 1 and a.refcount(2) == 0     # unlisted blocks start in use
+
+
+def test_allocator_errors():
+    a = kvs.BlockAllocator(2)
+    b0, b1 = a.alloc(), a.alloc()
+    with pytest.raises(kvs.KvsError) as e:
+        a.alloc()
+    assert e.value.code == -2
+    a.decref(b0)
+    with pytest.raises(kvs.KvsError) as e:
+        a.decref(b0)
+    assert e.value.code == -3
+    with pytest.raises(kvs.KvsError):
+        a.incref(b0)
+    with pytest.raises(kvs.KvsError):
+        a.refcount(7)
+    with pytest.raises(kvs.KvsError):
+        kvs.BlockAllocator(4, [1, 1])
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_allocator_matches_oracle_on_random_ops(seed):
+    r = np.random.default_rng(seed)
+    N = int(r.integers(4, 40))
+    order = list(r.permutation(N)[: int(r.integers(1, N + 1))])
+    ref = oracle.BlockAllocator(N, initial_free_order=order)
+    nat = kvs.BlockAllocator(N, order)
+    live = [b for b in range(N) if b not in set(order)]
+    for _ in range(800):
+        op = int(r.integers(0, 5))
+        try:
+            if op == 0:
+                try:
+                    b = ref.alloc()
+                except NoBlocksError:
+                    with pytest.raises(kvs.KvsError):
+                        nat.alloc()
+                    continue
+                assert nat.alloc() == b
+                live.append(b)
+            elif live:
+                b = live[int(r.integers(len(live)))]
+                if op == 1:
+                    ref.incref(b); nat.incref(b); live.append(b)
+                elif op == 2:
+                    ref.decref(b); nat.decref(b); live.remove(b)
+                elif op == 3:
+                    try:
+                        nb, c = ref.cow(b)
+                    except NoBlocksError:
+                        with pytest.raises(kvs.KvsError):
+                            nat.cow(b)
+                        continue
+                    assert nat.cow(b) == (nb, c)
+                    if c:
+                        live.remove(b); live.append(nb)
+                else:
+                    assert nat.refcount(b) == ref.ref[b]
+        except RefcountError:
+            raise
+        assert nat.free_list() == list(ref.free)
+        assert nat.num_free() == len(ref.free)
+    for b in range(N):
+        assert nat.refcount(b) == ref.ref[b]

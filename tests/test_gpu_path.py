@@ -1,0 +1,308 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Each test prints the case it is about to run (flushed) so a failing GPU step is named.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from tests._parity import (to_dev_bf16, bf16_to_f64, bf16_bits, i32, assert_rows_close, assert_lse_close,
+                           assert_scores_close, assert_keep_matches, gather_pools)
+
+pytestmark = pytest.mark.gpu
+
+kvs = pytest.importorskip("kv_cache_sparsification_amd")
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+
+
+def _f64(bits):
+    return wl.bf16_bits_to_f64(bits)
+
+
+def run_full_path(w: wl.Workload, layer: int, check_decode_steps, decode_steps: int):
+    """Prefill -> score -> top-k -> compaction -> decode for one single-sequence workload layer."""
+    n = w.fixed_len
+    k_budget = w.budgets[layer]
+    G, alpha, d = w.g, w.alpha, w.d
+    qb, kb, vb, cu = wl.prefill_batch(w, layer, [n])
+    q, k, v = to_dev_bf16(qb), to_dev_bf16(kb), to_dev_bf16(vb)
+    cu_d = i32(cu)
+    qf, kf, vf = _f64(qb), _f64(kb), _f64(vb)
+
+    # ---- step 1: prefill attention + LSE (+ row max and l)
+    rowmax = torch.empty(w.hq, n, device="cuda", dtype=torch.float32)
+    ell = torch.empty_like(rowmax)
+    o, lse = kvs.kvs_prefill_attn_lse(q, k, v, cu_d, n, rowmax=rowmax, ell=ell)
+    O_ref, lse_ref, m_ref, l_ref = oracle.causal_attention(qf, kf, vf)
+    assert_rows_close(bf16_to_f64(o), O_ref, what="prefill O")
+    lse_g = lse.cpu().numpy()
+    assert_lse_close(lse_g, lse_ref)
+    assert_lse_close(rowmax.cpu().numpy(), m_ref, what="rowmax")
+    np.testing.assert_allclose(ell.cpu().numpy(), l_ref, rtol=1e-3, atol=0)
+    # LSE = rowmax + ln(l) on the GPU side too
+    np.testing.assert_allclose(lse_g, rowmax.cpu().numpy() + np.log(ell.cpu().numpy()), rtol=0, atol=1e-4)
+
+    # ---- step 2: window score from the GPU's LSE
+    S = kvs.kvs_window_score(q, k, lse, cu_d, n, alpha)
+    S_ref = oracle.window_score(qf, kf, lse_ref, alpha)
+    S_g = S.cpu().numpy().astype(np.float64)
+    assert_scores_close(S_g, S_ref, G, alpha)
+    np.testing.assert_allclose(S_g.sum(1), G * min(alpha, n), rtol=1e-4)   # each window row sums to one
+
+    # ---- step 3: top-k
+    k_eff = oracle.keep_count(n, k_budget)
+    keep_off = i32([0, k_eff])
+    keep = kvs.kvs_topk_select(S, cu_d, n, alpha, k_budget, keep_off, total_keep=k_eff)
+    keep_g = keep.cpu().numpy().reshape(w.hkv, k_eff)
+    for g in range(w.hkv):
+        # same scores, same decision: bit-exact against the oracle fed the GPU's fp32 scores
+        np.testing.assert_array_equal(keep_g[g], oracle.select_keep(S_g[g], n, alpha, k_budget))
+        assert_keep_matches(keep_g[g], oracle.select_keep(S_ref[g], n, alpha, k_budget), S_ref[g], n, alpha,
+                            k_budget, what=f"keep head {g}")
+
+    # ---- step 4: compaction into blocks from the native allocator (pools poisoned with NaN)
+    total_tokens = k_eff + decode_steps
+    nblocks_needed = oracle.blocks_for(total_tokens)
+    num_blocks = nblocks_needed + 13
+    alloc = kvs.BlockAllocator(num_blocks, list(np.random.default_rng(5).permutation(num_blocks)))
+    table = alloc.alloc_n(oracle.blocks_for(k_eff))
+    max_blocks = nblocks_needed
+    k_pool, v_pool = kvs.new_pools(num_blocks, w.hkv, d)
+    k_pool.view(torch.int16).fill_(0x7FC0)
+    v_pool.view(torch.int16).fill_(0x7FC0)
+    tbl = np.full((1, max_blocks), -1, np.int32)
+    tbl[0, :len(table)] = table
+    kvs.kvs_compact_paged(k, v, cu_d, keep, keep_off, k_eff, k_pool, v_pool, i32(tbl))
+    gk, gv = gather_pools(k_pool, v_pool, table, k_eff)
+    for g in range(w.hkv):
+        np.testing.assert_array_equal(gk[:, g], kb[keep_g[g], g])
+        np.testing.assert_array_equal(gv[:, g], vb[keep_g[g], g])
+
+    # ---- step 5: decode steps with append (write-then-attend)
+    cache_k = [kf[keep_g[g], g] for g in range(w.hkv)]
+    cache_v = [vf[keep_g[g], g] for g in range(w.hkv)]
+    ws = None
+    for step in range(decode_steps):
+        L = k_eff + step + 1
+        if (L - 1) % 16 == 0:
+            table.append(alloc.alloc())
+            tbl[0, :len(table)] = table
+        dq, dk, dv = wl.decode_step_inputs(w, layer, step, 1)
+        ctx = i32([L])
+        lse_d = torch.empty(1, w.hq, device="cuda", dtype=torch.float32)
+        od = kvs.kvs_paged_decode(to_dev_bf16(dq), k_pool, v_pool, i32(tbl), ctx, L, new_k=to_dev_bf16(dk),
+                                  new_v=to_dev_bf16(dv), lse=lse_d)
+        for g in range(w.hkv):
+            cache_k[g] = np.concatenate([cache_k[g], _f64(dk)[0, g][None]])
+            cache_v[g] = np.concatenate([cache_v[g], _f64(dv)[0, g][None]])
+        if step in check_decode_steps:
+            kc = np.stack(cache_k, axis=1)
+            vc = np.stack(cache_v, axis=1)
+            o_ref, l_ref2 = oracle.decode_attention(_f64(dq)[0], kc, vc)
+            assert_rows_close(bf16_to_f64(od)[0], o_ref, what=f"decode step {step}")
+            assert_lse_close(lse_d.cpu().numpy()[0], l_ref2, what=f"decode lse step {step}")
+    # the appended tokens landed in the pool
+    gk, gv = gather_pools(k_pool, v_pool, table, k_eff + decode_steps)
+    last_k = wl.decode_step_inputs(w, layer, decode_steps - 1, 1)[1]
+    np.testing.assert_array_equal(gk[-1], last_k[0])
+    return dict(keep=keep_g, S=S_g)
+
+
+def test_tiny_workload_full_path():
+    w = wl.WORKLOADS[1]
+    _say("tiny workload: n=256 Hq=4 Hkv=2 d=64 alpha=16 k=64, 8 decode steps")
+    out = run_full_path(w, 0, check_decode_steps=set(range(8)), decode_steps=8)
+    # attention sink: token 0 is kept by every head
+    assert all(0 in set(out["keep"][g]) for g in range(w.hkv))
+
+
+def test_llama8b_layer_full_path():
+    w = wl.WORKLOADS[2]
+    _say("8B layer: n=4000 Hq=32 Hkv=8 d=128 alpha=32 k=400, 500 decode steps")
+    out = run_full_path(w, 0, check_decode_steps={0, 1, 15, 16, 17, 100, 249, 250, 498, 499}, decode_steps=500)
+    assert sum(0 in set(out["keep"][g]) for g in range(w.hkv)) >= 6
+
+
+@pytest.mark.parametrize("d,hq,hkv", [(128, 8, 2), (64, 4, 4), (128, 16, 1)])
+def test_prefill_ragged_batch(d, hq, hkv):
+    lengths = [1, 17, 130, 255, 64, 300]
+    _say(f"ragged prefill d={d} hq={hq} hkv={hkv} lengths={lengths}")
+    r = np.random.default_rng(d + hq)
+    T = sum(lengths)
+    qb = wl.f32_to_bf16_bits(r.standard_normal((T, hq, d), dtype=np.float32))
+    kb = wl.f32_to_bf16_bits(r.standard_normal((T, hkv, d), dtype=np.float32))
+    vb = wl.f32_to_bf16_bits(r.standard_normal((T, hkv, d), dtype=np.float32))
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    q, k, v = to_dev_bf16(qb), to_dev_bf16(kb), to_dev_bf16(vb)
+    o, lse = kvs.kvs_prefill_attn_lse(q, k, v, i32(cu), max(lengths))
+    og, lg = bf16_to_f64(o), lse.cpu().numpy()
+    for s, n in enumerate(lengths):
+        a, b = cu[s], cu[s + 1]
+        O_ref, lse_ref, _, _ = oracle.causal_attention(_f64(qb[a:b]), _f64(kb[a:b]), _f64(vb[a:b]))
+        assert_rows_close(og[a:b], O_ref, what=f"O seq {s}")
+        assert_lse_close(lg[:, a:b], lse_ref, what=f"LSE seq {s}")
+        # window score (alpha larger than some prompts) from the oracle's LSE fed to the GPU
+    lse_ref_all = np.zeros((hq, T))
+    for s, n in enumerate(lengths):
+        a, b = cu[s], cu[s + 1]
+        lse_ref_all[:, a:b] = oracle.causal_attention(_f64(qb[a:b]), _f64(kb[a:b]), _f64(vb[a:b]))[1]
+    for alpha in (1, 16, 64):
+        S = kvs.kvs_window_score(q, k, torch.from_numpy(lse_ref_all.astype(np.float32)).cuda(), i32(cu),
+                                 max(lengths), alpha).cpu().numpy()
+        lse32 = lse_ref_all.astype(np.float32).astype(np.float64)
+        for s, n in enumerate(lengths):
+            a, b = cu[s], cu[s + 1]
+            S_ref = oracle.window_score(_f64(qb[a:b]), _f64(kb[a:b]), lse32[:, a:b], alpha)
+            assert_scores_close(S[:, a:b].astype(np.float64), S_ref, hq // hkv, alpha, what=f"S seq {s} a={alpha}")
+
+
+def test_topk_exact_with_ties_and_budgets():
+    """Constructed scores with many ties: the kernel's kept set equals the oracle's exactly."""
+    r = np.random.default_rng(3)
+    lengths = [5, 40, 600, 1000, 4097, 33]
+    hkv = 3
+    T = sum(lengths)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    S = (r.integers(0, 6, size=(hkv, T)) / 64.0).astype(np.float32)
+    S[1] = r.random(T).astype(np.float32)                       # head 1: no ties
+    S[2, :] = 0.25                                              # head 2: everything tied
+    for alpha, kb in ((4, 4), (8, 30), (16, 512), (1, 2000)):
+        _say(f"topk alpha={alpha} k={kb}")
+        kept = [min(kb, n) for n in lengths]
+        off = np.concatenate([[0], np.cumsum(kept)]).astype(np.int32)
+        keep = kvs.kvs_topk_select(torch.from_numpy(S).cuda(), i32(cu), max(lengths), alpha, kb, i32(off),
+                                   total_keep=int(off[-1])).cpu().numpy()
+        for s, n in enumerate(lengths):
+            seg = keep[hkv * off[s]: hkv * off[s + 1]].reshape(hkv, kept[s])
+            for g in range(hkv):
+                ref = oracle.select_keep(S[g, cu[s]:cu[s + 1]].astype(np.float64), n, alpha, kb)
+                np.testing.assert_array_equal(seg[g], ref, err_msg=f"seq {s} head {g} alpha {alpha} k {kb}")
+
+
+def test_compaction_offsets_keep_all_and_partial_blocks():
+    _say("compaction with misaligned destination offsets, keep-all and partial blocks")
+    r = np.random.default_rng(4)
+    lengths = [3, 16, 33, 70]
+    hkv, d = 2, 128
+    T = sum(lengths)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    kb = wl.f32_to_bf16_bits(r.standard_normal((T, hkv, d), dtype=np.float32))
+    vb = wl.f32_to_bf16_bits(r.standard_normal((T, hkv, d), dtype=np.float32))
+    offs = [0, 5, 16, 31]
+    nb = 64
+    k_pool, v_pool = kvs.new_pools(nb, hkv, d)
+    k_pool.view(torch.int16).fill_(0x7FC0)
+    v_pool.view(torch.int16).fill_(0x7FC0)
+    perm = list(r.permutation(nb))
+    max_blocks = 8
+    tbl = np.full((len(lengths), max_blocks), -1, np.int32)
+    tables = []
+    for s, n in enumerate(lengths):
+        t = [perm.pop() for _ in range(oracle.blocks_for(offs[s] + n))]
+        tables.append(t)
+        tbl[s, :len(t)] = t
+    kvs.kvs_compact_paged(to_dev_bf16(kb), to_dev_bf16(vb), i32(cu), None, None, max(lengths), k_pool, v_pool,
+                          i32(tbl), dst_slot_offset=i32(offs))
+    for s, n in enumerate(lengths):
+        gk, gv = gather_pools(k_pool, v_pool, tables[s], offs[s] + n)
+        np.testing.assert_array_equal(gk[offs[s]:], kb[cu[s]:cu[s + 1]])
+        np.testing.assert_array_equal(gv[offs[s]:], vb[cu[s]:cu[s + 1]])
+        assert np.all(gk[:offs[s]] == 0x7FC0) and np.all(gv[:offs[s]] == 0x7FC0)   # earlier slots untouched
+
+
+@pytest.mark.parametrize("d,hq,hkv,lens", [(128, 32, 8, [5000, 1, 17, 900]), (64, 4, 2, [3, 2000]),
+                                           (128, 8, 8, [16, 32, 48])])
+def test_decode_batch_splits_and_merge(d, hq, hkv, lens):
+    """Full-cache decode over several contexts, with and without append; long contexts split and merge."""
+    _say(f"decode batch d={d} hq={hq} hkv={hkv} lens={lens}")
+    r = np.random.default_rng(d + len(lens))
+    B = len(lens)
+    max_ctx = max(lens)
+    max_blocks = oracle.blocks_for(max_ctx)
+    nb = B * max_blocks + 5
+    perm = list(r.permutation(nb))
+    k_pool, v_pool = kvs.new_pools(nb, hkv, d)
+    k_pool.view(torch.int16).fill_(0x7FC0)
+    v_pool.view(torch.int16).fill_(0x7FC0)
+    tbl = np.full((B, max_blocks), -1, np.int32)
+    caches = []
+    for b, L in enumerate(lens):
+        t = [perm.pop() for _ in range(oracle.blocks_for(L))]
+        tbl[b, :len(t)] = t
+        kc = wl.f32_to_bf16_bits(r.standard_normal((L, hkv, d), dtype=np.float32))
+        vc = wl.f32_to_bf16_bits(r.standard_normal((L, hkv, d), dtype=np.float32))
+        cu = i32([0, L])
+        # all L slots; the append case then overwrites slot L-1
+        kvs.kvs_compact_paged(to_dev_bf16(kc), to_dev_bf16(vc), cu, None, None, L, k_pool, v_pool, i32(tbl[b:b + 1]))
+        caches.append((kc, vc))
+    qb = wl.f32_to_bf16_bits(r.standard_normal((B, hq, d), dtype=np.float32))
+    nk = wl.f32_to_bf16_bits(r.standard_normal((B, hkv, d), dtype=np.float32))
+    nv = wl.f32_to_bf16_bits(r.standard_normal((B, hkv, d), dtype=np.float32))
+    ctx = i32(lens)
+    for append in (False, True):
+        lse = torch.empty(B, hq, device="cuda", dtype=torch.float32)
+        o = kvs.kvs_paged_decode(to_dev_bf16(qb), k_pool, v_pool, i32(tbl), ctx, max_ctx,
+                                 new_k=to_dev_bf16(nk) if append else None, new_v=to_dev_bf16(nv) if append else None,
+                                 lse=lse)
+        og, lg = bf16_to_f64(o), lse.cpu().numpy()
+        for b, L in enumerate(lens):
+            kc, vc = _f64(caches[b][0]), _f64(caches[b][1])
+            if append:
+                kc[L - 1], vc[L - 1] = _f64(nk[b]), _f64(nv[b])
+            o_ref, l_ref = oracle.decode_attention(_f64(qb[b]), kc, vc)
+            assert_rows_close(og[b], o_ref, what=f"decode b={b} append={append}")
+            assert_lse_close(lg[b], l_ref, what=f"decode lse b={b} append={append}")
+
+
+def test_copy_blocks_for_copy_on_write():
+    _say("copy_blocks")
+    hkv, d, nb = 2, 128, 10
+    k_pool, v_pool = kvs.new_pools(nb, hkv, d)
+    k_pool.copy_(torch.randn(k_pool.shape, device="cuda").to(torch.bfloat16))
+    v_pool.copy_(torch.randn(v_pool.shape, device="cuda").to(torch.bfloat16))
+    before_k, before_v = k_pool.clone(), v_pool.clone()
+    pairs = i32([[1, 7], [4, 2], [9, 0]])
+    kvs.kvs_copy_blocks(k_pool, v_pool, pairs)
+    torch.cuda.synchronize()
+    for s, t in ((1, 7), (4, 2), (9, 0)):
+        assert torch.equal(k_pool[t].view(torch.int16), before_k[s].view(torch.int16))
+        assert torch.equal(v_pool[t].view(torch.int16), before_v[s].view(torch.int16))
+    for untouched in (1, 3, 4, 5, 6, 8, 9):
+        assert torch.equal(k_pool[untouched].view(torch.int16), before_k[untouched].view(torch.int16))
+
+
+def test_single_token_and_window_only():
+    """n = 1 prompt; budget equal to the window."""
+    _say("n=1 and k == alpha")
+    r = np.random.default_rng(9)
+    hq, hkv, d = 4, 2, 64
+    for n, alpha, kb in ((1, 4, 4), (50, 8, 8)):
+        qb = wl.f32_to_bf16_bits(r.standard_normal((n, hq, d), dtype=np.float32))
+        kk = wl.f32_to_bf16_bits(r.standard_normal((n, hkv, d), dtype=np.float32))
+        vb = wl.f32_to_bf16_bits(r.standard_normal((n, hkv, d), dtype=np.float32))
+        q, k, v = to_dev_bf16(qb), to_dev_bf16(kk), to_dev_bf16(vb)
+        cu = i32([0, n])
+        o, lse = kvs.kvs_prefill_attn_lse(q, k, v, cu, n)
+        O_ref, lse_ref, _, _ = oracle.causal_attention(_f64(qb), _f64(kk), _f64(vb))
+        assert_rows_close(bf16_to_f64(o), O_ref)
+        S = kvs.kvs_window_score(q, k, lse, cu, n, alpha)
+        k_eff = min(kb, n)
+        keep = kvs.kvs_topk_select(S, cu, n, alpha, kb, i32([0, k_eff]), total_keep=k_eff).cpu().numpy()
+        for g in range(hkv):
+            np.testing.assert_array_equal(keep[g * k_eff:(g + 1) * k_eff], np.arange(n - k_eff, n))

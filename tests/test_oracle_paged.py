@@ -28,6 +28,7 @@ def test_worked_example_from_the_page():
     assert len(table) * bs - n == g["expected_unused_slots_paged"]
     assert g["reservation_tokens"] - n == g["expected_unused_slots_reserved"]
     assert list(alloc.free) == [2, 33]
+    assert alloc.ref[0] == 1 and alloc.ref[41] == 1 and alloc.ref[2] == 0   # unlisted blocks are in use
 
 
 @pytest.mark.parametrize("n,off", [(1, 0), (16, 0), (17, 0), (40, 0), (33, 5), (64, 16), (100, 31)])

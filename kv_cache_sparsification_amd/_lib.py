@@ -48,7 +48,19 @@ class KvsError(RuntimeError):
         self.code = code
 
 
+def _hip_runtimes_mapped():
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln})
+    except OSError:
+        return []
+
+
 def _load():
+    # Device memory and streams come from torch, so libkvs must run on the very HIP runtime
+    # torch loaded: import torch first, and the loader then resolves libkvs's libamdhip64
+    # dependency to that already-loaded copy (matched by its soname).
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built: run `python -m kv_cache_sparsification_amd.build` "
                           "(the HIP library is required; there is no fallback path)")
@@ -57,6 +69,9 @@ def _load():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
+    rts = _hip_runtimes_mapped()
+    if len(rts) > 1:
+        raise ImportError(f"two HIP runtimes are loaded in this process ({rts}); libkvs must share torch's")
     return lib
 
 

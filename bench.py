@@ -1,0 +1,335 @@
+"""Benchmark of the KV-sparsity prefill-and-compress path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Workload: one Llama-3-8B-shaped layer, batch 1 - a 4000-token prompt with 32 query heads,
+8 KV heads, head_dim 128, bf16 N(0,1) inputs with attention-sink keys at tokens 0 and 17
+(x20 in channels 7 and 101), window alpha = 32, budget k = 400 (10x compression), 16-token
+blocks, then 500 paged decode steps over the compressed cache.  Inputs are synthetic and
+resident in HBM before the timed region.
+
+One step = the whole hot path once: prefill attention with LSE, window score, top-k,
+compaction into blocks, then 500 decode steps with append.  Every kernel is launched on
+torch's current stream and bracketed by HIP events, so per-kernel durations come from the
+GPU clock of the timed steps.  The printed JSON line carries:
+  value        prefill+compress throughput: prompt tokens / GPU time of the four
+               prefill-side kernels (attention, score, top-k, compaction)
+  decode       paged-decode throughput: generated tokens / GPU time of the 500 decode calls
+  ms_per_step  wall time of one full step (host clock, synchronised on both sides)
+  roofline     the kernel with the largest share of the step's GPU time, against MI355X's
+               published peak (HBM 8 TB/s; bf16 dense MFMA 2.5 PFLOP/s); `rooflines` has all
+  cpu_baseline the fp64 numpy oracle on the host cores (a bounded sample, scaled)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-budget-s", type=float, default=20.0)
+    p.add_argument("--decode-mode", choices=("graph", "loop"), default="graph",
+                   help="graph: the 500 decode steps replay as one captured HIP graph (the launch mode of the "
+                        "pages' serving system); loop: one host launch per step")
+    return p.parse_args()
+
+
+def kernel_source_hash(name: str) -> str:
+    path = os.path.join(ROOT, "kv_cache_sparsification_amd", "csrc", name)
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel_key: str, source: str):
+    """HBM bytes per launch from the committed counter summary, or None if the kernel changed since."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(kernel_key)
+    if not rec or rec.get("source_sha256_16") != kernel_source_hash(source):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this path has no multi-GPU mode (--gpus {args.gpus} refused)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import workloads as wl
+    import kv_cache_sparsification_amd as kvs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = wl.WORKLOADS[2]
+    n, hq, hkv, d, alpha, kb = w.fixed_len, w.hq, w.hkv, w.d, w.alpha, w.budgets[0]
+    steps_dec = w.decode_steps
+    k_eff = min(kb, n)
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---- inputs resident in HBM
+    qb, kbits, vb, cu = wl.prefill_batch(w, 0, [n])
+    q, k, v = up(qb), up(kbits), up(vb)
+    cu_d = torch.from_numpy(cu).to(dev)
+    dec = [wl.decode_step_inputs(w, 0, s, 1) for s in range(steps_dec)]
+    dq = up(np.stack([x[0] for x in dec]))            # [steps][1][hq][d]
+    dk = up(np.stack([x[1] for x in dec]))
+    dv = up(np.stack([x[2] for x in dec]))
+    total_tokens_cache = k_eff + steps_dec
+    nblk = -(-total_tokens_cache // 16)
+    alloc = kvs.BlockAllocator(nblk + 7)
+    table = alloc.alloc_n(nblk)
+    tbl = torch.tensor([table], dtype=torch.int32, device=dev)
+    k_pool, v_pool = kvs.new_pools(nblk + 7, hkv, d, device=dev)
+    ctx = torch.arange(k_eff + 1, k_eff + steps_dec + 1, dtype=torch.int32, device=dev)   # L per step
+    keep_off = torch.tensor([0, k_eff], dtype=torch.int32, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(hq, n, dtype=torch.float32, device=dev)
+    S = torch.empty(hkv, n, dtype=torch.float32, device=dev)
+    keep = torch.empty(hkv * k_eff, dtype=torch.int32, device=dev)
+    od = torch.empty(steps_dec, 1, hq, d, dtype=torch.bfloat16, device=dev)
+    ws_bytes = kvs.kvs_paged_decode_workspace_size(1, hq, hkv, d, total_tokens_cache)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def decode_all(mark):
+        for s in range(steps_dec):
+            L = k_eff + s + 1
+            kvs.kvs_paged_decode(dq[s], k_pool, v_pool, tbl, ctx[s:s + 1], L, new_k=dk[s], new_v=dv[s], o=od[s],
+                                 workspace=ws)
+            mark("decode_end")
+
+    graph = None
+    if args.decode_mode == "graph":
+        # compaction first so the captured steps see a filled cache; capture records launches only
+        kvs.kvs_prefill_attn_lse(q, k, v, cu_d, n, o=o, lse=lse)
+        kvs.kvs_window_score(q, k, lse, cu_d, n, alpha, scores=S)
+        kvs.kvs_topk_select(S, cu_d, n, alpha, kb, keep_off, keep_idx=keep)
+        kvs.kvs_compact_paged(k, v, cu_d, keep, keep_off, k_eff, k_pool, v_pool, tbl)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            decode_all(lambda key: None)          # warm the side stream outside capture
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            decode_all(lambda key: None)
+        torch.cuda.synchronize()
+
+    def one_step(rec):
+        """rec: dict of event lists, or None for warm-up."""
+        def mark(key):
+            if rec is not None:
+                e = ev()
+                e.record(stream)
+                rec.setdefault(key, []).append(e)
+        mark("prefill_begin")
+        kvs.kvs_prefill_attn_lse(q, k, v, cu_d, n, o=o, lse=lse)
+        mark("prefill_end")
+        kvs.kvs_window_score(q, k, lse, cu_d, n, alpha, scores=S)
+        mark("score_end")
+        kvs.kvs_topk_select(S, cu_d, n, alpha, kb, keep_off, keep_idx=keep)
+        mark("topk_end")
+        kvs.kvs_compact_paged(k, v, cu_d, keep, keep_off, k_eff, k_pool, v_pool, tbl)
+        mark("compact_end")
+        if graph is not None:
+            graph.replay()
+            mark("decode_end")
+        else:
+            decode_all(mark)
+
+    for _ in range(args.warmup):
+        one_step(None)
+    torch.cuda.synchronize()
+    recs = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        rec = {}
+        one_step(rec)
+        recs.append(rec)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # ---- per-kernel GPU durations (ms) from the timed steps' events
+    def span(rec, a, b, i=0, j=0):
+        return rec[a][i].elapsed_time(rec[b][j])
+
+    dur = {"prefill_attn_lse": [], "window_score": [], "topk_select": [], "compact_paged": [], "paged_decode": []}
+    pre_phase, dec_phase = [], []
+    for rec in recs:
+        dur["prefill_attn_lse"].append(span(rec, "prefill_begin", "prefill_end"))
+        dur["window_score"].append(span(rec, "prefill_end", "score_end"))
+        dur["topk_select"].append(span(rec, "score_end", "topk_end"))
+        dur["compact_paged"].append(span(rec, "topk_end", "compact_end"))
+        de = rec["decode_end"]
+        if graph is not None:     # one event pair around the 500 captured steps
+            dur["paged_decode"].append(rec["compact_end"][0].elapsed_time(de[0]) / steps_dec)
+        else:
+            dur["paged_decode"].append(rec["compact_end"][0].elapsed_time(de[0]))
+            for s in range(1, len(de)):
+                dur["paged_decode"].append(de[s - 1].elapsed_time(de[s]))
+        pre_phase.append(span(rec, "prefill_begin", "compact_end"))
+        dec_phase.append(rec["compact_end"][0].elapsed_time(de[-1]))
+    avg_ms = {kname: float(np.mean(v)) for kname, v in dur.items()}
+    per_step_ms = {kname: avg_ms[kname] * (steps_dec if kname == "paged_decode" else 1) for kname in avg_ms}
+
+    # ---- algorithmic work per launch
+    P = sum(j + 1 for j in range(n - min(alpha, n), n))        # visited (window row, key) pairs
+    mean_L = k_eff + (steps_dec + 1) / 2.0
+    work = {
+        "prefill_attn_lse": ("mfma", 2.0 * d * hq * n * (n + 1), "TFLOP/s", MFMA_BF16_PEAK_TFLOPS,
+                             "prefill_attn.hip"),
+        "window_score": ("hbm", n * hkv * d * 2 + min(alpha, n) * hq * (2 * d + 4) + 4 * hkv * n, "GB/s",
+                         HBM_PEAK_GBS, "window_score.hip"),
+        "topk_select": ("hbm", 4 * hkv * n + 4 * hkv * k_eff, "GB/s", HBM_PEAK_GBS, "topk_select.hip"),
+        "compact_paged": ("hbm", 8 * k_eff * hkv * d, "GB/s", HBM_PEAK_GBS, "compact_paged.hip"),
+        "paged_decode": ("hbm", 4 * mean_L * hkv * d + 4 * hq * d + 8 * hkv * d + 4 * math.ceil(mean_L / 16),
+                         "GB/s", HBM_PEAK_GBS, "paged_decode.hip"),
+    }
+    rooflines = {}
+    for kname, (bound, amount, unit, peak, src) in work.items():
+        sec = avg_ms[kname] * 1e-3
+        achieved = amount / sec / (1e12 if unit == "TFLOP/s" else 1e9)
+        rooflines[kname] = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                            "frac": round(achieved / peak, 4),
+                            "traffic": measured_traffic(kname, src),
+                            "avg_launch_us": round(avg_ms[kname] * 1e3, 2),
+                            "algorithmic_per_launch": amount}
+    dominant = max(per_step_ms, key=per_step_ms.get)
+
+    prefill_ms = float(np.mean(pre_phase))
+    decode_ms = float(np.mean(dec_phase))
+    value = n / (prefill_ms * 1e-3)
+    decode_tok_s = steps_dec / (decode_ms * 1e-3)
+
+    line = {
+        "metric": "prefill+KV-compress tok/s & paged-decode tok/s, 8B layer n=4000; % roofline",
+        "value": round(value, 1),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16, sink keys x20 at tokens 0 and 17)",
+        "config": {"workload": "llama3-8b-layer n=4000 prompt, 32q/8kv heads, d=128, alpha=32, k=400, "
+                               "16-token blocks, then 500 paged decode steps",
+                   "global_batch": 1, "seq_len": n, "parallelism": "none (1 GPU)"},
+        "value_definition": "prompt tokens / GPU time of prefill attention + window score + top-k + compaction",
+        "decode": {"metric": "paged-decode tok/s", "value": round(decode_tok_s, 1), "unit": "tok/s",
+                   "ms_for_500_steps": round(decode_ms, 4)},
+        "phase_ms": {"prefill_compress": round(prefill_ms, 4), "decode_500": round(decode_ms, 4)},
+        "decode_launch_mode": args.decode_mode,
+        "roofline": {kk: rooflines[dominant][kk] for kk in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
+        "roofline_kernel": dominant,
+        "rooflines": rooflines,
+        "kernel_share_ms_per_step": {kk: round(vv, 4) for kk, vv in per_step_ms.items()},
+    }
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, qb, kbits, vb, dec, args.cpu_budget_s)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(w, qb, kbits, vb, dec, budget_s):
+    """The fp64 oracle, as it stands, on the host cores.
+
+    Prefill+compress: KV-head groups (G query heads + their KV head) of the same n=4000 layer
+    are run one after another until about 70% of the time budget is used (normally all 8);
+    the rate is scaled from the groups done to the full layer.  Decode: oracle decode steps
+    over the compressed cache (all heads), as many of the 500 as fit the rest of the budget.
+    """
+    import numpy as np
+    import oracle
+    import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    n, alpha, kb, G, hkv = w.fixed_len, w.alpha, w.budgets[0], w.g, w.hkv
+    k_eff = min(kb, n)
+    f = wl.bf16_bits_to_f64
+    keeps = []
+    t0 = time.perf_counter()
+    for g in range(hkv):
+        q = f(qb[:, g * G:(g + 1) * G])
+        k = f(kbits[:, g:g + 1])
+        v = f(vb[:, g:g + 1])
+        O, lse, _, _ = oracle.causal_attention(q, k, v)
+        S = oracle.window_score(q, k, lse, alpha)
+        keep = oracle.select_keep(S[0], n, alpha, kb)
+        nbk = oracle.blocks_for(k_eff)
+        pk = np.zeros((nbk, 1, 16, w.d)); pv = np.zeros_like(pk)
+        oracle.compact_into_pool(k, v, keep[None], list(range(nbk)), pk, pv)
+        keeps.append(keep)
+        if time.perf_counter() - t0 > 0.7 * budget_s:
+            break
+    t_pre = time.perf_counter() - t0
+    groups = len(keeps)
+    prefill_tok_s = n / (t_pre / groups * hkv)
+
+    # decode over the compressed cache of every head (heads not reached above keep the
+    # first group's index set: the timing does not depend on which tokens are kept)
+    kf, vf = f(kbits), f(vb)
+    ck = np.stack([kf[keeps[min(g, groups - 1)], g] for g in range(hkv)], axis=1)
+    cv = np.stack([vf[keeps[min(g, groups - 1)], g] for g in range(hkv)], axis=1)
+    t1 = time.perf_counter()
+    done = 0
+    for s, (dqb, dkb, dvb) in enumerate(dec):
+        ck = np.concatenate([ck, f(dkb)], axis=0)
+        cv = np.concatenate([cv, f(dvb)], axis=0)
+        oracle.decode_attention(f(dqb)[0], ck, cv)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    t_dec = time.perf_counter() - t1
+    return {"value": round(prefill_tok_s, 2), "unit": "tok/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"prefill+compress of {groups} of {hkv} KV-head groups of the n={n} layer "
+                      f"({t_pre:.2f} s, scaled to the layer); decode: {done} of {len(dec)} steps ({t_dec:.2f} s)",
+            "decode_value": round(done / t_dec, 2),
+            "cpu_model": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+if __name__ == "__main__":
+    main()

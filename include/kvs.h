@@ -152,9 +152,9 @@ int kvs_compact_paged(const void* k_src, const void* v_src, const int32_t* cu_se
  *      as in kvs_compact_paged; max_ctx >= every L.
  * Out: o [batch][hq][d] bf16; lse_opt [batch][hq] fp32 (natural log) or NULL.
  * Workspace: a device buffer of at least kvs_paged_decode_workspace_size(batch, hq, hkv, d,
- * max_ctx) bytes for split partial results (may be NULL when that size is 0).  The
- * context is split so that about 2048 workgroups run; partial (max, sum, output) triples
- * are merged by a second kernel.
+ * max_ctx) bytes (may be NULL when that size is 0).  The context is split so that about
+ * 2048 workgroups run; each split stores a (max, sum, output) partial there and a second
+ * kernel merges them.  Two calls that share a workspace must not run concurrently.
  * Errors: KVS_E_INVAL on a bad shape or a short workspace; KVS_E_HIP on launch failure.
  */
 size_t kvs_paged_decode_workspace_size(int batch, int hq, int hkv, int d, int max_ctx);

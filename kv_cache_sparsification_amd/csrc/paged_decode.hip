@@ -7,9 +7,11 @@
 // for vLLM", Key techniques 2 (last paragraph): PagedAttention does the decode-side work
 // over the cache the compression left.
 //
-// MI355X form.  Grid (context split, KV head, sequence); a workgroup of 4 wavefronts walks
-// the blocks of its split, wavefront w taking blocks w, w+4, ...  The G query heads of the
-// group are the N columns of the MFMAs, so each K/V byte is read once per KV head:
+// MI355X form.  Grid (context split, KV head, sequence).  A workgroup of W wavefronts walks
+// the blocks of its split, wavefront w taking blocks w, w+W, ..., NB at a time: the table
+// entries of the next NB are read while the current ones are computed, so a wavefront's
+// blocks cost one memory round trip per NB blocks.  The G query heads of the group are the N
+// columns of the MFMAs, so each K/V byte is read once per KV head:
 //   scores^T[16 tokens][16 cols] = K_block[16][d] . Q^T       (bf16 16x16x32, keys as rows)
 //   out^T[d][16 cols]          += V^T[d][16 tokens] . P^T      (bf16 16x16x16, V pool is
 //                                                               channel-major, so V^T loads
@@ -17,178 +19,238 @@
 // The score tile's lane layout (4 tokens of one column per lane) is exactly the B operand
 // layout of the second product, so P never leaves registers.  Online softmax runs per
 // column with two cross-lane maxima per block; the wavefronts of a workgroup merge through
-// LDS, and when the context is split a second kernel merges the (max, sum, output) triples.
+// LDS.
+//
+// Launch plan (see choose_plan).  When a context is split, each split stores a (max, sum,
+// output) partial and a second kernel merges them.  (A merge by the last workgroup to arrive
+// would save that launch, but making the partials of other XCDs visible needs an agent-scope
+// release, i.e. an L2 write-back per workgroup, which costs more on this chip than the
+// launch: measured about 3x slower.)
 #include "kvs_common.h"
 
 namespace kvs {
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kCUs = 256;
 constexpr int kTargetWGs = 2048;
+constexpr int kMaxSplitsMerge = 256;
 
-struct Split {
+struct Plan {
+  int waves;    // wavefronts per workgroup
+  int nb;       // blocks per wavefront in flight
   int bps;      // blocks per split
   int splits;
 };
 
-inline Split choose_split(int batch, int hkv, int max_ctx) {
+// One workgroup per (sequence, KV head) when the batch alone fills the chip (>= 512 pairs) or
+// the context is a single round of blocks; its wavefront count follows the head size and
+// group width so the LDS merge buffer (waves * G * d * 4 bytes) stays within 32 KiB and the
+// blocks in flight fit the registers.  Otherwise the context is split into pieces of >= 4
+// blocks so that about 2048 four-wavefront workgroups run, and a second kernel merges.
+// Measured on MI355X for one 8B layer (1 sequence, 8 KV heads, 400..900 cached tokens, graph
+// replay): 4 blocks per split 9.0 us per step, 8: 9.6, 16: 11.2, 32: 13.4, one workgroup per
+// pair: 11.7 - a single sequence's cache is read fastest by many CUs at once.
+inline Plan choose_plan(int batch, int hq, int hkv, int d, int max_ctx) {
+  const int G = hq / hkv;
   const int nblk = (max_ctx + kBlock - 1) / kBlock;
   const int units = batch * hkv;
+  Plan p;
+  if (d == 64) {
+    p.waves = G <= 4 ? 16 : (G <= 8 ? 8 : 4);
+    p.nb = 2;
+  } else {
+    p.waves = G <= 8 ? 8 : 4;
+    p.nb = 4;
+  }
+  if (units >= 2 * kCUs || nblk <= p.waves) {
+    p.bps = nblk > 0 ? nblk : 1;
+    p.splits = 1;
+    return p;
+  }
+  p.waves = 4;
   const int want = (kTargetWGs + units - 1) / units;
   int bps = (nblk + want - 1) / want;
-  if (bps < kWaves) bps = kWaves;
-  Split s;
-  s.bps = bps;
-  s.splits = nblk > 0 ? (nblk + bps - 1) / bps : 1;
-  return s;
+  if (bps < p.waves) bps = p.waves;
+  if ((nblk + bps - 1) / bps > kMaxSplitsMerge) bps = (nblk + kMaxSplitsMerge - 1) / kMaxSplitsMerge;
+  p.bps = bps;
+  p.splits = (nblk + bps - 1) / bps;
+  return p;
 }
 
-template <int D>
-__global__ __launch_bounds__(kWaves * kWave) void decode_kernel(
+template <int D, int W, int kNB>
+__global__ __launch_bounds__(W * kWave) void decode_kernel(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ k_pool, uint16_t* __restrict__ v_pool, int num_blocks,
     const int32_t* __restrict__ tables, int max_blocks, const int32_t* __restrict__ ctx_lens, int hq, int hkv,
     float c_log2, const uint16_t* __restrict__ new_k, const uint16_t* __restrict__ new_v, uint16_t* __restrict__ o,
     float* __restrict__ lse_out, float* __restrict__ ws, int splits, int bps) {
   constexpr int KS = D / 32;     // k-steps of the score product
   constexpr int MT = D / 16;     // d tiles of the output product
-  __shared__ float s_o[kWaves][D][16];
-  __shared__ float s_m[kWaves][16];
-  __shared__ float s_l[kWaves][16];
+  constexpr int NT = W * kWave;
+  extern __shared__ float smem[];
 
   const int sp = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform
   const int col = lane % 16, grp = lane / 16;
   const int G = hq / hkv;
+  float* s_o = smem;                   // [W][G][D]
+  float* s_m = smem + W * G * D;       // [W][16]
+  float* s_l = s_m + W * 16;           // [W][16]
+  const int blk_begin = sp * bps;
+  const int32_t* table = tables + (size_t)b * max_blocks;
+
+  // Issued together: the first round of table entries (in bounds of the table row, read
+  // before L is known), the context length and the query.
+  int nxt[kNB];   // kNB: blocks per wavefront in flight
+#pragma unroll
+  for (int j = 0; j < kNB; ++j) {
+    const int bi = blk_begin + w + W * j;
+    nxt[j] = bi < max_blocks ? table[bi] : -1;
+  }
   const int L = ctx_lens[b];
   const int nblk = min((L + kBlock - 1) / kBlock, max_blocks);
-  const int blk_begin = sp * bps;
   const int blk_end = min(blk_begin + bps, nblk);
-  if (blk_begin >= blk_end) return;   // empty split: the merge skips it
+  if (blk_begin >= blk_end) return;   // empty split: not merged
 
   // B operand of the score product: Q^T[d][col], col = query head g*G + col (zero if col >= G).
   bf16x8 qf[KS];
 #pragma unroll
   for (int st = 0; st < KS; ++st) {
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (col < G) v = *reinterpret_cast<const u32x4*>(q + ((size_t)b * hq + g * G + col) * D + st * 32 + grp * 8);
-    qf[st] = __builtin_bit_cast(bf16x8, v);
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (col < G) x = *reinterpret_cast<const u32x4*>(q + ((size_t)b * hq + g * G + col) * D + st * 32 + grp * 8);
+    qf[st] = __builtin_bit_cast(bf16x8, x);
   }
 
   const int last_blk = (L - 1) / kBlock, last_slot = (L - 1) % kBlock;
   const bool append = new_k != nullptr && new_v != nullptr;
-  const int32_t* table = tables + (size_t)b * max_blocks;
+  const uint16_t* nk = new_k + ((size_t)b * hkv + g) * D;
+  const uint16_t* nv = new_v + ((size_t)b * hkv + g) * D;
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 acc_o[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc_o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int bi = blk_begin + w; bi < blk_end; bi += kWaves) {
-    const int blk = table[bi];
-    if (blk < 0 || blk >= num_blocks) continue;
-    const uint16_t* kb = k_pool + ((size_t)blk * hkv + g) * kBlock * D;
-    const uint16_t* vb = v_pool + ((size_t)blk * hkv + g) * D * kBlock;
-    const bool app_blk = append && bi == last_blk;
-
-    // K rows (A operand): token = col, d = st*32 + grp*8 .. +8.
-    bf16x8 kf[KS];
+  for (int bi0 = blk_begin + w; bi0 < blk_end; bi0 += W * kNB) {
+    int cur[kNB];
 #pragma unroll
-    for (int st = 0; st < KS; ++st) {
-      const uint16_t* src = (app_blk && col == last_slot) ? new_k + ((size_t)b * hkv + g) * D : kb + col * D;
-      kf[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + st * 32 + grp * 8));
+    for (int j = 0; j < kNB; ++j) {
+      cur[j] = nxt[j];
+      const int bn = bi0 + W * kNB + W * j;            // next round's table entries
+      nxt[j] = bn < blk_end ? table[bn] : -1;
     }
-    // V^T (A operand of the output product): d = mt*16 + col, tokens grp*4 .. +4.
-    short4_t vf[MT];
+    bf16x8 kf[kNB][KS];
+    short4_t vf[kNB][MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      vf[mt] = *reinterpret_cast<const short4_t*>(vb + (size_t)(mt * 16 + col) * kBlock + grp * 4);
-    if (app_blk && grp == last_slot / 4) {
-      const uint16_t* nv = new_v + ((size_t)b * hkv + g) * D;
+    for (int j = 0; j < kNB; ++j) {
+      const int bi = bi0 + W * j;
+      const int blk = cur[j];
+      if (bi >= blk_end || blk < 0 || blk >= num_blocks) continue;
+      const uint16_t* kb = k_pool + ((size_t)blk * hkv + g) * kBlock * D;
+      const uint16_t* vb = v_pool + ((size_t)blk * hkv + g) * D * kBlock;
+      const bool app_blk = append && bi == last_blk;
+      // K rows (A operand): token = col, d = st*32 + grp*8 .. +8; the new token comes from new_k.
+      const uint16_t* ksrc = (app_blk && col == last_slot) ? nk : kb + col * D;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) vf[mt][last_slot % 4] = (short)nv[mt * 16 + col];
-    }
-
-    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+      for (int st = 0; st < KS; ++st)
+        kf[j][st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ksrc + st * 32 + grp * 8));
+      // V^T (A operand of the output product): d = mt*16 + col, tokens grp*4 .. +4.
 #pragma unroll
-    for (int st = 0; st < KS; ++st) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[st], qf[st], sc, 0, 0, 0);
-    // sc[i]: token grp*4 + i of this block against column col.
-    float x[4];
-    float bm = -INFINITY;
+      for (int mt = 0; mt < MT; ++mt)
+        vf[j][mt] = *reinterpret_cast<const short4_t*>(vb + (size_t)(mt * 16 + col) * kBlock + grp * 4);
+      if (app_blk && grp == last_slot / 4) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = bi * kBlock + grp * 4 + i;
-      x[i] = t < L ? sc[i] * c_log2 : -INFINITY;
-      bm = fmaxf(bm, x[i]);
-    }
-    bm = fmaxf(bm, wave_xor(bm, 16));
-    bm = fmaxf(bm, wave_xor(bm, 32));
-    const float m_new = fmaxf(m_run, bm);
-    const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
-    float p[4], psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = __builtin_amdgcn_exp2f(x[i] - m_new);
-      psum += p[i];
-    }
-    l_run = l_run * corr + psum;
-    m_run = m_new;
-    short4_t pb;
-    pb[0] = (short)f32_to_bf16_bits(p[0]);
-    pb[1] = (short)f32_to_bf16_bits(p[1]);
-    pb[2] = (short)f32_to_bf16_bits(p[2]);
-    pb[3] = (short)f32_to_bf16_bits(p[3]);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      acc_o[mt] *= corr;
-      acc_o[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf[mt], pb, acc_o[mt], 0, 0, 0);
-    }
-
-    if (app_blk) {   // keep the appended token in the pool for the next steps
-      if (col == last_slot) {
-        uint16_t* kd = k_pool + ((size_t)blk * hkv + g) * kBlock * D + last_slot * D;
-        const uint16_t* nk = new_k + ((size_t)b * hkv + g) * D;
-#pragma unroll
-        for (int st = 0; st < KS; ++st)
-          *reinterpret_cast<u32x4*>(kd + st * 32 + grp * 8) = *reinterpret_cast<const u32x4*>(nk + st * 32 + grp * 8);
+        for (int mt = 0; mt < MT; ++mt) vf[j][mt][last_slot % 4] = (short)nv[mt * 16 + col];
       }
-      if (grp == last_slot / 4) {
-        uint16_t* vd = v_pool + ((size_t)blk * hkv + g) * D * kBlock;
+    }
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) vd[(size_t)(mt * 16 + col) * kBlock + last_slot] = (uint16_t)vf[mt][last_slot % 4];
+    for (int j = 0; j < kNB; ++j) {
+      const int bi = bi0 + W * j;
+      const int blk = cur[j];
+      if (bi >= blk_end || blk < 0 || blk >= num_blocks) continue;
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < KS; ++st) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[j][st], qf[st], sc, 0, 0, 0);
+      // sc[i]: token grp*4 + i of this block against column col.
+      float x[4];
+      float bm = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = bi * kBlock + grp * 4 + i;
+        x[i] = t < L ? sc[i] * c_log2 : -INFINITY;
+        bm = fmaxf(bm, x[i]);
+      }
+      bm = fmaxf(bm, wave_xor(bm, 16));
+      bm = fmaxf(bm, wave_xor(bm, 32));
+      const float m_new = fmaxf(m_run, bm);
+      const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
+      float p[4], psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(x[i] - m_new);
+        psum += p[i];
+      }
+      l_run = l_run * corr + psum;
+      m_run = m_new;
+      short4_t pb;
+      pb[0] = (short)f32_to_bf16_bits(p[0]);
+      pb[1] = (short)f32_to_bf16_bits(p[1]);
+      pb[2] = (short)f32_to_bf16_bits(p[2]);
+      pb[3] = (short)f32_to_bf16_bits(p[3]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        acc_o[mt] *= corr;
+        acc_o[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf[j][mt], pb, acc_o[mt], 0, 0, 0);
+      }
+      if (append && bi == last_blk) {   // keep the appended token in the pool for later steps
+        if (col == last_slot) {
+          uint16_t* kd = k_pool + ((size_t)blk * hkv + g) * kBlock * D + last_slot * D;
+#pragma unroll
+          for (int st = 0; st < KS; ++st)
+            *reinterpret_cast<u32x4*>(kd + st * 32 + grp * 8) = *reinterpret_cast<const u32x4*>(nk + st * 32 + grp * 8);
+        }
+        if (grp == last_slot / 4) {
+          uint16_t* vd = v_pool + ((size_t)blk * hkv + g) * D * kBlock;
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) vd[(size_t)(mt * 16 + col) * kBlock + last_slot] = (uint16_t)vf[j][mt][last_slot % 4];
+        }
       }
     }
   }
   l_run += wave_xor(l_run, 16);
   l_run += wave_xor(l_run, 32);
 
-  // acc_o[mt][i] is output channel mt*16 + grp*4 + i of column col.
+  // acc_o[mt][i] is output channel mt*16 + grp*4 + i of column col; only real columns are kept.
+  if (col < G) {
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s_o[w][mt * 16 + grp * 4 + i][col] = acc_o[mt][i];
-  if (grp == 0) {
-    s_m[w][col] = m_run;
-    s_l[w][col] = l_run;
+      for (int i = 0; i < 4; ++i) s_o[((size_t)w * G + col) * D + mt * 16 + grp * 4 + i] = acc_o[mt][i];
+    if (grp == 0) {
+      s_m[w * 16 + col] = m_run;
+      s_l[w * 16 + col] = l_run;
+    }
   }
   __syncthreads();
 
-  // Merge the 4 wavefronts: thread -> (column, channel) pairs.
-  for (int e = tid; e < G * D; e += kWaves * kWave) {
+  // Merge the W wavefronts: thread -> (column, channel) pairs.
+  const int used = min((nblk + bps - 1) / bps, splits);   // non-empty splits of this sequence
+  for (int e = tid; e < G * D; e += NT) {
     const int c = e / D, dd = e % D;
     float m = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v) m = fmaxf(m, s_m[v][c]);
+    for (int v = 0; v < W; ++v) m = fmaxf(m, s_m[v * 16 + c]);
     float l = 0.f, acc = 0.f;
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v) {
-      const float wgt = __builtin_amdgcn_exp2f(s_m[v][c] - m);   // empty wavefront: exp2(-inf) = 0
-      l += s_l[v][c] * wgt;
-      acc += s_o[v][dd][c] * wgt;
+    for (int v = 0; v < W; ++v) {
+      const float wgt = __builtin_amdgcn_exp2f(s_m[v * 16 + c] - m);   // idle wavefront: exp2(-inf) = 0
+      l += s_l[v * 16 + c] * wgt;
+      acc += s_o[((size_t)v * G + c) * D + dd] * wgt;
     }
     const int h = g * G + c;
-    if (splits == 1) {
+    if (used == 1) {
       o[((size_t)b * hq + h) * D + dd] = (uint16_t)f32_to_bf16_bits(acc / l);
-      if (lse_out && dd == 0) lse_out[(size_t)b * hq + h] = (m + __log2f(l)) * kLn2;
+      if (lse_out && dd == 0) lse_out[(size_t)b * hq + h] = (m + log2f(l)) * kLn2;
     } else {
       float* part = ws + (((size_t)b * hq + h) * splits + sp) * (D + 2);
       part[2 + dd] = acc;
@@ -200,26 +262,55 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_kernel(
   }
 }
 
-// Merge of the split partials: one workgroup per (query head, sequence), one thread per channel.
+// Merge of the split partials: one workgroup per (KV head, sequence) covers the G query
+// heads.  Each thread takes splits 16 at a time and issues all their loads (its output
+// channel plus the (max, sum) pair, shared with its neighbours through L1) before using any,
+// then folds the chunk into a running (max, sum, output) - one memory round trip per 16
+// splits instead of one per split.
 template <int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict__ ws, const int32_t* __restrict__ ctx_lens,
-                                                        int hq, int splits, int bps, uint16_t* __restrict__ o,
-                                                        float* __restrict__ lse_out) {
-  const int h = blockIdx.x, b = blockIdx.y, dd = threadIdx.x;
+__global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restrict__ ws,
+                                                           const int32_t* __restrict__ ctx_lens, int hq, int hkv,
+                                                           int max_blocks, int splits, int bps,
+                                                           uint16_t* __restrict__ o, float* __restrict__ lse_out) {
+  constexpr int C = 16;
+  const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int G = hq / hkv;
   const int L = ctx_lens[b];
-  const int nblk = (L + kBlock - 1) / kBlock;
+  const int nblk = min((L + kBlock - 1) / kBlock, max_blocks);
   const int used = min((nblk + bps - 1) / bps, splits);
-  const float* part = ws + ((size_t)b * hq + h) * splits * (D + 2);
-  float m = -INFINITY;
-  for (int sp = 0; sp < used; ++sp) m = fmaxf(m, part[sp * (D + 2)]);
-  float l = 0.f, acc = 0.f;
-  for (int sp = 0; sp < used; ++sp) {
-    const float wgt = __builtin_amdgcn_exp2f(part[sp * (D + 2)] - m);
-    l += part[sp * (D + 2) + 1] * wgt;
-    acc += part[sp * (D + 2) + 2 + dd] * wgt;
+  if (used <= 1) return;                      // written directly by the decode kernel
+  const float* part0 = ws + ((size_t)b * hq + g * G) * splits * (D + 2);
+  for (int e = tid; e < G * D; e += 256) {
+    const int c = e / D, dd = e % D;
+    const float* part = part0 + (size_t)c * splits * (D + 2);
+    float M = -INFINITY, l = 0.f, acc = 0.f;
+    for (int sp0 = 0; sp0 < used; sp0 += C) {
+      float mv[C], lv[C], ov[C];
+#pragma unroll
+      for (int i = 0; i < C; ++i) {
+        const bool in = sp0 + i < used;
+        const float* ps = part + (size_t)(in ? sp0 + i : 0) * (D + 2);
+        mv[i] = in ? ps[0] : -INFINITY;
+        lv[i] = in ? ps[1] : 0.f;
+        ov[i] = in ? ps[2 + dd] : 0.f;
+      }
+      float cm = M;
+#pragma unroll
+      for (int i = 0; i < C; ++i) cm = fmaxf(cm, mv[i]);
+      const float corr = __builtin_amdgcn_exp2f(M - cm);   // first chunk: exp2(-inf) = 0
+      l *= corr;
+      acc *= corr;
+#pragma unroll
+      for (int i = 0; i < C; ++i) {
+        const float wgt = __builtin_amdgcn_exp2f(mv[i] - cm);
+        l += lv[i] * wgt;
+        acc += ov[i] * wgt;
+      }
+      M = cm;
+    }
+    o[((size_t)b * hq + g * G + c) * D + dd] = (uint16_t)f32_to_bf16_bits(acc / l);
+    if (lse_out && dd == 0) lse_out[(size_t)b * hq + g * G + c] = (M + log2f(l)) * kLn2;
   }
-  o[((size_t)b * hq + h) * D + dd] = (uint16_t)f32_to_bf16_bits(acc / l);
-  if (lse_out && dd == 0) lse_out[(size_t)b * hq + h] = (m + __log2f(l)) * kLn2;
 }
 
 }  // namespace
@@ -227,11 +318,41 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict
 
 using namespace kvs;
 
+// Workspace: partials [batch][hq][splits][d + 2] fp32 = (max, sum, unnormalised output).
 extern "C" size_t kvs_paged_decode_workspace_size(int batch, int hq, int hkv, int d, int max_ctx) {
-  if (batch <= 0 || hq <= 0 || hkv <= 0 || max_ctx <= 0 || d <= 0) return 0;
-  const Split s = choose_split(batch, hkv, max_ctx);
-  if (s.splits <= 1) return 0;
-  return (size_t)batch * hq * s.splits * (d + 2) * sizeof(float);
+  if (batch <= 0 || hq <= 0 || hkv <= 0 || hq % hkv || max_ctx <= 0 || d <= 0) return 0;
+  const Plan p = choose_plan(batch, hq, hkv, d, max_ctx);
+  if (p.splits <= 1) return 0;
+  return (size_t)batch * hq * p.splits * (d + 2) * sizeof(float);
+}
+
+template <int D, int W, int NB>
+static void launch_one(const Plan& p, dim3 grid, size_t lds, hipStream_t st, const uint16_t* q, uint16_t* kp,
+                       uint16_t* vp, int num_blocks, const int32_t* tables, int max_blocks, const int32_t* ctx, int hq,
+                       int hkv, float c, const uint16_t* nk, const uint16_t* nv, uint16_t* o, float* lse, float* ws) {
+  hipLaunchKernelGGL((decode_kernel<D, W, NB>), grid, dim3(W * kWave), lds, st, q, kp, vp, num_blocks, tables,
+                     max_blocks, ctx, hq, hkv, c, nk, nv, o, lse, ws, p.splits, p.bps);
+}
+
+template <int D>
+static void launch_decode(const Plan& p, dim3 grid, size_t lds, hipStream_t st, const uint16_t* q, uint16_t* kp,
+                          uint16_t* vp, int num_blocks, const int32_t* tables, int max_blocks, const int32_t* ctx,
+                          int hq, int hkv, float c, const uint16_t* nk, const uint16_t* nv, uint16_t* o, float* lse,
+                          float* ws) {
+  constexpr int NB = D == 64 ? 2 : 4;
+  if constexpr (D == 64) {   // 16 wavefronts only where their registers hold NB blocks
+    if (p.waves == 16) {
+      launch_one<D, 16, NB>(p, grid, lds, st, q, kp, vp, num_blocks, tables, max_blocks, ctx, hq, hkv, c, nk, nv, o,
+                            lse, ws);
+      return;
+    }
+  }
+  if (p.waves == 8)
+    launch_one<D, 8, NB>(p, grid, lds, st, q, kp, vp, num_blocks, tables, max_blocks, ctx, hq, hkv, c, nk, nv, o,
+                         lse, ws);
+  else
+    launch_one<D, 4, NB>(p, grid, lds, st, q, kp, vp, num_blocks, tables, max_blocks, ctx, hq, hkv, c, nk, nv, o,
+                         lse, ws);
 }
 
 extern "C" int kvs_paged_decode(const void* q, void* k_pool, void* v_pool, int num_blocks, const int32_t* block_tables,
@@ -247,33 +368,35 @@ extern "C" int kvs_paged_decode(const void* q, void* k_pool, void* v_pool, int n
                 max_ctx);
   if ((long long)max_blocks * kBlock < max_ctx) return fail(KVS_E_INVAL, "kvs_paged_decode: max_blocks*16 < max_ctx");
   if (batch == 0) return KVS_OK;
-  const Split sp = choose_split(batch, hkv, max_ctx);
+  const Plan p = choose_plan(batch, hq, hkv, d, max_ctx);
   const size_t need = kvs_paged_decode_workspace_size(batch, hq, hkv, d, max_ctx);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(KVS_E_INVAL, "kvs_paged_decode: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   const float c = scale * kLog2e;
-  dim3 grid(sp.splits, hkv, batch);
+  const int G = hq / hkv;
+  const size_t lds = ((size_t)p.waves * G * d + 2 * (size_t)p.waves * 16) * sizeof(float);
+  dim3 grid(p.splits, hkv, batch);
   auto* qq = static_cast<const uint16_t*>(q);
   auto* kp = static_cast<uint16_t*>(k_pool);
   auto* vp = static_cast<uint16_t*>(v_pool);
   auto* nk = static_cast<const uint16_t*>(new_k);
   auto* nv = static_cast<const uint16_t*>(new_v);
   auto* oo = static_cast<uint16_t*>(o);
-  auto* ws = static_cast<float*>(workspace);
+  float* ws = static_cast<float*>(workspace);
   hipStream_t st = as_stream(stream);
   if (d == 128)
-    hipLaunchKernelGGL(decode_kernel<128>, grid, dim3(kWaves * kWave), 0, st, qq, kp, vp, num_blocks, block_tables,
-                       max_blocks, ctx_lens, hq, hkv, c, nk, nv, oo, lse_opt, ws, sp.splits, sp.bps);
+    launch_decode<128>(p, grid, lds, st, qq, kp, vp, num_blocks, block_tables, max_blocks, ctx_lens, hq, hkv, c, nk, nv,
+                       oo, lse_opt, ws);
   else
-    hipLaunchKernelGGL(decode_kernel<64>, grid, dim3(kWaves * kWave), 0, st, qq, kp, vp, num_blocks, block_tables,
-                       max_blocks, ctx_lens, hq, hkv, c, nk, nv, oo, lse_opt, ws, sp.splits, sp.bps);
+    launch_decode<64>(p, grid, lds, st, qq, kp, vp, num_blocks, block_tables, max_blocks, ctx_lens, hq, hkv, c, nk, nv,
+                      oo, lse_opt, ws);
   int rc = launch_status("kvs_paged_decode");
-  if (rc != KVS_OK || sp.splits == 1) return rc;
+  if (rc != KVS_OK || p.splits == 1) return rc;
   if (d == 128)
-    hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(hq, batch), dim3(128), 0, st, ws, ctx_lens, hq, sp.splits, sp.bps,
-                       oo, lse_opt);
+    hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(hkv, batch), dim3(256), 0, st, ws, ctx_lens, hq, hkv, max_blocks,
+                       p.splits, p.bps, oo, lse_opt);
   else
-    hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(hq, batch), dim3(64), 0, st, ws, ctx_lens, hq, sp.splits, sp.bps,
-                       oo, lse_opt);
+    hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(hkv, batch), dim3(256), 0, st, ws, ctx_lens, hq, hkv, max_blocks,
+                       p.splits, p.bps, oo, lse_opt);
   return launch_status("kvs_paged_decode (merge)");
 }

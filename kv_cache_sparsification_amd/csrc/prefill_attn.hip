@@ -15,10 +15,13 @@
 //     scale of O is a per-lane scalar, and the exponentiated scores are already in the B
 //     operand layout of O^T = V^T . P^T: P never goes through LDS.
 //   * K tiles (64 keys) are staged row-major in LDS; V tiles are stored transposed (V^T,
-//     channel rows of 64 keys) so the A operand of the second product is two 8-byte reads.
-//     The transposing store maps lanes so a wavefront's 32-bit writes spread over all banks.
+//     channel rows of 64 keys).  The key order of the first product is permuted so that each
+//     lane's share of P^T is 8 consecutive keys: the A operand of the second product is then a
+//     single 16-byte LDS read.  The next tile's global loads are issued before the current tile
+//     is computed.
 //   * Q stays in registers for the whole key loop.  Wavefronts whose rows all precede a key
-//     tile skip it (causal); only the diagonal tile is masked.
+//     tile skip it (causal); only the diagonal tile is masked, and O is rescaled only when a
+//     row maximum grows by more than 2^8 (wave-uniform branches).
 //   * Workgroups are remapped so that each XCD (8 per chip, each with its own L2) works on
 //     one KV head at a time, heaviest (last) query tiles first.
 #include "kvs_common.h"
@@ -32,6 +35,11 @@ constexpr int kBK = 64;    // keys per tile
 constexpr int kRowsPerWave = 32;
 constexpr int kXcds = 8;
 
+// MFMA row m of the S^T product holds key kappa(m) of its 32-key tile: bits 2 and 3 of m are
+// swapped.  With that order the 16 scores a lane half gets back cover 8 consecutive keys per
+// 16-key step, so P^T needs no shuffling and the matching V^T operand is one 16-byte read.
+__device__ __forceinline__ int kappa(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
 template <int D>
 __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -39,10 +47,11 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_kernel(
     uint16_t* __restrict__ o, float* __restrict__ lse, float* __restrict__ rowmax, float* __restrict__ ell, int nqt,
     int total_items) {
   constexpr int KSTR = D + 8;    // bf16 per K row in LDS (16-byte pad)
-  constexpr int VSTR = kBK + 4;  // bf16 per V^T row in LDS (8-byte aligned, bank-spread)
+  constexpr int VSTR = kBK + 8;  // bf16 per V^T row in LDS: 36 words, 16 consecutive rows on distinct banks
   constexpr int ST1 = D / 16;    // k-steps of S^T = K Q^T
   constexpr int MT2 = D / 32;    // channel tiles of O^T
   constexpr int KS2 = kBK / 16;  // k-steps of O^T = V^T P^T
+  constexpr int NT = kWaves * kWave;
   __shared__ __attribute__((aligned(16))) uint16_t ks[kBK * KSTR];
   __shared__ __attribute__((aligned(16))) uint16_t vt[D * VSTR];
 
@@ -62,7 +71,8 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_kernel(
   const int r0 = qt * kBQ;
   if (r0 >= n) return;
 
-  const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform: branches on it stay scalar
   const int col = lane % 32, half = lane / 32;
   const int R = r0 + w * kRowsPerWave;   // first row of this wavefront
   const int row = R + col;               // this lane's query row (N index)
@@ -76,7 +86,11 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_kernel(
     qf[st] = __builtin_bit_cast(bf16x8, x);
   }
 
-  float m_run = -INFINITY;   // running max of the log2-scaled scores of `row`
+  // m_ref is the reference max (log2-scaled) the exponentials are taken against; it moves only
+  // when some row's true maximum exceeds it by more than kLazy, so most tiles skip the rescale
+  // of O (p may then reach 2^kLazy, harmless in fp32 and bf16).  m_true is the exact row max.
+  constexpr float kLazy = 8.f;
+  float m_ref = -INFINITY, m_true = -INFINITY;
   float l_lane = 0.f;        // this lane's part of the running sum (16 of every 32 keys)
   f32x16 acc_o[MT2];
 #pragma unroll
@@ -84,36 +98,97 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_kernel(
 
   const int kend = min(r0 + kBQ, n);
   const int ntiles = (kend + kBK - 1) / kBK;
-  for (int kt = 0; kt < ntiles; ++kt) {
+  const size_t tile_stride = (size_t)kBK * hkv * D;   // elements between consecutive key tiles
+
+  // ---- Global -> register staging of one K/V tile, prefetched one tile ahead.
+  // K item e: row r = e / (D/8), 16-byte chunk cc = e % (D/8): 16 lanes read one 256-byte row.
+  // V item e: key pair p and chunk cc, 16 lanes per row as well; stored transposed.
+  constexpr int KCH = kBK * (D / 8) / NT;
+  constexpr int VIT = (kBK / 2) * (D / 8) / NT;
+  const uint16_t* kp0[KCH];
+  const uint16_t* vp0[VIT];
+  int krow_of[KCH], vkey_of[VIT];
+#pragma unroll
+  for (int it = 0; it < KCH; ++it) {
+    const int e = it * NT + tid;
+    const int r = e / (D / 8), cc = e % (D / 8);
+    krow_of[it] = r;
+    kp0[it] = k + ((size_t)(base + r) * hkv + g) * D + cc * 8;
+  }
+#pragma unroll
+  for (int it = 0; it < VIT; ++it) {
+    const int e = it * NT + tid;
+    const int wv = e / kWave, ln = e % kWave;
+    const int p = (wv % 2) * 16 + ln % 16;
+    const int cc = (wv / 2) * 4 + ln / 16;
+    vkey_of[it] = 2 * p;
+    vp0[it] = v + ((size_t)(base + 2 * p) * hkv + g) * D + cc * 8;
+  }
+  u32x4 kreg[KCH], va[VIT], vb[VIT];
+  auto load_tile = [&](int kt) {
+    const size_t off = (size_t)kt * tile_stride;
     const int kb = kt * kBK;
-    __syncthreads();   // the previous tile is consumed
-    // K tile -> ks (row-major), zero past the prompt.
-    for (int e = tid; e < kBK * (D / 8); e += kWaves * kWave) {
-      const int r = e / (D / 8), cc = e % (D / 8);
-      const int key = kb + r;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (key < n) x = *reinterpret_cast<const u32x4*>(k + ((size_t)(base + key) * hkv + g) * D + cc * 8);
-      *reinterpret_cast<u32x4*>(&ks[r * KSTR + cc * 8]) = x;
+    if (kb + kBK <= n) {     // wave-uniform: whole tile inside the prompt
+#pragma unroll
+      for (int it = 0; it < KCH; ++it) kreg[it] = *reinterpret_cast<const u32x4*>(kp0[it] + off);
+#pragma unroll
+      for (int it = 0; it < VIT; ++it) {
+        va[it] = *reinterpret_cast<const u32x4*>(vp0[it] + off);
+        vb[it] = *reinterpret_cast<const u32x4*>(vp0[it] + off + (size_t)hkv * D);
+      }
+    } else {                 // ragged last tile: zero past the prompt
+#pragma unroll
+      for (int it = 0; it < KCH; ++it) {
+        kreg[it] = u32x4{0u, 0u, 0u, 0u};
+        if (kb + krow_of[it] < n) kreg[it] = *reinterpret_cast<const u32x4*>(kp0[it] + off);
+      }
+#pragma unroll
+      for (int it = 0; it < VIT; ++it) {
+        va[it] = u32x4{0u, 0u, 0u, 0u};
+        vb[it] = u32x4{0u, 0u, 0u, 0u};
+        if (kb + vkey_of[it] < n) va[it] = *reinterpret_cast<const u32x4*>(vp0[it] + off);
+        if (kb + vkey_of[it] + 1 < n) vb[it] = *reinterpret_cast<const u32x4*>(vp0[it] + off + (size_t)hkv * D);
+      }
     }
-    // V tile -> vt (transposed).  Item = (key pair p, 8-channel chunk cc); a wavefront covers
-    // 16 pairs x 4 chunks so its 32-bit stores land on distinct banks.
-    for (int e = tid; e < (kBK / 2) * (D / 8); e += kWaves * kWave) {
+  };
+  // K rows go to LDS as loaded.  The row stride (D + 8 bf16 = 4 banks past a multiple of 64)
+  // keeps the 16-byte reads of any 16 distinct rows mod 16 on distinct banks, which is what
+  // the kappa-ordered GEMM reads touch.
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int it = 0; it < KCH; ++it) {
+      const int e = it * NT + tid;
+      const int r = e / (D / 8), cc = e % (D / 8);
+      *reinterpret_cast<u32x4*>(&ks[r * KSTR + cc * 8]) = kreg[it];
+    }
+#pragma unroll
+    for (int it = 0; it < VIT; ++it) {
+      const int e = it * NT + tid;
       const int wv = e / kWave, ln = e % kWave;
       const int p = (wv % 2) * 16 + ln % 16;
       const int cc = (wv / 2) * 4 + ln / 16;
-      const int key0 = kb + 2 * p;
-      u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-      if (key0 < n) a = *reinterpret_cast<const u32x4*>(v + ((size_t)(base + key0) * hkv + g) * D + cc * 8);
-      if (key0 + 1 < n) b = *reinterpret_cast<const u32x4*>(v + ((size_t)(base + key0 + 1) * hkv + g) * D + cc * 8);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const uint32_t lo = (j % 2 == 0) ? (a[j / 2] & 0xffffu) : (a[j / 2] >> 16);
-        const uint32_t hi = (j % 2 == 0) ? (b[j / 2] & 0xffffu) : (b[j / 2] >> 16);
-        *reinterpret_cast<uint32_t*>(&vt[(cc * 8 + j) * VSTR + 2 * p]) = lo | (hi << 16);
+        // channel cc*8 + j of keys 2p (low half) and 2p + 1 (high half)
+        const uint32_t word = (j % 2 == 0)
+            ? __builtin_amdgcn_perm(vb[it][j / 2], va[it][j / 2], 0x05040100u)
+            : __builtin_amdgcn_perm(vb[it][j / 2], va[it][j / 2], 0x07060302u);
+        *reinterpret_cast<uint32_t*>(&vt[(cc * 8 + j) * VSTR + 2 * p]) = word;
       }
     }
+  };
+
+  // GEMM-1 A operand source rows: lane col reads K row kappa(col) of each 32-key M tile.
+  const int krow = kappa(col);
+
+  load_tile(0);
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int kb = kt * kBK;
+    __syncthreads();   // the previous tile is consumed
+    store_tile();
     __syncthreads();
-    if (kb > R + kRowsPerWave - 1) continue;   // every row of this wavefront precedes the tile
+    if (kt + 1 < ntiles) load_tile(kt + 1);   // in flight while this tile is computed
+    if (kb > R + kRowsPerWave - 1) continue;  // every row of this wavefront precedes the tile
 
     // ---- S^T tile: 64 keys x 32 rows as two 32x32 products over d.
     f32x16 sacc[2];
@@ -122,41 +197,46 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_kernel(
       sacc[mt] = f32x16{};
 #pragma unroll
       for (int st = 0; st < ST1; ++st) {
-        const u32x4 ka = *reinterpret_cast<const u32x4*>(&ks[(mt * 32 + col) * KSTR + st * 16 + half * 8]);
+        const int chunk = 2 * st + half;
+        const u32x4 ka = *reinterpret_cast<const u32x4*>(&ks[(mt * 32 + krow) * KSTR + chunk * 8]);
         sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka), qf[st], sacc[mt], 0, 0, 0);
       }
     }
-    // sacc[mt][i] is key kb + 32*mt + 8*(i/4) + 4*half + i%4 against `row`.
-    const bool diag = kb + kBK - 1 > R;
+    // sacc[mt][i] is key kb + 32*mt + 16*(i/8) + 8*half + i%8 against `row` (raw dot products).
+    if (kb + kBK - 1 > R) {   // diagonal tile (wave-uniform): mask keys past the row
+      const int lim = row - kb - 8 * half;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (mt * 32 + 16 * (i / 8) + (i % 8) > lim) sacc[mt][i] = -INFINITY;
+    }
     float bm = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = sacc[mt][i] * c_log2;
-        if (diag) {
-          const int key = kb + mt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-          x = key <= row ? x : -INFINITY;
-        }
-        sacc[mt][i] = x;
-        bm = fmaxf(bm, x);
-      }
-    bm = fmaxf(bm, wave_xor(bm, 32));
-    const float m_new = fmaxf(m_run, bm);
-    const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
+      for (int i = 0; i < 16; ++i) bm = fmaxf(bm, sacc[mt][i]);
+    bm = fmaxf(bm, wave_xor(bm, 32)) * c_log2;
+    m_true = fmaxf(m_true, bm);
+    if (__ballot(m_true > m_ref + kLazy) != 0ull) {   // some row moved too far: rescale (rare)
+      const float corr = __builtin_amdgcn_exp2f(m_ref - m_true);
+      m_ref = m_true;
+      l_lane *= corr;
+#pragma unroll
+      for (int mt = 0; mt < MT2; ++mt) acc_o[mt] *= corr;
+    }
     float psum = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(sacc[mt][i] - m_new);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][i], c_log2, -m_ref));
         sacc[mt][i] = p;
         psum += p;
       }
-    l_lane = l_lane * corr + psum;
-    m_run = m_new;
+    l_lane += psum;
 
-    // P^T as B operands: k-step ks covers keys 16*ks + {4*half + 0..3, 8 + 4*half + 0..3}.
+    // P^T as B operands: k-step ks2 holds keys 16*ks2 + 8*half + 0..7 in order.
     bf16x8 pf[KS2];
 #pragma unroll
     for (int ks2 = 0; ks2 < KS2; ++ks2) {
@@ -168,20 +248,16 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_kernel(
     }
 #pragma unroll
     for (int mt = 0; mt < MT2; ++mt) {
-      acc_o[mt] *= corr;
 #pragma unroll
       for (int ks2 = 0; ks2 < KS2; ++ks2) {
-        const uint16_t* vrow = &vt[(mt * 32 + col) * VSTR + ks2 * 16 + half * 4];
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
-        const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
-        acc_o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va), pf[ks2], acc_o[mt], 0, 0, 0);
+        const u32x4 va2 = *reinterpret_cast<const u32x4*>(&vt[(mt * 32 + col) * VSTR + ks2 * 16 + half * 8]);
+        acc_o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va2), pf[ks2], acc_o[mt], 0, 0, 0);
       }
     }
   }
 
-  // ---- epilogue: O = acc / l, LSE = ln 2 * (m + log2 l)
-  const float l = l_lane + wave_xor(l_lane, 32);
+  // ---- epilogue: O = acc / l, LSE = ln 2 * (m_ref + log2 l)
+  const float l = l_lane + wave_xor(l_lane, 32);   // sum of exp2(x - m_ref)
   if (row < n) {
     const float inv = 1.f / l;
     uint16_t* orow = o + ((size_t)(base + row) * hq + h) * D;
@@ -197,9 +273,9 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_kernel(
       }
     if (half == 0) {
       const size_t li = (size_t)h * total_tokens + base + row;
-      lse[li] = (m_run + log2f(l)) * kLn2;
-      if (rowmax) rowmax[li] = m_run * kLn2;
-      if (ell) ell[li] = l;
+      lse[li] = (m_ref + log2f(l)) * kLn2;
+      if (rowmax) rowmax[li] = m_true * kLn2;
+      if (ell) ell[li] = l * __builtin_amdgcn_exp2f(m_ref - m_true);   // sum of exp(s - rowmax)
     }
   }
 }

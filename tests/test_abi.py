@@ -48,9 +48,9 @@ def test_host_validation_rejects_before_launch():
     assert b"alpha" in L.kvs_last_error()
     assert L.kvs_compact_paged(fake, fake, fake, 1, 2, 100, None, None, 8, fake, fake, 4, fake, 4, None, None) == -1
     assert L.kvs_copy_blocks(fake, fake, 4, 2, 128, None, 3, None) == -1
-    ws = L.kvs_paged_decode_workspace_size(1, 32, 8, 128, 4000)
+    ws = L.kvs_paged_decode_workspace_size(1, 32, 8, 128, 30000)
     assert ws > 0
-    assert L.kvs_paged_decode(fake, fake, fake, 64, fake, 300, fake, 1, 4000, 32, 8, 128, 0.1, None, None, fake,
+    assert L.kvs_paged_decode(fake, fake, fake, 64, fake, 2000, fake, 1, 30000, 32, 8, 128, 0.1, None, None, fake,
                               None, fake, ws - 1, None) == -1
     assert b"workspace" in L.kvs_last_error()
     assert L.kvs_paged_decode(fake, fake, fake, 64, fake, 10, fake, 1, 4000, 32, 8, 128, 0.1, None, None, fake,
@@ -62,9 +62,11 @@ def test_host_validation_rejects_before_launch():
 
 def test_workspace_size_policy():
     L = kvs.lib
-    # short contexts at large batch need no split; long single-sequence contexts do
-    assert L.kvs_paged_decode_workspace_size(64, 32, 8, 128, 64) == 0
+    # a batch that fills the chip, or one round of blocks, needs no split; a single sequence does
+    assert L.kvs_paged_decode_workspace_size(64, 32, 8, 128, 4000) == 0
+    assert L.kvs_paged_decode_workspace_size(1, 32, 8, 128, 100) == 0
     assert L.kvs_paged_decode_workspace_size(1, 32, 8, 128, 900) > 0
+    assert L.kvs_paged_decode_workspace_size(1, 32, 8, 128, 30000) > 0
     assert L.kvs_paged_decode_workspace_size(0, 32, 8, 128, 900) == 0
 
 

@@ -44,6 +44,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=20.0)
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of MIB mebibytes three times (reference for the "
+                        "FETCH_SIZE / WRITE_SIZE counters) and exit")
     p.add_argument("--decode-mode", choices=("graph", "loop"), default="graph",
                    help="graph: the 500 decode steps replay as one captured HIP graph (the launch mode of the "
                         "pages' serving system); loop: one host launch per step")
@@ -80,6 +83,16 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        nbytes = args.copy_calibration << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read": nbytes, "bytes_written": nbytes,
+                          "launches": 3}), flush=True)
+        return
     w = wl.WORKLOADS[2]
     n, hq, hkv, d, alpha, kb = w.fixed_len, w.hq, w.hkv, w.d, w.alpha, w.budgets[0]
     steps_dec = w.decode_steps

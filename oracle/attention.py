@@ -34,15 +34,26 @@ def _check(q, k, v):
 
 
 def causal_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: Optional[float] = None,
-                     rows: Optional[Sequence[int]] = None, row_chunk: int = 2048):
+                     rows: Optional[Sequence[int]] = None, row_chunk: int = 2048, q_holds_rows: bool = False):
     """One sequence: O [r][Hq][d], LSE, m, l [Hq][r] for the requested rows (default all n).
 
     m is the row maximum of the scaled logits and l the sum of exp(s - m);
     both are what the page says FlashAttention computes but does not return.
     Pass 1 takes the maximum, pass 2 the exponentials, their sum, the
-    probabilities and O = A V.
+    probabilities and O = A V.  With q_holds_rows, q[i] is the query of rows[i]
+    (so long prompts need not be held whole).
     """
-    n, hq, hkv, d = _check(q, k, v)
+    if q_holds_rows:
+        if rows is None or len(rows) != q.shape[0]:
+            raise ValueError("q_holds_rows needs one query per requested row")
+        n = k.shape[0]
+        hq, d = q.shape[1], q.shape[2]
+        hkv = k.shape[1]
+        if hq % hkv or k.shape != v.shape or k.shape[2] != d:
+            raise ValueError("shape mismatch")
+        q_rows = q
+    else:
+        n, hq, hkv, d = _check(q, k, v)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     rows = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
@@ -56,9 +67,10 @@ def causal_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: Optiona
         rr = rows[c0:c0 + row_chunk]
         kmax = int(rr.max()) + 1                     # causal: no row needs keys beyond its own index
         visible = np.arange(kmax)[None, :] <= rr[:, None]
+        qsel = q_rows[c0:c0 + len(rr)] if q_holds_rows else q[rr]
         for h in range(hq):
             g = h // G
-            s = scale * (q[rr, h, :] @ k[:kmax, g, :].T)
+            s = scale * (qsel[:, h, :] @ k[:kmax, g, :].T)
             s = np.where(visible, s, -np.inf)
             m = s.max(axis=1)                        # pass 1: row maximum
             e = np.exp(s - m[:, None])               # pass 2: exponentials (masked entries give 0)

@@ -28,14 +28,16 @@ import numpy as np
 
 
 def window_score(q: np.ndarray, k: np.ndarray, lse: np.ndarray, alpha: int,
-                 scale: Optional[float] = None) -> np.ndarray:
+                 scale: Optional[float] = None, window_only: bool = False) -> np.ndarray:
     """One sequence: S [Hkv][n] from the window rows of q, the keys and the saved LSE [Hq][n].
 
     Explicit sum in the pages' order: for every KV head g, every query head h
     of its group and every window row j, add exp(scale * q_hj . k_gi - LSE_hj)
-    to S_g[i] for the keys i <= j.
+    to S_g[i] for the keys i <= j.  With window_only, q is [a][Hq][d] and lse
+    [Hq][a]: only the a = min(alpha, n) window rows (long prompts).
     """
-    n, hq, d = q.shape
+    n = k.shape[0]
+    hq, d = q.shape[1], q.shape[2]
     hkv = k.shape[1]
     if hq % hkv:
         raise ValueError("Hq must be a multiple of Hkv")
@@ -43,12 +45,15 @@ def window_score(q: np.ndarray, k: np.ndarray, lse: np.ndarray, alpha: int,
         scale = 1.0 / math.sqrt(d)
     G = hq // hkv
     a = min(alpha, n)
+    first = n - a if window_only else 0            # prompt row held at index 0 of q / lse
+    if window_only and (q.shape[0] != a or lse.shape[1] != a):
+        raise ValueError("window_only needs the last min(alpha, n) rows")
     S = np.zeros((hkv, n))
     for g in range(hkv):
         for h in range(g * G, (g + 1) * G):
             for j in range(n - a, n):
-                s = scale * (k[:j + 1, g, :] @ q[j, h, :])
-                S[g, :j + 1] += np.exp(s - lse[h, j])
+                s = scale * (k[:j + 1, g, :] @ q[j - first, h, :])
+                S[g, :j + 1] += np.exp(s - lse[h, j - first])
     return S
 
 

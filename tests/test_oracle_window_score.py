@@ -98,3 +98,21 @@ def test_visited_pairs_counts_the_pages_example():
     assert v <= 5000 * 256 and v > 0.95 * 5000 * 256
     assert visited_pairs(10, 3) == 8 + 9 + 10
     assert visited_pairs(4, 10) == 1 + 2 + 3 + 4
+
+
+def test_row_subset_interfaces_equal_full_calls():
+    """q_holds_rows / window_only only change what the caller passes, not the result."""
+    from oracle import causal_attention
+    n, hq, hkv, d = 200, 4, 2, 16
+    q, k = _rand(n, hq, hkv, d, 21)
+    v = np.random.default_rng(22).standard_normal((n, hkv, d))
+    rows = [0, 7, 150, 199]
+    O1, l1, m1, e1 = causal_attention(q, k, v, rows=rows)
+    O2, l2, m2, e2 = causal_attention(q[rows], k, v, rows=rows, q_holds_rows=True)
+    assert np.array_equal(O1, O2) and np.array_equal(l1, l2) and np.array_equal(m1, m2) and np.array_equal(e1, e2)
+    lse = causal_attention(q, k, v)[1]
+    for alpha in (1, 8, 500):
+        a = min(alpha, n)
+        S1 = window_score(q, k, lse, alpha)
+        S2 = window_score(q[n - a:], k, lse[:, n - a:], alpha, window_only=True)
+        assert np.array_equal(S1, S2)

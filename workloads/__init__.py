@@ -172,20 +172,68 @@ def decode_step_inputs(w: Workload, layer: int, step: int, batch: int, seq_ids: 
     return f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
 
 
-def device_normal_bf16(shape, seed: int, device="cuda"):
-    """Large inputs drawn on the device: torch's seeded Philox stream, rounded to bf16.
-
-    Used where host generation of hundreds of millions of values would dominate
-    a test (the 30k-token and mixed-batch workloads); the sampled slices the
-    oracle needs are copied back, so both sides see the same bf16 values.
-    """
-    import torch
-    gen = torch.Generator(device=device)
-    gen.manual_seed(int(seed))
-    return torch.randn(shape, generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
-
-
 def spawn_seed(w: Workload, *key) -> int:
     """A 63-bit seed for a device stream, derived from (workload seed, key)."""
     ss = np.random.SeedSequence(w.seed, spawn_key=tuple(int(x) for x in key))
     return int(ss.generate_state(1, dtype=np.uint64)[0]) & ((1 << 63) - 1)
+
+
+def _device_normal_f32(shape, seed: int, device):
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    return torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+
+
+# Device-drawn inputs: torch's seeded Philox streams on the GPU, one per (layer, seq, tensor,
+# step).  Used where host generation of hundreds of millions of values would dominate a test
+# (the 32-layer, 30k-token and mixed workloads); the oracle gets the sampled slices copied back,
+# so both sides see the same bf16 values.  Same distribution and sink rule as the host path.
+PREFIX_SEQ_BASE = 1 << 20    # seq id space of the shared prefixes of the mixed workload
+
+
+def device_prompt(w: Workload, layer: int, seq: int, n: int, device="cuda", prefix_group=None, prefix_len=0):
+    """bf16 Q [n][Hq][d], K, V [n][Hkv][d] on the device for one prompt.
+
+    With prefix_group set, rows 0..prefix_len-1 come from the group's own streams (identical for
+    every member of the group) and the rest from the prompt's streams.
+    """
+    import torch
+    parts = []
+    for tensor, heads in ((T_Q, w.hq), (T_K, w.hkv), (T_V, w.hkv)):
+        if prefix_group is None or prefix_len <= 0:
+            x = _device_normal_f32((n, heads, w.d), spawn_seed(w, layer, seq, tensor), device)
+        else:
+            pre = _device_normal_f32((prefix_len, heads, w.d),
+                                     spawn_seed(w, layer, PREFIX_SEQ_BASE + prefix_group, tensor), device)
+            suf = _device_normal_f32((n - prefix_len, heads, w.d), spawn_seed(w, layer, seq, tensor), device)
+            x = torch.cat([pre, suf])
+        if tensor == T_K:
+            for p in w.sink_positions:
+                if p < n:
+                    for c in w.sink_channels:
+                        x[p, :, c] *= 20.0
+        parts.append(x.to(torch.bfloat16))
+    return tuple(parts)
+
+
+def device_batch(w: Workload, layer: int, lengths: Sequence[int], seq_ids: Sequence[int], device="cuda", **kw):
+    """Ragged device batch (Q, K, V, cu_seqlens as int32 numpy) of the given prompts."""
+    import torch
+    qs, ks, vs = [], [], []
+    for sid, n in zip(seq_ids, lengths):
+        q, k, v = device_prompt(w, layer, sid, n, device=device, **kw)
+        qs.append(q); ks.append(k); vs.append(v)
+    cu = np.zeros(len(lengths) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lengths)
+    return torch.cat(qs), torch.cat(ks), torch.cat(vs), cu
+
+
+def device_decode_step(w: Workload, layer: int, step: int, seq_ids: Sequence[int], device="cuda"):
+    """Fresh N(0,1) decode query [B][Hq][d] and appended K/V [B][Hkv][d], bf16 on the device."""
+    import torch
+    out = []
+    for tensor, heads in ((T_DQ, w.hq), (T_DK, w.hkv), (T_DV, w.hkv)):
+        out.append(torch.stack([_device_normal_f32((heads, w.d), spawn_seed(w, layer, s, tensor, step), device)
+                                for s in seq_ids]).to(torch.bfloat16))
+    return tuple(out)

@@ -237,3 +237,58 @@ def device_decode_step(w: Workload, layer: int, step: int, seq_ids: Sequence[int
         out.append(torch.stack([_device_normal_f32((heads, w.d), spawn_seed(w, layer, s, tensor, step), device)
                                 for s in seq_ids]).to(torch.bfloat16))
     return tuple(out)
+
+
+# ---------------------------------------------------------------- continuous-batch trace
+@dataclasses.dataclass(frozen=True)
+class MixSequence:
+    seq_id: int        # admission index (0..63 are the initial batch)
+    slot: int
+    group: int         # prefix group = slot // group_size
+    n: int             # prompt length
+    lifetime: int      # decode tokens before it finishes
+
+
+def mix_sequence(w: Workload, seq_id: int, slot: int) -> MixSequence:
+    """Prompt length log-uniform in the workload's range and lifetime uniform in its range, per admission."""
+    r = w.rng(0, seq_id, T_LIFE)
+    lo, hi = w.len_range
+    u = float(r.random())
+    n = int(round(math.exp(math.log(lo) + u * (math.log(hi) - math.log(lo)))))
+    llo, lhi = w.lifetime_range
+    life = int(r.integers(llo, lhi + 1))
+    return MixSequence(seq_id, slot, slot // w.group_size, n, life)
+
+
+def mix_trace(w: Workload, iterations: int):
+    """Per iteration: (admitted sequences, finished seq ids).
+
+    Iteration semantics: admitted prompts are prefilled and compressed first, then every live
+    sequence decodes one token, then sequences that reached their lifetime finish and free
+    their slot, which the next iteration refills (slots in ascending order, admission ids
+    counting up).  Depends only on the seeded lengths and lifetimes.
+    """
+    live = {}
+    decoded = {}
+    next_id = 0
+    empty = list(range(w.num_seqs))
+    out = []
+    for _ in range(iterations):
+        admitted = []
+        for slot in sorted(empty):
+            sq = mix_sequence(w, next_id, slot)
+            next_id += 1
+            live[sq.seq_id] = sq
+            decoded[sq.seq_id] = 0
+            admitted.append(sq)
+        empty = []
+        finished = []
+        for sid in sorted(live):
+            decoded[sid] += 1
+            if decoded[sid] >= live[sid].lifetime:
+                finished.append(sid)
+        for sid in finished:
+            empty.append(live[sid].slot)
+            del live[sid]
+        out.append((admitted, finished))
+    return out

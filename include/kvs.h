@@ -73,7 +73,9 @@ const char* kvs_version(void);
  *      max_seqlen >= every n_s; total_tokens = cu_seqlens[num_seqs]; scale > 0 (1/sqrt(d)).
  * Out: o [total][hq][d] bf16 (round to nearest even); lse [hq][total_tokens] fp32 natural
  *      log; rowmax_opt, ell_opt [hq][total_tokens] fp32 (m_j and l_j; NULL to skip).
- * Errors: KVS_E_INVAL on a bad shape, KVS_E_HIP if the launch fails.
+ * Errors: KVS_E_INVAL on a bad shape or when max_seqlen * hkv * d * 2 exceeds 2^31 - 1 (one
+ *         prompt's K or V rows are addressed with 32-bit byte offsets), KVS_E_HIP if the
+ *         launch fails.
  */
 int kvs_prefill_attn_lse(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
                          int num_seqs, int total_tokens, int max_seqlen, int hq, int hkv, int d,

@@ -3,7 +3,7 @@
     kvs_prefill_attn_lse -> kvs_window_score -> kvs_topk_select -> kvs_compact_paged -> kvs_paged_decode
 
 Every step runs in hand-written HIP kernels for gfx950 (libkvs.so, built in-tree with
-``python -m kv_cache_sparsification_amd.build``).  This package only marshals torch tensors
+``python kv_cache_sparsification_amd/build.py``).  This package only marshals torch tensors
 into the C ABI declared in include/kvs.h; importing it fails if the library is not built.
 """
 from ._lib import lib, KvsError, BLOCK_SIZE, LIB_PATH

@@ -62,7 +62,7 @@ def _load():
     # dependency to that already-loaded copy (matched by its soname).
     import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built: run `python -m kv_cache_sparsification_amd.build` "
+        raise ImportError(f"{LIB_PATH} is not built: run `python kv_cache_sparsification_amd/build.py` "
                           "(the HIP library is required; there is no fallback path)")
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():

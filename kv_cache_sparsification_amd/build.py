@@ -1,6 +1,6 @@
 """Build libkvs.so in-tree with hipcc for gfx950.
 
-    python -m kv_cache_sparsification_amd.build [-v]
+    python kv_cache_sparsification_amd/build.py [-v]
 
 Every HIP and C++ source under csrc/ is compiled to an object file under _build/ and linked
 into kv_cache_sparsification_amd/libkvs.so.  All HIP code is built with the packed-fp32
@@ -63,7 +63,8 @@ def build(verbose: bool = False) -> str:
     with concurrent.futures.ThreadPoolExecutor(workers) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = LIB + ".tmp"
-    _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
+    # -z defs: an unresolved symbol (say a kernel stub the host pass dropped) fails the link
+    _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-Wl,-z,defs", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -44,6 +44,30 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // ---------------------------------------------------------------- wave helpers
 __device__ __forceinline__ float wave_xor(float v, int mask) { return __shfl_xor(v, mask, kWave); }
 
+// Lane l and lane l ^ 32 combined without LDS: v_permlane32_swap hands each lane the pair
+// {own value, partner's value} (in either order), which suits commutative operations.
+__device__ __forceinline__ float half_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return a > b ? a : b;
+}
+__device__ __forceinline__ float half_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Word 3 of a gfx9-family buffer descriptor: 32-bit data format (untyped loads are then valid)
+// and raw addressing, so each load is range-checked against the descriptor's byte count and
+// reads zero past it.
+constexpr int kBufferFlags = 0x00020000;
+
+// 16 bytes per lane from a buffer straight into LDS: lane i's bytes land at lds + 16 * i (the
+// LDS address must be the same for the whole wavefront).  Callers must not depend on what
+// out-of-range lanes leave in LDS.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void* lds, int voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voffset, 0, 0, 0);
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

@@ -68,6 +68,15 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voffset, 0, 0, 0);
 }
 
+// gfx950 transposing LDS read: within each group of 16 lanes, lane j supplies the address of 4
+// consecutive 16-bit values (row j/4, values 4*(j%4) .. +3 of a 4 x 16 block) and receives
+// column j of the block, i.e. the 4 values the group's addresses hold at position j.
+__device__ __forceinline__ u32x2 ds_read_tr16_b64(const uint16_t* p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p);
+  return __builtin_bit_cast(u32x2, r);
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

@@ -8,20 +8,27 @@
 // Here the pair is written as LSE = rowmax + ln(l) (plus rowmax and l on request).
 //
 // MI355X form (bf16 MFMA 32x32x16, fp32 accumulation, online softmax in registers):
-//   * A workgroup = 4 wavefronts = 128 query rows of one query head; each wavefront owns 32
-//     rows.  The product is computed transposed, S^T = K . Q^T: keys are the M dimension,
-//     query rows the N dimension, so every lane holds 16 scores of a single query row per
-//     32-key tile.  The row maximum is an in-lane max plus one cross-lane exchange, the row
+//   * A workgroup = 8 wavefronts = 256 query rows of one query head; each wavefront owns a
+//     strip of 32 rows.  The product is computed transposed, S^T = K . Q^T: keys are the M
+//     dimension, query rows the N dimension, so every lane holds 16 scores of a single query
+//     row per 32-key tile.  The row maximum is an in-lane max plus one lane-half swap, the row
 //     scale of O is a per-lane scalar, and the exponentiated scores are already in the B
 //     operand layout of O^T = V^T . P^T: P never goes through LDS.
-//   * K tiles (64 keys) are staged row-major in LDS; V tiles are stored transposed (V^T,
-//     channel rows of 64 keys).  The key order of the first product is permuted so that each
-//     lane's share of P^T is 8 consecutive keys: the A operand of the second product is then a
-//     single 16-byte LDS read.  The next tile's global loads are issued before the current tile
-//     is computed.
+//   * K tiles (64 keys) go from memory straight into LDS in their natural row-major layout
+//     (buffer loads with an LDS destination, range-checked against the prompt), rows padded by
+//     one chunk so the operand reads are free of bank conflicts.  V tiles go through registers
+//     and are stored transposed (V^T, channel rows of 64 keys): 16-byte operand reads of V^T
+//     run at twice the LDS rate of the transposing 8-byte read.  The key order of the first
+//     product is permuted so that each lane's share of P^T is 8 consecutive keys, so the V^T
+//     operand is one 16-byte read.
+//   * Ping-pong: per tile a wavefront has a matrix phase (O^T product of the previous tile,
+//     S^T product of this one) and a vector phase (mask, row maximum, exponentials).  The two
+//     groups of four wavefronts (one of each on every SIMD) run one phase apart, separated by
+//     workgroup barriers, so each SIMD's matrix core works for one group while its vector unit
+//     works for the other.  Loads are issued two phases before their tile is first read.
 //   * Q stays in registers for the whole key loop.  Wavefronts whose rows all precede a key
-//     tile skip it (causal); only the diagonal tile is masked, and O is rescaled only when a
-//     row maximum grows by more than 2^8 (wave-uniform branches).
+//     tile skip its work; only the diagonal tiles are masked, and O is rescaled only when a
+//     row maximum grows by more than 2^8 (wave-uniform branch).
 //   * Workgroups are remapped so that each XCD (8 per chip, each with its own L2) works on
 //     one KV head at a time, heaviest (last) query tiles first.
 #include "kvs_common.h"
@@ -29,20 +36,19 @@
 namespace kvs {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kBQ = 128;   // query rows per workgroup
+constexpr int kWaves = 8;
+constexpr int kGroupWaves = 4;   // wavefronts per ping-pong group
+constexpr int kBQ = 256;   // query rows per workgroup
 constexpr int kBK = 64;    // keys per tile
 constexpr int kRowsPerWave = 32;
 constexpr int kXcds = 8;
 
-// Chunk swizzle of the K tile in LDS: 16 chunk positions make one 256-byte line of the 64
-// banks, so rows r of one line group (16 / KCU rows per line) rotate their chunks by
-// (r / (16 / KCU)) % KCU; any 16 consecutive rows then put a given chunk on 16 distinct positions.
-template <int D>
-__device__ __forceinline__ int kswz(int r) {
-  constexpr int KCU = D / 8;
-  return (r / (16 / KCU)) % KCU;
-}
+// LDS layouts (one 256-byte line spans the 64 banks):
+//  * K: rows padded by one 16-byte chunk (KSTR bf16).  A lane group of the first product
+//    reads one chunk of 16 consecutive rows, which the pad rotates onto all 64 banks; the
+//    read addresses are one register plus immediates.
+//  * V^T: channel rows of kBK keys padded by one chunk (VSTR bf16, 36 words): the 16-byte
+//    reads of 16 consecutive channel rows land on distinct banks.
 
 // s_waitcnt vmcnt(0) with the other counters left alone (gfx9 encoding: vmcnt 0, expcnt 7,
 // lgkmcnt 15).
@@ -50,26 +56,32 @@ constexpr int kVmcntZero = 0x0F70;
 
 // MFMA row m of the S^T product holds key kappa(m) of its 32-key tile: bits 2 and 3 of m are
 // swapped.  With that order the 16 scores a lane half gets back cover 8 consecutive keys per
-// 16-key step, so P^T needs no shuffling and the matching V^T operand is one 16-byte read.
+// 16-key step, so P^T needs no shuffling.
 __device__ __forceinline__ int kappa(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
 template <int D>
-__global__ __launch_bounds__(kWaves * kWave, 2) void prefill_kernel(
+__global__ __launch_bounds__(kWaves * kWave, 1) void prefill_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ cu_seqlens, int num_seqs, int total_tokens, int hq, int hkv, float c_log2,
     uint16_t* __restrict__ o, float* __restrict__ lse, float* __restrict__ rowmax, float* __restrict__ ell, int nqt,
     int total_items) {
-  constexpr int KCU = D / 8;      // 16-byte chunks per K row
-  constexpr int VSTR = kBK + 8;  // bf16 per V^T row in LDS: 36 words, 16 consecutive rows on distinct banks
+  constexpr int KCU = D / 8;     // 16-byte chunks per tile row
   constexpr int ST1 = D / 16;    // k-steps of S^T = K Q^T
   constexpr int MT2 = D / 32;    // channel tiles of O^T
   constexpr int KS2 = kBK / 16;  // k-steps of O^T = V^T P^T
   constexpr int NT = kWaves * kWave;
-  // Double-buffered tiles as four distinct LDS objects: with the buffer of each access known at
-  // compile time, the compiler can tell the loads into one buffer from the reads of the other
+  constexpr int KSTR = D + 8;           // bf16 per K row in LDS (one pad chunk)
+  constexpr int KPOS = kBK * (KCU + 1);  // 16-byte positions of a K tile, pads included
+  constexpr int KLD = (KPOS + NT - 1) / NT;   // K loads per lane per tile (the last one partial)
+  constexpr int VSTR = kBK + 8;          // bf16 per V^T row in LDS
+  constexpr int VITEMS = (kBK / 2) * KCU;   // (key pair, 16-byte channel chunk) items of a V tile
+  // Triple-buffered tiles as distinct LDS objects: with the buffer of each access known at
+  // compile time, the compiler can tell the loads into one buffer from the reads of another
   // and does not make those reads wait for the loads.
-  __shared__ __attribute__((aligned(16))) uint16_t ks0[kBK * D], ks1[kBK * D];
-  __shared__ __attribute__((aligned(16))) uint16_t vt0[D * VSTR], vt1[D * VSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t ks0[kBK * KSTR], ks1[kBK * KSTR], ks2[kBK * KSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t vs0[D * VSTR], vs1[D * VSTR], vs2[D * VSTR];
+  auto kbuf = [&](int b) { return b == 0 ? ks0 : b == 1 ? ks1 : ks2; };   // b: a constant at every call
+  auto vbuf = [&](int b) { return b == 0 ? vs0 : b == 1 ? vs1 : vs2; };
 
   // ---- XCD-aware work mapping: item order (g, s, query tile descending, head in group).
   const int per_xcd = gridDim.x / kXcds;
@@ -90,8 +102,11 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_kernel(
   const int tid = threadIdx.x, lane = tid % kWave;
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform: branches on it stay scalar
   const int col = lane % 32, half = lane / 32;
-  const int R = r0 + w * kRowsPerWave;   // first row of this wavefront
+  const int grp = w / kGroupWaves;       // ping-pong group; wavefronts w and w +- 4 share a SIMD
+  const int R = r0 + (2 * (w % kGroupWaves) + grp) * kRowsPerWave;   // first row of this wavefront's strip
   const int row = R + col;               // this lane's query row (N index)
+  const int kend = min(r0 + kBQ, n);
+  const int ntiles = (kend + kBK - 1) / kBK;
 
   // B operand of S^T: Q^T[d][row] for each 16-wide d step.
   bf16x8 qf[ST1];
@@ -112,140 +127,174 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_kernel(
 #pragma unroll
   for (int mt = 0; mt < MT2; ++mt) acc_o[mt] = f32x16{};
 
-  const int kend = min(r0 + kBQ, n);
-  const int ntiles = (kend + kBK - 1) / kBK;
-
-  // ---- Global -> register staging of one K/V tile, prefetched one tile ahead.
-  // K item e: row r = e / (D/8), 16-byte chunk cc = e % (D/8): 16 lanes read one 256-byte row.
-  // V item e: key pair p and chunk cc, 16 lanes per row as well; stored transposed.
-  // The loads go through buffer resources that cover this sequence's rows of KV head g only,
-  // so the ragged last tile needs no branch and the per-tile address is a scalar move of the
-  // resource base.  V rows past the prompt read as zero (P is zero there, and 0 * garbage
-  // could be NaN); K rows past the prompt only meet masked scores, so whatever the LDS holds
-  // for them is replaced by -inf before use.
-  constexpr int KCH = kBK * (D / 8) / NT;
-  constexpr int VIT = (kBK / 2) * (D / 8) / NT;
+  // ---- Tile loads.  K: load `it` of wave w fills LDS chunk positions p = (it*kWaves + w)*64 +
+  // lane of a tile (1 KB per wave per load); position p is chunk p % (KCU+1) of row
+  // p / (KCU+1), the pad position taking a copy of the row's last chunk (same cache line).
+  // K rows past the prompt only meet masked scores (replaced by -inf), so whatever LDS holds
+  // for them does not matter.  V: thread e < VITEMS loads chunk cc of keys 2p and 2p+1 into
+  // registers (rows past the prompt read as zero: P is zero there and 0 * garbage could be
+  // NaN) and later stores the 8 channel pairs transposed.  Buffer resources cover this
+  // sequence's rows of KV head g only, so the ragged last tile needs no branch and a tile's
+  // address is a scalar move of the resource base.
   constexpr int kRowBytes = 2 * D;
   const int row_pitch = hkv * kRowBytes;                           // bytes between consecutive keys
   const int seq_bytes = (n - 1) * row_pitch + kRowBytes;           // this head's rows of the prompt
   const int tile_bytes = kBK * row_pitch;
   const char* kbase = reinterpret_cast<const char*>(k + ((size_t)base * hkv + g) * D);
   const char* vbase = reinterpret_cast<const char*>(v + ((size_t)base * hkv + g) * D);
-  // K goes from memory straight into LDS: load `it` of wave w fills the 1 KB of LDS units
-  // u = (it * kWaves + w) * 64 + lane (16 bytes each), unit u being chunk position
-  // u % KCU of row u / KCU.  Chunk c of row r sits at position c ^ kswz(r): the 16 rows a
-  // lane group reads in one product step then cover all 64 banks, with no row padding.
-  int koff[KCH], voff[VIT];
+  int koff[KLD];
 #pragma unroll
-  for (int it = 0; it < KCH; ++it) {
-    const int u = (it * kWaves + w) * kWave + lane;
-    const int r = u / KCU;
-    koff[it] = r * row_pitch + ((u % KCU) ^ kswz<D>(r)) * 16;
+  for (int it = 0; it < KLD; ++it) {
+    const int p = (it * kWaves + w) * kWave + lane;
+    const int r = p / (KCU + 1), c = p % (KCU + 1);
+    koff[it] = r * row_pitch + min(c, KCU - 1) * 16;
   }
+  // V item of this thread: wavefront e / 64 and lane e % 64 pick key pair p and chunk cc so
+  // that 16 lanes read one 256-byte row.
+  const bool v_item = tid < VITEMS;   // every thread when D = 128, half of them when D = 64
+  const int vp = ((tid / kWave) % 2) * 16 + lane % 16;
+  const int vcc = (tid / kWave / 2) * 4 + lane / 16;
+  const int voff = 2 * vp * row_pitch + vcc * 16;
+  u32x4 va = {0u, 0u, 0u, 0u}, vb = {0u, 0u, 0u, 0u};
+  auto rsrc = [&](const char* src, int kt) {
+    const int skip = kt * tile_bytes;    // < seq_bytes for every tile that is loaded
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(src) + skip, 0, seq_bytes - skip, kBufferFlags);
+  };
+  // buf: a constant at every call
+  auto load_k = [&](int kt, int buf) {
+    uint16_t* dst = kbuf(buf);
+    const __amdgpu_buffer_rsrc_t rs = rsrc(kbase, kt);
 #pragma unroll
-  for (int it = 0; it < VIT; ++it) {
-    const int e = it * NT + tid;
-    const int wv = e / kWave, ln = e % kWave;
-    const int p = (wv % 2) * 16 + ln % 16;
-    const int cc = (wv / 2) * 4 + ln / 16;
-    voff[it] = 2 * p * row_pitch + cc * 16;
-  }
-  u32x4 va[VIT], vb[VIT];
-  auto load_tile = [&](int kt, int buf) {   // buf: a constant at every call
-    uint16_t* ks = buf ? ks1 : ks0;
-    const int skip = kt * tile_bytes;   // < seq_bytes for every tile that is loaded
-    const __amdgpu_buffer_rsrc_t kr =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase) + skip, 0, seq_bytes - skip, kBufferFlags);
-    const __amdgpu_buffer_rsrc_t vr =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase) + skip, 0, seq_bytes - skip, kBufferFlags);
-#pragma unroll
-    for (int it = 0; it < KCH; ++it)
-      buffer_load_lds16(kr, &ks[(it * kWaves + w) * kWave * 8], koff[it]);
-#pragma unroll
-    for (int it = 0; it < VIT; ++it) {
-      va[it] = __builtin_amdgcn_raw_buffer_load_b128(vr, voff[it], 0, 0);
-      vb[it] = __builtin_amdgcn_raw_buffer_load_b128(vr, voff[it] + row_pitch, 0, 0);
+    for (int it = 0; it < KLD; ++it)
+      if ((it * kWaves + w) * kWave < KPOS)   // wave-uniform; the last load of a tile is partial
+        buffer_load_lds16(rs, &dst[(it * kWaves + w) * kWave * 8], koff[it]);
+  };
+  auto load_v = [&](int kt) {            // V tile kt into registers
+    const __amdgpu_buffer_rsrc_t rs = rsrc(vbase, kt);
+    if (v_item) {
+      va = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0);
+      vb = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + row_pitch, 0, 0);
     }
   };
-  // V^T goes through registers (the transpose), K is already in place once its loads land.
-  auto store_tile = [&](int buf) {
-    uint16_t* vt = buf ? vt1 : vt0;
-#pragma unroll
-    for (int it = 0; it < VIT; ++it) {
-      const int e = it * NT + tid;
-      const int wv = e / kWave, ln = e % kWave;
-      const int p = (wv % 2) * 16 + ln % 16;
-      const int cc = (wv / 2) * 4 + ln / 16;
+  auto store_v = [&](int buf) {          // the registers of load_v into V^T buffer buf
+    uint16_t* vt = vbuf(buf);
+    if (v_item) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        // channel cc*8 + j of keys 2p (low half) and 2p + 1 (high half)
-        const uint32_t word = (j % 2 == 0)
-            ? __builtin_amdgcn_perm(vb[it][j / 2], va[it][j / 2], 0x05040100u)
-            : __builtin_amdgcn_perm(vb[it][j / 2], va[it][j / 2], 0x07060302u);
-        *reinterpret_cast<uint32_t*>(&vt[(cc * 8 + j) * VSTR + 2 * p]) = word;
+        // channel vcc*8 + j of keys 2vp (low half) and 2vp + 1 (high half)
+        const uint32_t word = (j % 2 == 0) ? __builtin_amdgcn_perm(vb[j / 2], va[j / 2], 0x05040100u)
+                                           : __builtin_amdgcn_perm(vb[j / 2], va[j / 2], 0x07060302u);
+        *reinterpret_cast<uint32_t*>(&vt[(vcc * 8 + j) * VSTR + 2 * vp]) = word;
       }
     }
   };
 
-  // GEMM-1 A operand: lane col reads K row kappa(col) of each 32-key M tile, chunk 2*st + half
-  // at its swizzled position (the swizzle of rows 32 apart is the same).
-  const int krow = kappa(col);
-  int kofs[ST1];
+  // ---- Operand reads.
+  // S^T A operand, fragment f = 2*st + mt: lane col reads K row mt*32 + kappa(col), chunk
+  // 2*st + half.
+  const int kofs = kappa(col) * KSTR + half * 8;
+  constexpr int NF1 = 2 * ST1, NG1 = NF1 / 4;
+  auto kfrag = [&](const uint16_t* ks, int f) {
+    return *reinterpret_cast<const u32x4*>(&ks[(f % 2) * 32 * KSTR + (f / 2) * 16 + kofs]);
+  };
+  // O^T A operand, fragment f = ks2*MT2 + mt: lane l reads V^T row 32*mt + l%32 (a channel),
+  // keys 16*ks2 + 8*half + 0..7.
+  const int vofs = col * VSTR + half * 8;
+  constexpr int NF2 = MT2 * KS2, NG2 = NF2 / 4;
+  auto vfrag = [&](const uint16_t* vt, int f) {
+    return *reinterpret_cast<const u32x4*>(&vt[(f % MT2) * 32 * VSTR + (f / MT2) * 16 + vofs]);
+  };
+  auto mfma1 = [&](f32x16 (&sacc)[2], int f, u32x4 a) {
+    sacc[f % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[f / 2], sacc[f % 2], 0, 0, 0);
+  };
+  auto mfma2 = [&](const bf16x8 (&pf)[KS2], int f, u32x4 a) {
+    acc_o[f % MT2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pf[f / MT2], acc_o[f % MT2],
+                                                              0, 0, 0);
+  };
+  // sacc[mt][i] is key kb + 32*mt + 16*(i/8) + 8*half + i%8 against `row` (raw dot products).
+  // P^T as B operands: k-step ks2 holds keys 16*ks2 + 8*half + 0..7, i.e. sacc[ks2/2][8*(ks2%2) + 0..7].
+  auto softmax_step = [&](f32x16 (&sacc)[2], bf16x8 (&pf)[KS2], int ks2, float& psum) {
+    const int mt = ks2 / 2, i0 = 8 * (ks2 % 2);
+    u32x4 x;
 #pragma unroll
-  for (int st = 0; st < ST1; ++st) kofs[st] = krow * D + (((2 * st + half) ^ kswz<D>(krow)) * 8);
-
-  // One barrier per tile: tile kt+1's global loads are issued before tile kt is computed and
-  // stored into the other LDS buffer right after it, while the barrier that ends iteration kt
-  // makes those stores visible and guarantees nobody still reads that buffer's previous tile.
-  load_tile(0, 0);
-  store_tile(0);
-  __builtin_amdgcn_s_waitcnt(kVmcntZero);   // this wave's K transfers into LDS have landed
-  __syncthreads();
-  auto tile_step = [&](const int cur, int kt) {   // cur: a constant at every call
-    const int kb = kt * kBK;
-    const uint16_t* ks = cur ? ks1 : ks0;
-    const uint16_t* vt = cur ? vt1 : vt0;
-    if (kt + 1 < ntiles) load_tile(kt + 1, cur ^ 1);   // in flight while this tile is computed
-    if (kb <= R + kRowsPerWave - 1) {           // else every row of this wavefront precedes the tile
-    // ---- S^T tile: 64 keys x 32 rows as two 32x32 products over d.  The 2*ST1 A fragments
-    // are read from LDS in groups of four, the next group's reads in flight while the current
-    // group's products run (the two 32-key halves alternate, so neighbours are independent).
-    constexpr int NF1 = 2 * ST1, NG1 = NF1 / 4;
-    auto kfrag = [&](int f) {
-      const int mt = f % 2, st = f / 2;
-      return *reinterpret_cast<const u32x4*>(&ks[mt * 32 * D + kofs[st]]);
-    };
+    for (int j = 0; j < 4; ++j) {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][i0 + 2 * j], c_log2, -m_ref));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][i0 + 2 * j + 1], c_log2, -m_ref));
+      psum += p0 + p1;
+      x[j] = pack_bf16x2(p0, p1);
+    }
+    pf[ks2] = __builtin_bit_cast(bf16x8, x);
+  };
+  // Running maximum (log2 units) after a tile, then the lazy rescale of O and l when some row
+  // moved past m_ref + kLazy (wave-uniform branch, rare after the first tiles).
+  auto update_max = [&](float bm) {
+    bm = half_max(bm) * c_log2;
+    m_true = fmaxf(m_true, bm);
+    if (__ballot(m_true > m_ref + kLazy) != 0ull) {
+      const float corr = __builtin_amdgcn_exp2f(m_ref - m_true);
+      m_ref = m_true;
+      l_lane *= corr;
+#pragma unroll
+      for (int mt = 0; mt < MT2; ++mt) acc_o[mt] *= corr;
+    }
+  };
+  auto tile_max = [&](const f32x16 (&sacc)[2]) {   // four independent chains, then combined
+    float bm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) bm[2 * mt + i / 8] = fmaxf(bm[2 * mt + i / 8], sacc[mt][i]);
+    return fmaxf(fmaxf(bm[0], bm[1]), fmaxf(bm[2], bm[3]));
+  };
+  // Products of one tile on their own (first tile, last pipelined tile, diagonal tiles):
+  // operand fragments are read from LDS in groups of four, the next group's reads in flight
+  // while the current group's products run.
+  auto gemm1 = [&](const uint16_t* ks, f32x16 (&sacc)[2]) {
     u32x4 fr[2][4];
-    f32x16 sacc[2];
     sacc[0] = f32x16{};
     sacc[1] = f32x16{};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) fr[0][j] = kfrag(j);
+    for (int j = 0; j < 4; ++j) fr[0][j] = kfrag(ks, j);
 #pragma unroll
     for (int grp = 0; grp < NG1; ++grp) {
       if (grp + 1 < NG1) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) fr[(grp + 1) & 1][j] = kfrag(4 * (grp + 1) + j);
+        for (int j = 0; j < 4; ++j) fr[(grp + 1) & 1][j] = kfrag(ks, 4 * (grp + 1) + j);
       }
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int f = 4 * grp + j;
-        sacc[f % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fr[grp & 1][j]),
-                                                               qf[f / 2], sacc[f % 2], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      for (int j = 0; j < 4; ++j) mfma1(sacc, 4 * grp + j, fr[grp & 1][j]);
     }
-    // The first group of V^T fragments is read now, to be in registers when P is.
-    constexpr int NF2 = MT2 * KS2, NG2 = NF2 / 4;
-    auto vfrag = [&](int f) {
-      const int mt = f % MT2, ks2 = f / MT2;
-      return *reinterpret_cast<const u32x4*>(&vt[(mt * 32 + col) * VSTR + ks2 * 16 + half * 8]);
-    };
+  };
+  // The O^T product takes all its V^T fragments from registers: they are read during the
+  // preceding vector phase, when this wavefront's LDS reads are otherwise idle, so the matrix
+  // phase starts without waiting on LDS.
+  u32x4 vpre[NF2];
+  auto prefetch_v = [&](const uint16_t* vs) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) fr[0][j] = vfrag(j);
-    // sacc[mt][i] is key kb + 32*mt + 16*(i/8) + 8*half + i%8 against `row` (raw dot products).
-    if (kb + kBK - 1 > R) {   // diagonal tile (wave-uniform): mask keys past the row
+    for (int f = 0; f < NF2; ++f) vpre[f] = vfrag(vs, f);
+  };
+  auto gemm2 = [&](const bf16x8 (&pf)[KS2]) {
+#pragma unroll
+    for (int f = 0; f < NF2; ++f) mfma2(pf, f, vpre[f]);
+  };
+
+  // ---- Ping-pong schedule.  K tile t lives in ks{t%3}, V tile t in vs{t%3}.  Per tile t a
+  // wavefront's work is a matrix phase M(t-1) (O^T += V_{t-1}^T P_{t-1}^T, then S_t = K_t Q^T)
+  // and a vector phase X(t) (mask, maximum, rescale, P_t), each closed by a barrier.  Both
+  // groups run the same sequence, group 1 one barrier behind (it passes one extra barrier at
+  // the start, group 0 one at the end), so in every phase one group is in its matrix phase and
+  // the other in its vector phase.  Iteration t issues K_{t+2} (into LDS) and V_{t+1} (into
+  // registers, stored transposed at its end); their buffers were last read by M(t-2), at least
+  // one barrier earlier for either group, and they are first read by M(t+1), after the
+  // barrier that follows every wavefront's wait for its own loads and V^T stores.
+  // Every wavefront does every tile of the workgroup: a tile past all of its rows is fully
+  // masked (P = 0) by the same code that masks the diagonal, which keeps the loop free of
+  // branches around the products.
+  f32x16 sacc[2];
+  bf16x8 pf[KS2];
+  auto vector_phase = [&](int t) {                 // X(t)
+    const int kb = t * kBK;
+    if (kb + kBK - 1 > R) {   // wave-uniform: mask keys past the row
       const int lim = row - kb - 8 * half;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
@@ -253,63 +302,58 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_kernel(
         for (int i = 0; i < 16; ++i)
           if (mt * 32 + 16 * (i / 8) + (i % 8) > lim) sacc[mt][i] = -INFINITY;
     }
-    float bm = -INFINITY;
+    update_max(tile_max(sacc));
+    float psum[KS2];   // one chain per key step, added up at the end
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) bm = fmaxf(bm, sacc[mt][i]);
-    bm = half_max(bm) * c_log2;
-    m_true = fmaxf(m_true, bm);
-    if (__ballot(m_true > m_ref + kLazy) != 0ull) {   // some row moved too far: rescale (rare)
-      const float corr = __builtin_amdgcn_exp2f(m_ref - m_true);
-      m_ref = m_true;
-      l_lane *= corr;
-#pragma unroll
-      for (int mt = 0; mt < MT2; ++mt) acc_o[mt] *= corr;
+    for (int ks = 0; ks < KS2; ++ks) {
+      psum[ks] = 0.f;
+      softmax_step(sacc, pf, ks, psum[ks]);
     }
-    float psum = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][i], c_log2, -m_ref));
-        sacc[mt][i] = p;
-        psum += p;
-      }
-    l_lane += psum;
-
-    // P^T as B operands: k-step ks2 holds keys 16*ks2 + 8*half + 0..7 in order.
-    bf16x8 pf[KS2];
-#pragma unroll
-    for (int ks2 = 0; ks2 < KS2; ++ks2) {
-      const int mt = ks2 / 2, i0 = 8 * (ks2 % 2);
-      u32x4 x;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) x[j] = pack_bf16x2(sacc[mt][i0 + 2 * j], sacc[mt][i0 + 2 * j + 1]);
-      pf[ks2] = __builtin_bit_cast(bf16x8, x);
-    }
-#pragma unroll
-    for (int grp = 0; grp < NG2; ++grp) {
-      if (grp + 1 < NG2) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) fr[(grp + 1) & 1][j] = vfrag(4 * (grp + 1) + j);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int f = 4 * grp + j;
-        acc_o[f % MT2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fr[grp & 1][j]),
-                                                                  pf[f / MT2], acc_o[f % MT2], 0, 0, 0);
-      }
-    }
-    }
-    if (kt + 1 < ntiles) store_tile(cur ^ 1);
-    __builtin_amdgcn_s_waitcnt(kVmcntZero);
+    l_lane += (psum[0] + psum[1]) + (psum[2] + psum[3]);
+  };
+  auto close_phase = [&](bool wait_loads) {
+    if (wait_loads) __builtin_amdgcn_s_waitcnt(kVmcntZero);
     __syncthreads();
   };
-  for (int kt = 0; kt < ntiles; kt += 2) {
-    tile_step(0, kt);
-    if (kt + 1 < ntiles) tile_step(1, kt + 1);
+  auto iteration = [&](const int b, int t) {       // 0 < t < ntiles; b = t % 3, a constant
+    if (t + 2 < ntiles) load_k(t + 2, (b + 2) % 3);
+    if (t + 1 < ntiles) load_v(t + 1);
+    gemm2(pf);                                     // M(t-1), V_{t-1} fragments in registers
+    gemm1(kbuf(b), sacc);
+    close_phase(false);
+    vector_phase(t);
+    prefetch_v(vbuf(b));                           // V_t for M(t)
+    if (t + 1 < ntiles) store_v((b + 1) % 3);
+    close_phase(true);
+  };
+  load_k(0, 0);
+  if (1 < ntiles) load_k(1, 1);
+  load_v(0);
+  store_v(0);
+  __builtin_amdgcn_s_waitcnt(kVmcntZero);
+  __syncthreads();
+  if (grp == 1) __syncthreads();
+  // t = 0: no O^T product yet
+  if (2 < ntiles) load_k(2, 2);
+  if (1 < ntiles) load_v(1);
+  gemm1(ks0, sacc);
+  close_phase(false);
+  vector_phase(0);
+  prefetch_v(vs0);
+  if (1 < ntiles) store_v(1);
+  close_phase(true);
+  for (int t = 1; t < ntiles; t += 3) {
+    iteration(1, t);
+    if (t + 1 < ntiles) iteration(2, t + 1);
+    if (t + 2 < ntiles) iteration(0, t + 2);
   }
+  // t = ntiles: the last O^T product (all loads have landed)
+  {
+    gemm2(pf);
+    close_phase(false);
+    close_phase(false);
+  }
+  if (grp == 0) __syncthreads();
 
   // ---- epilogue: O = acc / l, LSE = ln 2 * (m_ref + log2 l)
   const float l = half_sum(l_lane);   // sum of exp2(x - m_ref)

@@ -35,32 +35,55 @@ __global__ __launch_bounds__(kWavesPerWG * kWave) void compact_kernel(
   const int bi = unit / hkv;
   const int g = unit % hkv;
 
-  const int base = cu_seqlens[s];
-  const int n = cu_seqlens[s + 1] - base;
+  // The prompt's metadata is read in one go; the block-table entry and the 16 source rows
+  // then in a second; the K/V rows in a third; all loads of a round precede any store.
   const bool keep_all = keep_idx == nullptr;
-  const int k_eff = keep_all ? n : keep_offsets[s + 1] - keep_offsets[s];
+  const int base = cu_seqlens[s], end = cu_seqlens[s + 1];
+  const int ko0 = keep_all ? 0 : keep_offsets[s], ko1 = keep_all ? 0 : keep_offsets[s + 1];
   const int off = dst_slot_offset ? dst_slot_offset[s] : 0;
+  const int n = end - base;
+  const int k_eff = keep_all ? n : ko1 - ko0;
   const int tbl_pos = off / kBlock + bi;          // table entry this unit fills
   const int p0 = tbl_pos * kBlock;                 // slot position of its first slot
   if (k_eff <= 0 || p0 >= off + k_eff || tbl_pos >= max_blocks) return;
-  const int blk = block_tables[(size_t)s * max_blocks + tbl_pos];
-  if (blk < 0 || blk >= num_blocks) return;
-
-  const int32_t* keep = keep_all ? nullptr : keep_idx + (size_t)hkv * keep_offsets[s] + (size_t)g * k_eff;
+  const int32_t* keep = keep_all ? nullptr : keep_idx + (size_t)hkv * ko0 + (size_t)g * k_eff;
   const int t0 = p0 - off;                         // rank written to slot 0 (may be negative)
   const bool full = t0 >= 0 && t0 + kBlock <= k_eff;
+  // Source rows of the 16 slots (wave-uniform addresses); -1 marks a slot this block does not fill.
+  int srcrow[kBlock];
+#pragma unroll
+  for (int j = 0; j < kBlock; ++j) {
+    const int t = min(max(t0 + j, 0), k_eff - 1);
+    srcrow[j] = keep_all ? t : keep[t];
+  }
+  const int blk = block_tables[(size_t)s * max_blocks + tbl_pos];
+#pragma unroll
+  for (int j = 0; j < kBlock; ++j)
+    if (t0 + j < 0 || t0 + j >= k_eff) srcrow[j] = -1;
+  if (blk < 0 || blk >= num_blocks) return;
 
   // ---- K: row-major slots, 16-byte lanes
   constexpr int kLanesPerRow = D * 2 / 16;         // 16 (d=128) or 8 (d=64)
   constexpr int kRowsPerIter = kWave / kLanesPerRow;
+  constexpr int kIters = kBlock / kRowsPerIter;
   uint16_t* kdst = k_pool + ((size_t)blk * hkv + g) * kBlock * D;
-  for (int j = lane / kLanesPerRow; j < kBlock; j += kRowsPerIter) {
-    const int t = t0 + j;
-    if (t < 0 || t >= k_eff) continue;
-    const int src = keep_all ? t : keep[t];
+  {
     const int c = lane % kLanesPerRow;
-    const u32x4 val = *reinterpret_cast<const u32x4*>(k_src + ((size_t)(base + src) * hkv + g) * D + c * 8);
-    *reinterpret_cast<u32x4*>(kdst + j * D + c * 8) = val;
+    u32x4 val[kIters];
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+      const int j = it * kRowsPerIter + lane / kLanesPerRow;
+      int src = srcrow[0];
+#pragma unroll
+      for (int jj = 1; jj < kBlock; ++jj) src = j == jj ? srcrow[jj] : src;   // select, no dynamic indexing
+      val[it] = u32x4{0u, 0u, 0u, 0u};
+      if (src >= 0) val[it] = *reinterpret_cast<const u32x4*>(k_src + ((size_t)(base + src) * hkv + g) * D + c * 8);
+    }
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+      const int j = it * kRowsPerIter + lane / kLanesPerRow;
+      if (t0 + j >= 0 && t0 + j < k_eff) *reinterpret_cast<u32x4*>(kdst + j * D + c * 8) = val[it];
+    }
   }
 
   // ---- V: channel-major slots; lane owns channels 2*lane and 2*lane + 1
@@ -70,10 +93,8 @@ __global__ __launch_bounds__(kWavesPerWG * kWave) void compact_kernel(
   if (full) {
     uint32_t pair[kBlock];
 #pragma unroll
-    for (int j = 0; j < kBlock; ++j) {
-      const int src = keep_all ? t0 + j : keep[t0 + j];
-      pair[j] = *reinterpret_cast<const uint32_t*>(v_src + ((size_t)(base + src) * hkv + g) * D + 2 * lane);
-    }
+    for (int j = 0; j < kBlock; ++j)
+      pair[j] = *reinterpret_cast<const uint32_t*>(v_src + ((size_t)(base + srcrow[j]) * hkv + g) * D + 2 * lane);
     u32x4 lo[2], hi[2];   // channel 2*lane (low halves) and 2*lane + 1 (high halves), 16 slots each
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
@@ -86,10 +107,10 @@ __global__ __launch_bounds__(kWavesPerWG * kWave) void compact_kernel(
     d0[0] = lo[0]; d0[1] = lo[1];
     d1[0] = hi[0]; d1[1] = hi[1];
   } else {
+#pragma unroll
     for (int j = 0; j < kBlock; ++j) {
-      const int t = t0 + j;
-      if (t < 0 || t >= k_eff) continue;
-      const int src = keep_all ? t : keep[t];
+      const int src = srcrow[j];
+      if (src < 0) continue;
       const uint32_t x = *reinterpret_cast<const uint32_t*>(v_src + ((size_t)(base + src) * hkv + g) * D + 2 * lane);
       vdst[(size_t)(2 * lane) * kBlock + j] = (uint16_t)(x & 0xffffu);
       vdst[(size_t)(2 * lane + 1) * kBlock + j] = (uint16_t)(x >> 16);

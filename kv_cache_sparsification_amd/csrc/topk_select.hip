@@ -10,10 +10,12 @@
 // equal scores going to the lower index; indices are emitted in ascending order.
 //
 // One workgroup per (prompt, KV head).  Scores are non-negative fp32, so their bit patterns
-// order like unsigned integers: four 8-bit radix passes find the threshold value T (the
-// (k-a)-th largest) and how many copies of T are still needed; a final in-order pass keeps
-// every score above T plus the first `ties` indices equal to T, and writes the kept
-// indices through ballot-based block prefix sums.  No sort, no device-wide traffic.
+// order like unsigned integers: three radix passes (11, 11 and 10 bits) over the candidates
+// find the threshold value T (the (k-a)-th largest) and how many copies of T are still
+// needed.  The candidates are read from memory once, into LDS, when they fit; the passes
+// then run on LDS.  A final pass over contiguous per-thread chunks keeps every score above T
+// plus the first `ties` copies of T (lowest index first), placing them with two block scans,
+// and writes the window after them.  No sort, no device-wide traffic.
 #include "kvs_common.h"
 
 namespace kvs {
@@ -21,23 +23,31 @@ namespace {
 
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / kWave;
+constexpr int kLdsCap = 16384;   // candidates held in LDS (64 KB); longer prompts read L2 each pass
 
-// Exclusive block-wide prefix count of `flag`; returns (prefix, total).
-__device__ __forceinline__ int2 block_count(bool flag, int* wave_tot) {
+// Inclusive scan across the 64 lanes with DPP moves (no LDS): prefix sums within rows of 16
+// lanes by shifts of 1, 2, 4 and 8, then row 0's total into rows 1 and 3 (row_bcast:15) and
+// rows 0-1's total into rows 2 and 3 (row_bcast:31).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31
+  return x;
+}
+
+// Block-wide inclusive scan of one int per thread; `tot` is kWaves ints of LDS, and the
+// caller's next write to it must follow a barrier.
+__device__ __forceinline__ int block_incl_scan(int x, int* tot) {
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
-  const uint64_t m = __ballot(flag);
-  const int in_wave = __popcll(m & ((1ull << lane) - 1ull));
-  if (lane == 0) wave_tot[w] = __popcll(m);
+  x = wave_incl_scan(x);
+  if (lane == kWave - 1) tot[w] = x;
   __syncthreads();
-  int before = 0, total = 0;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
-    const int t = wave_tot[i];
-    before += i < w ? t : 0;
-    total += t;
-  }
-  __syncthreads();   // wave_tot is reused by the next call
-  return make_int2(before + in_wave, total);
+  for (int i = 0; i < kWaves; ++i) x += i < w ? tot[i] : 0;
+  return x;
 }
 
 __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict__ scores,
@@ -45,9 +55,10 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
                                                         int total_tokens, int hkv, int alpha, int k_budget,
                                                         const int32_t* __restrict__ keep_offsets,
                                                         int32_t* __restrict__ keep_idx) {
-  __shared__ int hist[256];
-  __shared__ int wave_tot[kWaves];
-  __shared__ int sel_digit, sel_remaining;
+  extern __shared__ uint32_t cand[];    // up to kLdsCap candidate bit patterns
+  __shared__ int hist[2][2048];    // alternate passes: one is cleared while the other is read
+  __shared__ int tot[2][kWaves];
+  __shared__ int sel_bin, sel_rem;
 
   const int g = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
   const int base = cu_seqlens[s];
@@ -62,61 +73,79 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   const int a = alpha < n ? alpha : n;
   const int n_cand = n - a;
   const int kk = k_budget - a;   // slots filled by score (0 when the budget is the window)
+  // the window follows the kk chosen candidates (its indices are all larger)
+  for (int i = n_cand + tid; i < n; i += kThreads) out[kk + i - n_cand] = i;
+  if (kk == 0) return;
   const uint32_t* bits = reinterpret_cast<const uint32_t*>(scores + (size_t)g * total_tokens + base);
+  const bool in_lds = n_cand <= kLdsCap;   // block-uniform
+  if (in_lds) {
+    for (int i = tid; i < n_cand; i += kThreads) cand[i] = bits[i];
+  }
+  auto at = [&](int i) { return in_lds ? cand[i] : bits[i]; };
 
   uint32_t prefix = 0, mask = 0;
   int remaining = kk;
-  if (kk > 0) {
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      if (tid < 256) hist[tid] = 0;
-      __syncthreads();
-      for (int i = tid; i < n_cand; i += kThreads) {
-        const uint32_t u = bits[i];
-        if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 0xffu], 1);
-      }
-      __syncthreads();
-      // Thread t < 256 looks at digit b = 255 - t; an inclusive scan from the top gives the
-      // number of candidates with digit >= b.  The selected digit is where that count first
-      // reaches `remaining`.  Threads >= 256 take part with a zero count.
-      {
-        const int lane = tid % kWave, w = tid / kWave;
-        const int x = tid < 256 ? hist[255 - tid] : 0;
-        int incl = x;
+  for (int b = tid; b < 2048; b += kThreads) hist[0][b] = 0;
+  __syncthreads();   // also publishes the candidates in LDS
 #pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-          const int y = __shfl_up(incl, o, kWave);
-          if (lane >= o) incl += y;
-        }
-        if (lane == kWave - 1) wave_tot[w] = incl;
-        __syncthreads();
-        for (int q = 0; q < w; ++q) incl += wave_tot[q];
-        if (tid < 256 && incl >= remaining && incl - x < remaining) {
-          sel_digit = 255 - tid;
-          sel_remaining = remaining - (incl - x);
-        }
-      }
-      __syncthreads();
-      prefix |= (uint32_t)sel_digit << shift;
-      mask |= 0xffu << shift;
-      remaining = sel_remaining;
-      __syncthreads();   // sel_* and hist are rewritten next pass
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : pass == 1 ? 10 : 0;
+    const int nbins = pass == 2 ? 1024 : 2048;
+    int* hs = hist[pass & 1];
+    for (int i = tid; i < n_cand; i += kThreads) {
+      const uint32_t u = at(i);
+      if ((u & mask) == prefix) atomicAdd(&hs[(u >> shift) & (nbins - 1)], 1);
     }
+    if (pass < 2) {   // the next pass's histogram; its last reader finished two barriers ago
+      for (int b = tid; b < 2048; b += kThreads) hist[(pass + 1) & 1][b] = 0;
+    }
+    __syncthreads();
+    // Thread t owns bins hi = nbins-1-t*per down to hi-per+1; a scan in thread order counts the
+    // candidates at or above each thread's lowest bin.  The thread where that count first
+    // reaches `remaining` finds the bin holding the remaining-th largest.
+    const int per = nbins / kThreads;
+    const int hi = nbins - 1 - tid * per;
+    int local = 0;
+    for (int j = 0; j < per; ++j) local += hs[hi - j];
+    const int incl = block_incl_scan(local, tot[pass & 1]);
+    if (incl >= remaining && incl - local < remaining) {
+      int cum = incl - local;
+      for (int j = 0; j < per; ++j) {
+        const int c = hs[hi - j];
+        if (cum + c >= remaining) {
+          sel_bin = hi - j;
+          sel_rem = remaining - cum;
+          break;
+        }
+        cum += c;
+      }
+    }
+    __syncthreads();
+    prefix |= (uint32_t)sel_bin << shift;
+    mask |= (uint32_t)(nbins - 1) << shift;
+    remaining = sel_rem;
+    // sel_* are rewritten one pass later, after that pass's two barriers
   }
   const uint32_t T = prefix;
-  const int ties = remaining;   // copies of T still to take, lowest index first
+  const int ties = remaining;   // copies of T to take, lowest index first
 
-  int carry_eq = 0, carry_out = 0;
-  for (int c0 = 0; c0 < n; c0 += kThreads) {
-    const int i = c0 + tid;
-    const bool cand = i < n_cand;
-    const uint32_t u = cand ? bits[i] : 0u;
-    const bool is_eq = kk > 0 && cand && u == T;
-    const int2 eq = block_count(is_eq, wave_tot);
-    const bool sel = (kk > 0 && cand && (u > T || (is_eq && carry_eq + eq.x < ties))) || (i >= n_cand && i < n);
-    const int2 pos = block_count(sel, wave_tot);
-    if (sel) out[carry_out + pos.x] = i;
-    carry_eq += eq.y;
-    carry_out += pos.y;
+  // Contiguous chunk per thread, in index order.
+  const int per = (n_cand + kThreads - 1) / kThreads;
+  const int c0 = min(tid * per, n_cand), c1 = min(c0 + per, n_cand);
+  int gt = 0, eq = 0;
+  for (int i = c0; i < c1; ++i) {
+    const uint32_t u = at(i);
+    gt += u > T;
+    eq += u == T;
+  }
+  const int eq_before = block_incl_scan(eq, tot[1]) - eq;   // tot[1] was last read in pass 1
+  const int take_eq = min(max(ties - eq_before, 0), eq);
+  const int sel = gt + take_eq;
+  int pos = block_incl_scan(sel, tot[0]) - sel;             // tot[0] was last read in pass 2
+  int e = eq_before;
+  for (int i = c0; i < c1; ++i) {
+    const uint32_t u = at(i);
+    if (u > T || (u == T && e++ < ties)) out[pos++] = i;
   }
 }
 
@@ -134,7 +163,8 @@ extern "C" int kvs_topk_select(const float* scores, const int32_t* cu_seqlens, i
   if (alpha < 1 || k_budget < alpha)
     return fail(KVS_E_INVAL, "kvs_topk_select: need 1 <= alpha <= k_budget (alpha=%d k=%d)", alpha, k_budget);
   if (num_seqs == 0 || total_tokens == 0) return KVS_OK;
-  hipLaunchKernelGGL(topk_kernel, dim3(hkv, num_seqs), dim3(kThreads), 0, as_stream(stream), scores, cu_seqlens,
+  const size_t lds = (size_t)min(max(max_seqlen, 1), kLdsCap) * sizeof(uint32_t);
+  hipLaunchKernelGGL(topk_kernel, dim3(hkv, num_seqs), dim3(kThreads), lds, as_stream(stream), scores, cu_seqlens,
                      total_tokens, hkv, alpha, k_budget, keep_offsets, keep_idx);
   return launch_status("kvs_topk_select");
 }

@@ -15,7 +15,8 @@
 // MI355X form.  A workgroup (4 wavefronts) owns 128 consecutive keys of one KV head; each
 // wavefront owns 32 keys, which are the N dimension of a bf16 32x32x16 MFMA, while the
 // G * a window rows of the group's query heads are the M dimension, staged through LDS in
-// chunks of 64 rows together with LSE * log2(e) and each row's causal limit.  Every lane
+// chunks of 128 rows (one chunk for 4 query heads x a 32-token window) together with
+// LSE * log2(e) and each row's causal limit.  Every lane
 // ends up holding 16 (row, key) products for one key, so the window sum is 16 adds in
 // registers per M tile plus a single cross-lane add at the end: the pages' "row sum in
 // registers".  The key fragment is read from HBM once and kept in registers; nothing but
@@ -28,7 +29,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kKeysPerWave = 32;
 constexpr int kKeysPerWG = kWaves * kKeysPerWave;
-constexpr int kRowChunk = 64;   // window rows staged in LDS at a time (2 M tiles)
+constexpr int kRowChunk = 128;  // window rows staged in LDS at a time (4 M tiles)
 
 template <int D>
 __global__ __launch_bounds__(kWaves * kWave) void window_score_kernel(

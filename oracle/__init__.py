@@ -26,8 +26,11 @@ Modules and the step each one follows:
                 blocks between sequences", "Related techniques")
   decode        attention of one new token over a paged cache ([PAG] "How
                 paging works"; [KVS] Key techniques 2, last paragraph)
+  eviction      decode-time scores and the replacement of the lowest-score
+                token in a full compressed layer ([KVS] Key techniques 1, step
+                preparation; Key techniques 2, last paragraph)
 
-Readings taken where the pages are silent or garbled are named R1..R19 in the
+Readings taken where the pages are silent or garbled are named R1..R21 in the
 docstrings; each one is listed with its justification in the design notes.
 Every function is pinned by the CPU tests (``pytest -m "not gpu"``); none is
 "parity unpinned".
@@ -37,6 +40,7 @@ from .window_score import window_score, window_score_from_probs, visited_pairs
 from .topk import select_keep, keep_count
 from .paged import BlockAllocator, blocks_for, write_rows, gather_rows, compact_into_pool
 from .decode import decode_attention
+from .eviction import SlotCache, init_cache, select_slot, decode_step
 
 __all__ = [
     "causal_attention", "attention_probs",
@@ -44,4 +48,5 @@ __all__ = [
     "select_keep", "keep_count",
     "BlockAllocator", "blocks_for", "write_rows", "gather_rows", "compact_into_pool",
     "decode_attention",
+    "SlotCache", "init_cache", "select_slot", "decode_step",
 ]

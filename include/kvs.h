@@ -167,6 +167,63 @@ int kvs_paged_decode(const void* q, void* k_pool, void* v_pool, int num_blocks,
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decode-time scores and eviction in a compressed layer.
+ *   [KVS] Key techniques 1 (step preparation): the layers after the third use a
+ *   sliding-window strategy that replaces the KV entries with the lowest scores under a
+ *   fixed budget; Key techniques 2, last paragraph: PagedAttention shares FlashAttention's
+ *   goal of computing the score S.
+ * Slot state, per sequence b, KV head g and slot t, row stride slot_stride (>= the
+ * cache's capacity; slot t lives at block table_b[t/16], slot t%16):
+ *   slot_scores [B][hkv][slot_stride] fp32  accumulated score, >= 0;
+ *   slot_pos    [B][hkv][slot_stride] int32 prompt-local position of the token, -1 if empty.
+ * A decode step of a full cache: kvs_decode_select_slot picks each head's slot for the new
+ * token, then kvs_paged_decode_scored writes it there, attends and adds every live slot's
+ * probability (summed over the group's query heads) to its score.
+ */
+
+/*
+ * kvs_slot_init - slot state after compaction.  Slot t < k_eff_s of head g gets the kept
+ * token keep(g, t) (layout of kvs_topk_select; t itself when keep_idx is NULL) with score
+ * S[g][cu_seqlens[s] + keep(g, t)]; slots from k_eff_s to slot_stride-1 get score 0 and
+ * position -1.  scores: [hkv][total_tokens] fp32 (kvs_window_score's output).
+ * Errors: KVS_E_INVAL on a NULL tensor or bad shape; KVS_E_HIP on launch failure.
+ */
+int kvs_slot_init(const float* scores, const int32_t* keep_idx, const int32_t* keep_offsets,
+                  const int32_t* cu_seqlens, int num_seqs, int total_tokens, int hkv, int slot_stride,
+                  float* slot_scores, int32_t* slot_pos, void* stream);
+
+/*
+ * kvs_decode_select_slot - where each KV head writes the new token of sequence b, whose
+ * cache holds n_filled[b] tokens before the step, at position new_pos[b].
+ *   n_filled[b] < cap: slot n_filled[b] (append, every head);
+ *   otherwise: the slot with the lowest score among tokens at positions
+ *   < new_pos[b] - alpha (the alpha most recent tokens stay), ties to the lower position.
+ * The chosen slot's score becomes 0 and its position new_pos[b] (slot_scores, slot_pos are
+ * read and written).  Out: dst_slot [B][hkv] int32.
+ * Errors: KVS_E_INVAL unless 0 <= alpha < cap <= slot_stride; KVS_E_HIP on launch failure.
+ */
+int kvs_decode_select_slot(float* slot_scores, int32_t* slot_pos, int slot_stride, const int32_t* n_filled,
+                           int batch, int hkv, int cap, const int32_t* new_pos, int alpha, int32_t* dst_slot,
+                           void* stream);
+
+/*
+ * kvs_paged_decode_scored - kvs_paged_decode whose new token goes to slot dst_slots[b][g]
+ * of head g (NULL: slot L-1 for every head), and which adds, for every live slot t < L,
+ * sum_{h in group(g)} exp(scale*<q_bh, K_t> - lse_bh) to slot_scores[b][g][t] after the
+ * attention.  ctx_lens[b] = L counts the live slots after the write.  slot_stride >=
+ * max_ctx.  Workspace: kvs_paged_decode_scored_workspace_size(...) bytes (never 0): the
+ * split partials and the step's logits.  Calls sharing a workspace must not overlap.
+ * Errors: as kvs_paged_decode; KVS_E_INVAL also for a NULL slot_scores or dst_slots given
+ * without new_k/new_v.
+ */
+size_t kvs_paged_decode_scored_workspace_size(int batch, int hq, int hkv, int d, int max_ctx);
+int kvs_paged_decode_scored(const void* q, void* k_pool, void* v_pool, int num_blocks, const int32_t* block_tables,
+                            int max_blocks, const int32_t* ctx_lens, int batch, int max_ctx, int hq, int hkv, int d,
+                            float scale, const void* new_k, const void* new_v, const int32_t* dst_slots,
+                            float* slot_scores, int slot_stride, void* o, float* lse_opt, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
  * kvs_copy_blocks - device side of copy-on-write: whole-block copies in both pools.
  *   [PAG] "Sharing blocks between sequences": a sequence that must write a block still
  *   used by others copies it first.

@@ -8,7 +8,9 @@ into the C ABI declared in include/kvs.h; importing it fails if the library is n
 """
 from ._lib import lib, KvsError, BLOCK_SIZE, LIB_PATH
 from .ops import (kvs_prefill_attn_lse, kvs_window_score, kvs_topk_select, kvs_compact_paged,
-                  kvs_paged_decode, kvs_paged_decode_workspace_size, kvs_copy_blocks, new_pools)
+                  kvs_paged_decode, kvs_paged_decode_workspace_size, kvs_copy_blocks, new_pools,
+                  kvs_slot_init, kvs_decode_select_slot, kvs_paged_decode_scored,
+                  kvs_paged_decode_scored_workspace_size)
 from .allocator import BlockAllocator
 from .pipeline import layer_policy, keep_counts, prefill_compress_layer
 
@@ -16,5 +18,6 @@ __all__ = [
     "lib", "KvsError", "BLOCK_SIZE", "LIB_PATH",
     "kvs_prefill_attn_lse", "kvs_window_score", "kvs_topk_select", "kvs_compact_paged",
     "kvs_paged_decode", "kvs_paged_decode_workspace_size", "kvs_copy_blocks", "new_pools",
+    "kvs_slot_init", "kvs_decode_select_slot", "kvs_paged_decode_scored", "kvs_paged_decode_scored_workspace_size",
     "BlockAllocator", "layer_policy", "keep_counts", "prefill_compress_layer",
 ]

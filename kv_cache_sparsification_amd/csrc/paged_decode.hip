@@ -82,12 +82,22 @@ inline Plan choose_plan(int batch, int hq, int hkv, int d, int max_ctx) {
   return p;
 }
 
+// Extras of the scored decode (decode-time scores and eviction): the slot each KV head
+// writes the new token to, the log2-scaled logits of every (query head, slot) for the score
+// pass, and partials even for a single split (the merge-and-score kernel reads them).
+struct DecodeExtra {
+  const int32_t* dst_slots;   // [batch][hkv], or NULL: slot L-1 for every head
+  float* logits;              // [batch][hq][logit_stride], or NULL
+  int logit_stride;
+  int force_partials;
+};
+
 template <int D, int W, int kNB>
 __global__ __launch_bounds__(W * kWave) void decode_kernel(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ k_pool, uint16_t* __restrict__ v_pool, int num_blocks,
     const int32_t* __restrict__ tables, int max_blocks, const int32_t* __restrict__ ctx_lens, int hq, int hkv,
     float c_log2, const uint16_t* __restrict__ new_k, const uint16_t* __restrict__ new_v, uint16_t* __restrict__ o,
-    float* __restrict__ lse_out, float* __restrict__ ws, int splits, int bps) {
+    float* __restrict__ lse_out, float* __restrict__ ws, int splits, int bps, DecodeExtra ex) {
   constexpr int KS = D / 32;     // k-steps of the score product
   constexpr int MT = D / 16;     // d tiles of the output product
   constexpr int NT = W * kWave;
@@ -126,8 +136,9 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
     qf[st] = __builtin_bit_cast(bf16x8, x);
   }
 
-  const int last_blk = (L - 1) / kBlock, last_slot = (L - 1) % kBlock;
-  const bool append = new_k != nullptr && new_v != nullptr;
+  const int dst = ex.dst_slots ? ex.dst_slots[b * hkv + g] : L - 1;   // slot of the new token
+  const int last_blk = dst / kBlock, last_slot = dst % kBlock;
+  const bool append = new_k != nullptr && new_v != nullptr && dst >= 0 && dst < L;   // else nothing is written
   const uint16_t* nk = new_k + ((size_t)b * hkv + g) * D;
   const uint16_t* nv = new_v + ((size_t)b * hkv + g) * D;
 
@@ -184,6 +195,7 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
         const int t = bi * kBlock + grp * 4 + i;
         x[i] = t < L ? sc[i] * c_log2 : -INFINITY;
         bm = fmaxf(bm, x[i]);
+        if (ex.logits && col < G && t < L) ex.logits[((size_t)b * hq + g * G + col) * ex.logit_stride + t] = x[i];
       }
       bm = fmaxf(bm, wave_xor(bm, 16));
       bm = fmaxf(bm, wave_xor(bm, 32));
@@ -253,7 +265,7 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
       acc += s_o[((size_t)v * G + c) * D + dd] * wgt;
     }
     const int h = g * G + c;
-    if (used == 1) {
+    if (used == 1 && !ex.force_partials) {
       o[((size_t)b * hq + h) * D + dd] = (uint16_t)f32_to_bf16_bits(acc / l);
       if (lse_out && dd == 0) lse_out[(size_t)b * hq + h] = (m + log2f(l)) * kLn2;
     } else {
@@ -272,46 +284,91 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
 // channel plus the (max, sum) pair, shared with its neighbours through L1) before using any,
 // then folds the chunk into a running (max, sum, output) - one memory round trip per 16
 // splits instead of one per split.
+// Fold the `used` split partials of one (sequence, query head) for output channel dd:
+// returns the running max M (log2 units), the sum l against it and the output numerator.
+template <int D>
+__device__ __forceinline__ void merge_partials(const float* __restrict__ part, int used, int dd, float& M, float& l,
+                                               float& acc) {
+  constexpr int C = 16;
+  M = -INFINITY;
+  l = 0.f;
+  acc = 0.f;
+  for (int sp0 = 0; sp0 < used; sp0 += C) {
+    float mv[C], lv[C], ov[C];
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+      const bool in = sp0 + i < used;
+      const float* ps = part + (size_t)(in ? sp0 + i : 0) * (D + 2);
+      mv[i] = in ? ps[0] : -INFINITY;
+      lv[i] = in ? ps[1] : 0.f;
+      ov[i] = in ? ps[2 + dd] : 0.f;
+    }
+    float cm = M;
+#pragma unroll
+    for (int i = 0; i < C; ++i) cm = fmaxf(cm, mv[i]);
+    const float corr = __builtin_amdgcn_exp2f(M - cm);   // first chunk: exp2(-inf) = 0
+    l *= corr;
+    acc *= corr;
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+      const float wgt = __builtin_amdgcn_exp2f(mv[i] - cm);
+      l += lv[i] * wgt;
+      acc += ov[i] * wgt;
+    }
+    M = cm;
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict__ ws,
                                                          const int32_t* __restrict__ ctx_lens, int hq, int hkv,
                                                          int max_blocks, int splits, int bps,
                                                          uint16_t* __restrict__ o, float* __restrict__ lse_out) {
-  constexpr int C = 16;
   const int h = blockIdx.x, b = blockIdx.y, dd = threadIdx.x;
   const int L = ctx_lens[b];
   const int nblk = min((L + kBlock - 1) / kBlock, max_blocks);
   const int used = min((nblk + bps - 1) / bps, splits);
   if (used <= 1) return;                      // written directly by the decode kernel
   {
-    const float* part = ws + ((size_t)b * hq + h) * splits * (D + 2);
-    float M = -INFINITY, l = 0.f, acc = 0.f;
-    for (int sp0 = 0; sp0 < used; sp0 += C) {
-      float mv[C], lv[C], ov[C];
-#pragma unroll
-      for (int i = 0; i < C; ++i) {
-        const bool in = sp0 + i < used;
-        const float* ps = part + (size_t)(in ? sp0 + i : 0) * (D + 2);
-        mv[i] = in ? ps[0] : -INFINITY;
-        lv[i] = in ? ps[1] : 0.f;
-        ov[i] = in ? ps[2 + dd] : 0.f;
-      }
-      float cm = M;
-#pragma unroll
-      for (int i = 0; i < C; ++i) cm = fmaxf(cm, mv[i]);
-      const float corr = __builtin_amdgcn_exp2f(M - cm);   // first chunk: exp2(-inf) = 0
-      l *= corr;
-      acc *= corr;
-#pragma unroll
-      for (int i = 0; i < C; ++i) {
-        const float wgt = __builtin_amdgcn_exp2f(mv[i] - cm);
-        l += lv[i] * wgt;
-        acc += ov[i] * wgt;
-      }
-      M = cm;
-    }
+    float M, l, acc;
+    merge_partials<D>(ws + ((size_t)b * hq + h) * splits * (D + 2), used, dd, M, l, acc);
     o[((size_t)b * hq + h) * D + dd] = (uint16_t)f32_to_bf16_bits(acc / l);
     if (lse_out && dd == 0) lse_out[(size_t)b * hq + h] = (M + log2f(l)) * kLn2;
+  }
+}
+
+// Scored decode, second kernel: one workgroup per (KV head, sequence).  Merges the partials
+// of the G query heads (output, LSE), then adds every live slot's probability summed over
+// those heads, exp2(logit - LSE2), to its score: the decode row's contribution to S.
+template <int D>
+__global__ __launch_bounds__(256) void decode_merge_score_kernel(
+    const float* __restrict__ ws, const float* __restrict__ logits, int logit_stride,
+    const int32_t* __restrict__ ctx_lens, int hq, int hkv, int max_blocks, int splits, int bps,
+    uint16_t* __restrict__ o, float* __restrict__ lse_out, float* __restrict__ slot_scores, int slot_stride) {
+  __shared__ float lse2[16];
+  const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int G = hq / hkv;
+  const int L = ctx_lens[b];
+  const int nblk = min((L + kBlock - 1) / kBlock, max_blocks);
+  const int used = min((nblk + bps - 1) / bps, splits);
+  for (int e = tid; e < G * D; e += 256) {
+    const int c = e / D, dd = e % D;
+    const int h = g * G + c;
+    float M, l, acc;
+    merge_partials<D>(ws + ((size_t)b * hq + h) * splits * (D + 2), used, dd, M, l, acc);
+    o[((size_t)b * hq + h) * D + dd] = (uint16_t)f32_to_bf16_bits(acc / l);
+    if (dd == 0) {
+      lse2[c] = M + log2f(l);
+      if (lse_out) lse_out[(size_t)b * hq + h] = (M + log2f(l)) * kLn2;
+    }
+  }
+  __syncthreads();
+  const float* lg = logits + ((size_t)b * hq + g * G) * logit_stride;
+  float* sc = slot_scores + ((size_t)b * hkv + g) * slot_stride;
+  for (int t = tid; t < L; t += 256) {
+    float sum = 0.f;
+    for (int c = 0; c < G; ++c) sum += __builtin_amdgcn_exp2f(lg[(size_t)c * logit_stride + t] - lse2[c]);
+    sc[t] += sum;
   }
 }
 
@@ -331,30 +388,31 @@ extern "C" size_t kvs_paged_decode_workspace_size(int batch, int hq, int hkv, in
 template <int D, int W, int NB>
 static void launch_one(const Plan& p, dim3 grid, size_t lds, hipStream_t st, const uint16_t* q, uint16_t* kp,
                        uint16_t* vp, int num_blocks, const int32_t* tables, int max_blocks, const int32_t* ctx, int hq,
-                       int hkv, float c, const uint16_t* nk, const uint16_t* nv, uint16_t* o, float* lse, float* ws) {
+                       int hkv, float c, const uint16_t* nk, const uint16_t* nv, uint16_t* o, float* lse, float* ws,
+                       const DecodeExtra& ex) {
   hipLaunchKernelGGL((decode_kernel<D, W, NB>), grid, dim3(W * kWave), lds, st, q, kp, vp, num_blocks, tables,
-                     max_blocks, ctx, hq, hkv, c, nk, nv, o, lse, ws, p.splits, p.bps);
+                     max_blocks, ctx, hq, hkv, c, nk, nv, o, lse, ws, p.splits, p.bps, ex);
 }
 
 template <int D>
 static void launch_decode(const Plan& p, dim3 grid, size_t lds, hipStream_t st, const uint16_t* q, uint16_t* kp,
                           uint16_t* vp, int num_blocks, const int32_t* tables, int max_blocks, const int32_t* ctx,
                           int hq, int hkv, float c, const uint16_t* nk, const uint16_t* nv, uint16_t* o, float* lse,
-                          float* ws) {
+                          float* ws, const DecodeExtra& ex) {
   constexpr int NB = D == 64 ? 2 : 4;
   if constexpr (D == 64) {   // 16 wavefronts only where their registers hold NB blocks
     if (p.waves == 16) {
       launch_one<D, 16, NB>(p, grid, lds, st, q, kp, vp, num_blocks, tables, max_blocks, ctx, hq, hkv, c, nk, nv, o,
-                            lse, ws);
+                            lse, ws, ex);
       return;
     }
   }
   if (p.waves == 8)
     launch_one<D, 8, NB>(p, grid, lds, st, q, kp, vp, num_blocks, tables, max_blocks, ctx, hq, hkv, c, nk, nv, o,
-                         lse, ws);
+                         lse, ws, ex);
   else
     launch_one<D, 4, NB>(p, grid, lds, st, q, kp, vp, num_blocks, tables, max_blocks, ctx, hq, hkv, c, nk, nv, o,
-                         lse, ws);
+                         lse, ws, ex);
 }
 
 extern "C" int kvs_paged_decode(const void* q, void* k_pool, void* v_pool, int num_blocks, const int32_t* block_tables,
@@ -386,12 +444,13 @@ extern "C" int kvs_paged_decode(const void* q, void* k_pool, void* v_pool, int n
   auto* oo = static_cast<uint16_t*>(o);
   float* ws = static_cast<float*>(workspace);
   hipStream_t st = as_stream(stream);
+  const DecodeExtra ex{nullptr, nullptr, 0, 0};
   if (d == 128)
     launch_decode<128>(p, grid, lds, st, qq, kp, vp, num_blocks, block_tables, max_blocks, ctx_lens, hq, hkv, c, nk, nv,
-                       oo, lse_opt, ws);
+                       oo, lse_opt, ws, ex);
   else
     launch_decode<64>(p, grid, lds, st, qq, kp, vp, num_blocks, block_tables, max_blocks, ctx_lens, hq, hkv, c, nk, nv,
-                      oo, lse_opt, ws);
+                      oo, lse_opt, ws, ex);
   int rc = launch_status("kvs_paged_decode");
   if (rc != KVS_OK || p.splits == 1) return rc;
   if (d == 128)
@@ -401,4 +460,70 @@ extern "C" int kvs_paged_decode(const void* q, void* k_pool, void* v_pool, int n
     hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(hq, batch), dim3(64), 0, st, ws, ctx_lens, hq, hkv, max_blocks,
                        p.splits, p.bps, oo, lse_opt);
   return launch_status("kvs_paged_decode (merge)");
+}
+
+// ---- Scored decode: partials (always, even for one split) then the logits.
+static size_t scored_logits_offset(int batch, int hq, int splits, int d) {
+  const size_t part = (size_t)batch * hq * splits * (d + 2) * sizeof(float);
+  return (part + 255) / 256 * 256;
+}
+
+extern "C" size_t kvs_paged_decode_scored_workspace_size(int batch, int hq, int hkv, int d, int max_ctx) {
+  if (batch <= 0 || hq <= 0 || hkv <= 0 || hq % hkv || max_ctx <= 0 || d <= 0) return 0;
+  const Plan p = choose_plan(batch, hq, hkv, d, max_ctx);
+  return scored_logits_offset(batch, hq, p.splits, d) + (size_t)batch * hq * max_ctx * sizeof(float);
+}
+
+extern "C" int kvs_paged_decode_scored(const void* q, void* k_pool, void* v_pool, int num_blocks,
+                                       const int32_t* block_tables, int max_blocks, const int32_t* ctx_lens, int batch,
+                                       int max_ctx, int hq, int hkv, int d, float scale, const void* new_k,
+                                       const void* new_v, const int32_t* dst_slots, float* slot_scores,
+                                       int slot_stride, void* o, float* lse_opt, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  if (!q || !k_pool || !v_pool || !block_tables || !ctx_lens || !o || !slot_scores)
+    return fail(KVS_E_INVAL, "kvs_paged_decode_scored: NULL tensor");
+  if ((new_k == nullptr) != (new_v == nullptr))
+    return fail(KVS_E_INVAL, "kvs_paged_decode_scored: new_k and new_v go together");
+  if (dst_slots && !new_k) return fail(KVS_E_INVAL, "kvs_paged_decode_scored: dst_slots without a new token");
+  if (batch < 0 || max_ctx < 1 || hq <= 0 || hkv <= 0 || hq % hkv || hq / hkv > 16 || (d != 64 && d != 128) ||
+      num_blocks <= 0 || max_blocks <= 0 || !(scale > 0.f) || slot_stride < max_ctx)
+    return fail(KVS_E_INVAL, "kvs_paged_decode_scored: bad shape (batch=%d hq=%d hkv=%d d=%d max_ctx=%d stride=%d)",
+                batch, hq, hkv, d, max_ctx, slot_stride);
+  if ((long long)max_blocks * kBlock < max_ctx)
+    return fail(KVS_E_INVAL, "kvs_paged_decode_scored: max_blocks*16 < max_ctx");
+  if (batch == 0) return KVS_OK;
+  const Plan p = choose_plan(batch, hq, hkv, d, max_ctx);
+  const size_t need = kvs_paged_decode_scored_workspace_size(batch, hq, hkv, d, max_ctx);
+  if (!workspace || workspace_bytes < need)
+    return fail(KVS_E_INVAL, "kvs_paged_decode_scored: workspace of %zu bytes needed, %zu given", need,
+                workspace_bytes);
+  const float c = scale * kLog2e;
+  const int G = hq / hkv;
+  const size_t lds = ((size_t)p.waves * G * d + 2 * (size_t)p.waves * 16) * sizeof(float);
+  dim3 grid(p.splits, hkv, batch);
+  auto* qq = static_cast<const uint16_t*>(q);
+  auto* kp = static_cast<uint16_t*>(k_pool);
+  auto* vp = static_cast<uint16_t*>(v_pool);
+  auto* nk = static_cast<const uint16_t*>(new_k);
+  auto* nv = static_cast<const uint16_t*>(new_v);
+  auto* oo = static_cast<uint16_t*>(o);
+  float* ws = static_cast<float*>(workspace);
+  float* logits = reinterpret_cast<float*>(static_cast<char*>(workspace) + scored_logits_offset(batch, hq, p.splits, d));
+  hipStream_t st = as_stream(stream);
+  const DecodeExtra ex{dst_slots, logits, max_ctx, 1};
+  if (d == 128)
+    launch_decode<128>(p, grid, lds, st, qq, kp, vp, num_blocks, block_tables, max_blocks, ctx_lens, hq, hkv, c, nk, nv,
+                       oo, lse_opt, ws, ex);
+  else
+    launch_decode<64>(p, grid, lds, st, qq, kp, vp, num_blocks, block_tables, max_blocks, ctx_lens, hq, hkv, c, nk, nv,
+                      oo, lse_opt, ws, ex);
+  int rc = launch_status("kvs_paged_decode_scored");
+  if (rc != KVS_OK) return rc;
+  if (d == 128)
+    hipLaunchKernelGGL(decode_merge_score_kernel<128>, dim3(hkv, batch), dim3(256), 0, st, ws, logits, max_ctx,
+                       ctx_lens, hq, hkv, max_blocks, p.splits, p.bps, oo, lse_opt, slot_scores, slot_stride);
+  else
+    hipLaunchKernelGGL(decode_merge_score_kernel<64>, dim3(hkv, batch), dim3(256), 0, st, ws, logits, max_ctx,
+                       ctx_lens, hq, hkv, max_blocks, p.splits, p.bps, oo, lse_opt, slot_scores, slot_stride);
+  return launch_status("kvs_paged_decode_scored (merge and score)");
 }

@@ -134,6 +134,72 @@ def kvs_paged_decode(q, k_pool, v_pool, block_tables, ctx_lens, max_ctx: int, sc
     return o
 
 
+def kvs_slot_init(scores, cu_seqlens, keep_idx, keep_offsets, slot_stride: int, slot_scores=None, slot_pos=None,
+                  stream=None):
+    """Slot state after compaction: scores/positions [S][Hkv][slot_stride] (keep_idx None: keep all)."""
+    _dev(scores, torch.float32, "scores"); _dev(cu_seqlens, torch.int32, "cu_seqlens")
+    hkv, T = scores.shape
+    S = cu_seqlens.shape[0] - 1
+    if keep_idx is not None:
+        _dev(keep_idx, torch.int32, "keep_idx"); _dev(keep_offsets, torch.int32, "keep_offsets")
+    if slot_scores is None:
+        slot_scores = torch.empty(S, hkv, slot_stride, device=scores.device, dtype=torch.float32)
+    if slot_pos is None:
+        slot_pos = torch.empty(S, hkv, slot_stride, device=scores.device, dtype=torch.int32)
+    _dev(slot_scores, torch.float32, "slot_scores"); _dev(slot_pos, torch.int32, "slot_pos")
+    check(lib.kvs_slot_init(scores.data_ptr(), _ptr(keep_idx), _ptr(keep_offsets), cu_seqlens.data_ptr(), S, T, hkv,
+                            int(slot_stride), slot_scores.data_ptr(), slot_pos.data_ptr(), _stream(stream)))
+    return slot_scores, slot_pos
+
+
+def kvs_decode_select_slot(slot_scores, slot_pos, n_filled, new_pos, cap: int, alpha: int, dst_slot=None,
+                           stream=None):
+    """Slot of the new token per (sequence, KV head) [B][Hkv] int32 (updates the slot state)."""
+    _dev(slot_scores, torch.float32, "slot_scores"); _dev(slot_pos, torch.int32, "slot_pos")
+    _dev(n_filled, torch.int32, "n_filled"); _dev(new_pos, torch.int32, "new_pos")
+    B, hkv, stride = slot_scores.shape
+    if dst_slot is None:
+        dst_slot = torch.empty(B, hkv, device=slot_scores.device, dtype=torch.int32)
+    _dev(dst_slot, torch.int32, "dst_slot")
+    check(lib.kvs_decode_select_slot(slot_scores.data_ptr(), slot_pos.data_ptr(), stride, n_filled.data_ptr(), B, hkv,
+                                     int(cap), new_pos.data_ptr(), int(alpha), dst_slot.data_ptr(), _stream(stream)))
+    return dst_slot
+
+
+def kvs_paged_decode_scored_workspace_size(batch: int, hq: int, hkv: int, d: int, max_ctx: int) -> int:
+    return int(lib.kvs_paged_decode_scored_workspace_size(batch, hq, hkv, d, max_ctx))
+
+
+def kvs_paged_decode_scored(q, k_pool, v_pool, block_tables, ctx_lens, max_ctx: int, slot_scores, new_k=None,
+                            new_v=None, dst_slots=None, scale: Optional[float] = None, o=None, lse=None,
+                            workspace=None, stream=None):
+    """Decode step writing the new token to dst_slots (per head) and adding its probabilities to slot_scores."""
+    _dev(q, torch.bfloat16, "q"); _dev(k_pool, torch.bfloat16, "k_pool"); _dev(v_pool, torch.bfloat16, "v_pool")
+    _dev(block_tables, torch.int32, "block_tables"); _dev(ctx_lens, torch.int32, "ctx_lens")
+    _dev(slot_scores, torch.float32, "slot_scores")
+    B, hq, d = q.shape
+    hkv = k_pool.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if new_k is not None:
+        _dev(new_k, torch.bfloat16, "new_k"); _dev(new_v, torch.bfloat16, "new_v")
+    if dst_slots is not None:
+        _dev(dst_slots, torch.int32, "dst_slots")
+    o = torch.empty_like(q) if o is None else _dev(o, torch.bfloat16, "o")
+    if lse is not None:
+        _dev(lse, torch.float32, "lse")
+    need = kvs_paged_decode_scored_workspace_size(B, hq, hkv, d, int(max_ctx))
+    if workspace is None:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    check(lib.kvs_paged_decode_scored(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), k_pool.shape[0],
+                                      block_tables.data_ptr(), block_tables.shape[1], ctx_lens.data_ptr(), B,
+                                      int(max_ctx), hq, hkv, d, float(scale), _ptr(new_k), _ptr(new_v),
+                                      _ptr(dst_slots), slot_scores.data_ptr(), slot_scores.shape[2], o.data_ptr(),
+                                      _ptr(lse), workspace.data_ptr(), ws_bytes, _stream(stream)))
+    return o
+
+
 def kvs_copy_blocks(k_pool, v_pool, src_dst_pairs, stream=None):
     """Copy whole blocks (both pools): src_dst_pairs [n][2] int32 device."""
     _dev(k_pool, torch.bfloat16, "k_pool"); _dev(v_pool, torch.bfloat16, "v_pool")

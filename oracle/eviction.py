@@ -79,17 +79,19 @@ def select_slot(score: np.ndarray, pos: np.ndarray, n: int, cap: int, new_pos: i
 
 
 def decode_step(c: SlotCache, q: np.ndarray, new_k: np.ndarray, new_v: np.ndarray, new_pos: int, alpha: int,
-                scale: Optional[float] = None):
+                scale: Optional[float] = None, dst: Optional[np.ndarray] = None):
     """One decode step of one sequence: q [Hq][d], new_k/new_v [Hkv][d].
 
-    Returns (o [Hq][d], lse [Hq], dst [Hkv]); the cache is updated in place.
+    Returns (o [Hq][d], lse [Hq], dst [Hkv]); the cache is updated in place.  A caller that
+    has already decided the slots (a GPU run being followed step by step) passes dst.
     """
     hq, d = q.shape
     hkv = c.k.shape[0]
     G = hq // hkv
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    dst = np.array([select_slot(c.score[g], c.pos[g], c.n, c.cap, new_pos, alpha) for g in range(hkv)])
+    if dst is None:
+        dst = np.array([select_slot(c.score[g], c.pos[g], c.n, c.cap, new_pos, alpha) for g in range(hkv)])
     for g in range(hkv):
         c.k[g, dst[g]] = new_k[g]
         c.v[g, dst[g]] = new_v[g]

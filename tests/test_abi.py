@@ -139,3 +139,27 @@ def test_allocator_matches_oracle_on_random_ops(seed):
         assert nat.num_free() == len(ref.free)
     for b in range(N):
         assert nat.refcount(b) == ref.ref[b]
+
+
+def test_eviction_calls_validate_on_the_host():
+    L = kvs.lib
+    fake = 0x1000   # never dereferenced: the checks fail first
+    # alpha must leave a replaceable slot, and cap must fit the slot rows
+    assert L.kvs_decode_select_slot(fake, fake, 64, fake, 1, 2, 64, fake, 64, fake, None) == -1
+    assert b"alpha" in L.kvs_last_error()
+    assert L.kvs_decode_select_slot(fake, fake, 32, fake, 1, 2, 64, fake, 16, fake, None) == -1
+    assert L.kvs_decode_select_slot(fake, fake, 64, fake, 0, 2, 64, fake, 16, fake, None) == 0    # empty batch
+    assert L.kvs_slot_init(fake, fake, None, fake, 1, 10, 2, 64, fake, fake, None) == -1           # no offsets
+    assert L.kvs_slot_init(fake, None, None, fake, 0, 0, 2, 64, fake, fake, None) == 0
+    ws = L.kvs_paged_decode_scored_workspace_size(1, 32, 8, 128, 400)
+    assert ws >= 32 * 400 * 4 > 0                      # the logits of one step are always kept
+    args = dict(q=fake, kp=fake, vp=fake, nb=64, tbl=fake, mb=25, ctx=fake, B=1, mc=400, hq=32, hkv=8, d=128,
+                sc=0.1, nk=fake, nv=fake, dst=fake, ss=fake, stride=400, o=fake, lse=None, ws=fake, wsb=ws, st=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.kvs_paged_decode_scored(*a.values())
+    assert call(ss=None) == -1                          # slot scores are required
+    assert call(nk=None, nv=None) == -1                 # dst_slots without a new token
+    assert call(stride=399) == -1                       # slot rows shorter than the context
+    assert call(wsb=ws - 1) == -1 and b"workspace" in L.kvs_last_error()

@@ -1,0 +1,174 @@
+"""GPU parity of decode-time scoring and eviction (readings R20, R21) through the C ABI.
+
+After prefill + compaction of a compressed layer the cache is full (k_eff = k_l), so every
+decode step evicts.  The fp64 oracle follows the GPU step by step: each step the GPU's
+chosen slots must be exactly what the oracle's rule picks on the GPU's own fp32 scores
+(same values, same decision), the oracle then takes those slots, and outputs, LSE and the
+accumulated scores are compared within the usual tolerances.  The pools' contents are
+checked bit-exactly against the oracle's cache at the end.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from tests._parity import bf16_to_f64, bf16_bits, i32, assert_rows_close, assert_lse_close, gather_pools
+
+pytestmark = pytest.mark.gpu
+
+kvs = pytest.importorskip("kv_cache_sparsification_amd")
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+
+
+def _run(w, steps, check_every):
+    n, alpha, cap = w.fixed_len, w.alpha, w.budgets[0]
+    layer = 3 if len(w.budgets) > 3 else 0
+    _say(f"eviction: n={n} hq={w.hq} hkv={w.hkv} d={w.d} alpha={alpha} cap={cap} steps={steps}")
+    qb, kbits, vb, cu = wl.prefill_batch(w, layer, [n])
+    up = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v = up(qb), up(kbits), up(vb)
+    cu_d = i32(cu)
+    nblk = -(-cap // 16)
+    alloc = kvs.BlockAllocator(nblk + 3, list(np.random.default_rng(9).permutation(nblk + 3)))
+    k_pool, v_pool = kvs.new_pools(nblk + 3, w.hkv, w.d)
+    k_pool.view(torch.int16).fill_(0x7FC0)
+    v_pool.view(torch.int16).fill_(0x7FC0)
+    res = kvs.prefill_compress_layer(q, k, v, cu_d, [n], alpha, cap, alloc, k_pool, v_pool, nblk)
+    stride = nblk * 16
+    sl_sc, sl_pos = kvs.kvs_slot_init(res["scores"], cu_d, res["keep_idx"], res["keep_offsets"], stride)
+    torch.cuda.synchronize()
+    # oracle cache from the GPU's kept set and fp32 scores
+    keep = res["keep_idx"].cpu().numpy().reshape(w.hkv, cap)
+    S = res["scores"].cpu().numpy().astype(np.float64)
+    kf, vf = bf16_to_f64(k), bf16_to_f64(v)
+    c = oracle.init_cache(kf, vf, S, keep, cap)
+    np.testing.assert_array_equal(sl_pos.cpu().numpy()[0, :, :cap], keep)
+    np.testing.assert_array_equal(sl_sc.cpu().numpy()[0, :, :cap].astype(np.float64), S[np.arange(w.hkv)[:, None], keep])
+    tbl = res["tables_dev"]
+    n_filled = i32(np.array([cap]))
+    ctx = i32(np.array([cap]))
+    ws = torch.empty(kvs.kvs_paged_decode_scored_workspace_size(1, w.hq, w.hkv, w.d, cap), dtype=torch.uint8,
+                     device="cuda")
+    for step in range(steps):
+        new_pos = n + step
+        dq, dk, dv = wl.device_decode_step(w, layer, step, [0])
+        sc_before = sl_sc.cpu().numpy()[0].astype(np.float64)
+        pos_before = sl_pos.cpu().numpy()[0]
+        dst = kvs.kvs_decode_select_slot(sl_sc, sl_pos, n_filled, i32(np.array([new_pos])), cap, alpha)
+        lse = torch.empty(1, w.hq, device="cuda")
+        o = kvs.kvs_paged_decode_scored(dq, k_pool, v_pool, tbl, ctx, cap, sl_sc, new_k=dk, new_v=dv, dst_slots=dst,
+                                        lse=lse, workspace=ws)
+        torch.cuda.synchronize()
+        dst_h = dst.cpu().numpy()[0]
+        for g in range(w.hkv):   # same decision on the same (fp32) scores
+            assert dst_h[g] == oracle.select_slot(sc_before[g], pos_before[g], cap, cap, new_pos, alpha), \
+                f"step {step} head {g}"
+        o_ref, lse_ref, _ = oracle.decode_step(c, bf16_to_f64(dq)[0], bf16_to_f64(dk)[0], bf16_to_f64(dv)[0],
+                                               new_pos, alpha, dst=dst_h)
+        if step % check_every == 0 or step == steps - 1:
+            assert_rows_close(bf16_to_f64(o)[0], o_ref, what=f"eviction o step {step}")
+            assert_lse_close(lse.cpu().numpy()[0], lse_ref, what=f"eviction lse step {step}")
+            sc_gpu = sl_sc.cpu().numpy()[0, :, :cap].astype(np.float64)
+            np.testing.assert_allclose(sc_gpu, c.score, rtol=1e-4, atol=1e-6, err_msg=f"scores step {step}")
+            np.testing.assert_array_equal(sl_pos.cpu().numpy()[0, :, :cap], c.pos)
+    # pool contents = the oracle's slots, bit for bit
+    gk, gv = gather_pools(k_pool, v_pool, res["tables"][0], cap)
+    for g in range(w.hkv):
+        np.testing.assert_array_equal(gk[:, g].view(np.uint16), bf16_bits_from_f64(c.k[g]), err_msg=f"K head {g}")
+        np.testing.assert_array_equal(gv[:, g].view(np.uint16), bf16_bits_from_f64(c.v[g]), err_msg=f"V head {g}")
+    return c
+
+
+def bf16_bits_from_f64(x):
+    """Exact bf16 values (as the oracle holds them) back to their bit patterns."""
+    f = np.asarray(x, dtype=np.float32)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_eviction_tiny_many_steps():
+    c = _run(wl.WORKLOADS[1], steps=120, check_every=7)
+    assert c.n == c.cap
+
+
+def test_eviction_llama8b_layer():
+    c = _run(wl.WORKLOADS[2], steps=40, check_every=13)
+    assert c.n == c.cap
+
+
+def test_eviction_batch_appends_then_evicts():
+    """Three prompts (30, 48, 100 tokens), budget 48, alpha 8: the short one appends (taking a
+    block when a slot opens one) until it is full, the others evict from the first step."""
+    from workloads import Workload
+    w = Workload(cid=91, name="eviction batch", hq=8, hkv=2, d=128, alpha=8, n_layers=1, budgets=[48],
+                 decode_steps=40, sink_positions=(0,), num_seqs=3)
+    lengths = [30, 48, 100]
+    cap, alpha, steps = 48, 8, 40
+    B = len(lengths)
+    q, k, v, cu = wl.device_batch(w, 0, lengths, list(range(B)))
+    cu_d = i32(cu)
+    nb_seq = -(-cap // 16)
+    alloc = kvs.BlockAllocator(B * nb_seq + 4, list(np.random.default_rng(5).permutation(B * nb_seq + 4)))
+    k_pool, v_pool = kvs.new_pools(B * nb_seq + 4, w.hkv, w.d)
+    k_pool.view(torch.int16).fill_(0x7FC0)
+    v_pool.view(torch.int16).fill_(0x7FC0)
+    res = kvs.prefill_compress_layer(q, k, v, cu_d, lengths, alpha, cap, alloc, k_pool, v_pool, nb_seq)
+    stride = nb_seq * 16
+    sl_sc, sl_pos = kvs.kvs_slot_init(res["scores"], cu_d, res["keep_idx"], res["keep_offsets"], stride)
+    torch.cuda.synchronize()
+    kept = res["kept"]
+    flat = res["keep_idx"].cpu().numpy()
+    off = np.concatenate([[0], np.cumsum(kept)])
+    S = res["scores"].cpu().numpy().astype(np.float64)
+    caches = []
+    for s, n in enumerate(lengths):
+        keep = flat[w.hkv * off[s]: w.hkv * off[s + 1]].reshape(w.hkv, kept[s])
+        a = cu[s]
+        caches.append(oracle.init_cache(bf16_to_f64(k[a:a + n]), bf16_to_f64(v[a:a + n]), S[:, a:a + n], keep, cap))
+    tables = [list(t) for t in res["tables"]]
+    tbl = np.full((B, nb_seq), -1, np.int32)
+    n_fill = list(kept)
+    ws = torch.empty(kvs.kvs_paged_decode_scored_workspace_size(B, w.hq, w.hkv, w.d, cap), dtype=torch.uint8,
+                     device="cuda")
+    for step in range(steps):
+        for s in range(B):                     # a block for an appended token that opens one
+            if n_fill[s] < cap and n_fill[s] % 16 == 0 and n_fill[s] // 16 >= len(tables[s]):
+                tables[s].append(alloc.alloc())
+            tbl[s, :len(tables[s])] = tables[s]
+        new_pos = [n + step for n in lengths]
+        sc_before = sl_sc.cpu().numpy().astype(np.float64)
+        pos_before = sl_pos.cpu().numpy()
+        dst = kvs.kvs_decode_select_slot(sl_sc, sl_pos, i32(n_fill), i32(new_pos), cap, alpha)
+        n_fill = [min(x + 1, cap) for x in n_fill]
+        dq, dk, dv = wl.device_decode_step(w, 0, step, list(range(B)))
+        lse = torch.empty(B, w.hq, device="cuda")
+        o = kvs.kvs_paged_decode_scored(dq, k_pool, v_pool, i32(tbl), i32(n_fill), cap, sl_sc, new_k=dk, new_v=dv,
+                                        dst_slots=dst, lse=lse, workspace=ws)
+        torch.cuda.synchronize()
+        dst_h = dst.cpu().numpy()
+        og, lg = bf16_to_f64(o), lse.cpu().numpy()
+        dqh, dkh, dvh = bf16_to_f64(dq), bf16_to_f64(dk), bf16_to_f64(dv)
+        for s in range(B):
+            c = caches[s]
+            for g in range(w.hkv):
+                assert dst_h[s, g] == oracle.select_slot(sc_before[s, g], pos_before[s, g], c.n, cap, new_pos[s],
+                                                         alpha), f"step {step} seq {s} head {g}"
+            o_ref, l_ref, _ = oracle.decode_step(c, dqh[s], dkh[s], dvh[s], new_pos[s], alpha, dst=dst_h[s])
+            assert_rows_close(og[s], o_ref, what=f"batch eviction o step {step} seq {s}")
+            assert_lse_close(lg[s], l_ref, what=f"batch eviction lse step {step} seq {s}")
+            np.testing.assert_allclose(sl_sc.cpu().numpy()[s, :, :c.n].astype(np.float64), c.score[:, :c.n],
+                                       rtol=1e-4, atol=1e-6, err_msg=f"scores step {step} seq {s}")
+    assert all(c.n == cap for c in caches)

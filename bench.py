@@ -270,6 +270,9 @@ def main():
     }
 
     line["decode_at_scale"] = decode_at_scale(kvs, torch, wl, 100)
+    # the prefill-side pass of the last step left the compressed cache in the pools
+    kvs.kvs_compact_paged(k, v, cu_d, keep, keep_off, k_eff, k_pool, v_pool, tbl)
+    line["decode_evict"] = decode_evict(kvs, torch, wl, w, k_pool, v_pool, tbl, S, cu_d, keep, keep_off, 200)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, qb, kbits, vb, dec, args.cpu_budget_s)
     print(json.dumps(line), flush=True)
@@ -332,6 +335,54 @@ def decode_at_scale(kvs, torch, wl, steps):
             "us_per_step": round(us, 3), "algorithmic_bytes_per_step": int(nbytes),
             "achieved_GBs": round(gbs, 1), "peak_GBs": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4),
             "tok_s": round(B / (us * 1e-6), 1)}
+
+
+def decode_evict(kvs, torch, wl, w, k_pool, v_pool, tbl, S, cu_d, keep, keep_off, steps):
+    """Decode with scoring and eviction on the bench layer: the compressed cache is full
+    (k_eff = k_l), so every step picks each head's lowest-score replaceable slot and runs the
+    scored decode (attention, then the probabilities added to the slot scores); `steps` steps
+    replayed as one HIP graph."""
+    dev = torch.device("cuda:0")
+    n, hq, hkv, d, alpha, cap = w.fixed_len, w.hq, w.hkv, w.d, w.alpha, w.budgets[0]
+    stride = tbl.shape[1] * 16
+    sl_sc, sl_pos = kvs.kvs_slot_init(S, cu_d, keep, keep_off, stride)
+    n_fill = torch.tensor([cap], dtype=torch.int32, device=dev)
+    pos = torch.tensor([[n + s] for s in range(steps)], dtype=torch.int32, device=dev)
+    qs, nks, nvs = zip(*[wl.device_decode_step(w, 0, 1000 + s, [0], device=dev) for s in range(steps)])
+    dst = torch.empty(1, hkv, dtype=torch.int32, device=dev)
+    ws = torch.empty(kvs.kvs_paged_decode_scored_workspace_size(1, hq, hkv, d, cap), dtype=torch.uint8, device=dev)
+    od = torch.empty(steps, 1, hq, d, dtype=torch.bfloat16, device=dev)
+
+    def run():
+        for s in range(steps):
+            kvs.kvs_decode_select_slot(sl_sc, sl_pos, n_fill, pos[s], cap, alpha, dst_slot=dst)
+            kvs.kvs_paged_decode_scored(qs[s], k_pool, v_pool, tbl, n_fill, cap, sl_sc, new_k=nks[s], new_v=nvs[s],
+                                        dst_slots=dst, o=od[s], workspace=ws)
+
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        run()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 3
+    e0.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * steps)
+    return {"workload": f"bench layer, cache full at k={cap} (alpha={alpha}): every step evicts per KV head, "
+                        f"{steps} steps (HIP graph)",
+            "us_per_step": round(us, 3), "tok_s": round(1.0 / (us * 1e-6), 1),
+            "launches_per_step": 3}
 
 
 def cpu_baseline(w, qb, kbits, vb, dec, budget_s):

@@ -29,8 +29,11 @@ Modules and the step each one follows:
   eviction      decode-time scores and the replacement of the lowest-score
                 token in a full compressed layer ([KVS] Key techniques 1, step
                 preparation; Key techniques 2, last paragraph)
+  fp8           the 8-bit (E4M3) cache: encoding, per-row scales, the
+                quantized compaction and decode append ([PAG] "Related
+                techniques")
 
-Readings taken where the pages are silent or garbled are named R1..R21 in the
+Readings taken where the pages are silent or garbled are named R1..R24 in the
 docstrings; each one is listed with its justification in the design notes.
 Every function is pinned by the CPU tests (``pytest -m "not gpu"``); none is
 "parity unpinned".
@@ -41,6 +44,7 @@ from .topk import select_keep, keep_count
 from .paged import BlockAllocator, blocks_for, write_rows, gather_rows, compact_into_pool
 from .decode import decode_attention
 from .eviction import SlotCache, init_cache, select_slot, decode_step
+from . import fp8
 
 __all__ = [
     "causal_attention", "attention_probs",
@@ -49,4 +53,5 @@ __all__ = [
     "BlockAllocator", "blocks_for", "write_rows", "gather_rows", "compact_into_pool",
     "decode_attention",
     "SlotCache", "init_cache", "select_slot", "decode_step",
+    "fp8",
 ]

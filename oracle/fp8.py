@@ -12,12 +12,15 @@ Readings:
       the subnormals m * 2^-9).  Conversion rounds the magnitude to nearest, ties
       to the even code, saturates at 448 and keeps the sign bit (a negative value
       that rounds to zero becomes -0, code 0x80).
-  R23 one float32 scale per cached row, i.e. per (token, KV head): scale =
-      max_c |x_c| / 448 and code_c = E4M3(x_c / scale), both quotients rounded
-      once in float32 (the kernel's precision, so both sides take the same
-      rounding decision); a row of zeros has scale 0 and codes 0.  The stored
-      value is code * scale.  A per-row scale lets a decode step append a token
-      to a partly filled block without touching the rows already there.
+  R23 one float32 scale per cached row, i.e. per (token, KV head): with amax =
+      max_c |x_c|, scale = amax / 448 is stored and code_c = E4M3(x_c * r) with
+      r = 448 / amax; each of the two quotients and the product is rounded once
+      in float32 (the kernel's precision, so both sides take the same rounding
+      decision).  One division per row, one product per value.  A row whose
+      amax is below 2^-112 (zero included; there 448 / amax would leave the
+      float32 range) is stored as scale 0 and codes 0.  The stored value is
+      code * scale.  A per-row scale lets a decode step append a token to a
+      partly filled block without touching the rows already there.
   R24 the cache (compaction output and decode appends) is the only thing kept at
       8 bits; the prefill and the decode query stay at 16 bits, and the decode
       attention uses the values code * scale.
@@ -34,6 +37,7 @@ import numpy as np
 from .paged import BLOCK
 
 E4M3_MAX = 448.0
+TINY_ROW = 2.0 ** -112     # rows below this largest magnitude are stored as zeros (R23)
 
 
 def e4m3_decode(codes) -> np.ndarray:
@@ -70,17 +74,19 @@ def e4m3_encode(x) -> np.ndarray:
 def quantize_rows(x) -> Tuple[np.ndarray, np.ndarray]:
     """x [..., d] (values a float32 holds exactly) -> (codes uint8 [..., d], scale float32 [...]).
 
-    R23: scale = amax / 448 and code = E4M3(x / scale), each quotient rounded to float32.
+    R23: scale = amax / 448, code = E4M3(x * (448 / amax)), every step rounded to float32.
     """
     x32 = np.asarray(x, dtype=np.float32)
     if not np.array_equal(x32.astype(np.float64), np.asarray(x, dtype=np.float64)):
         raise ValueError("inputs must be exact in float32 (the cache is written from 16-bit values)")
     amax = np.max(np.abs(x32), axis=-1)
-    scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
-    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
-    q = (x32 / safe[..., None]).astype(np.float32)
+    live = amax >= np.float32(TINY_ROW)
+    safe = np.where(live, amax, np.float32(1.0)).astype(np.float32)
+    scale = np.where(live, safe / np.float32(E4M3_MAX), np.float32(0.0)).astype(np.float32)
+    r = (np.float32(E4M3_MAX) / safe).astype(np.float32)
+    q = (x32 * r[..., None]).astype(np.float32)
     codes = e4m3_encode(q)
-    codes[scale == 0] = 0
+    codes[~live] = 0
     return codes, scale
 
 

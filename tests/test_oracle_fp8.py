@@ -80,19 +80,26 @@ def test_quantize_rows():
     rng = np.random.default_rng(11)
     x = torch.from_numpy(rng.standard_normal((64, 8, 128)) * 3).to(torch.bfloat16).float().numpy()
     x[5, 2] = 0.0                                   # a zero row
+    x[6, 1] = np.float32(2.0 ** -113) * np.sign(x[6, 1])   # below the smallest live row
+    x[7, 3] *= np.float32(2.0 ** -108)              # small but live
     codes, scale = fp8.quantize_rows(x)
     assert codes.shape == x.shape and scale.shape == x.shape[:2] and scale.dtype == np.float32
-    assert scale[5, 2] == 0 and not codes[5, 2].any()
+    for z in ((5, 2), (6, 1)):
+        assert scale[z] == 0 and not codes[z].any()
     amax = np.abs(x).max(-1)
-    nz = amax > 0
-    assert np.array_equal(scale[nz], (amax[nz] / np.float32(448)).astype(np.float32))
-    # the largest element of each row lands on +-448 (scale rounding moves it by far less than an ulp)
+    live = amax >= 2.0 ** -112
+    assert live.sum() == 64 * 8 - 2
+    assert np.array_equal(scale[live], (amax[live] / np.float32(448)).astype(np.float32))
+    # the largest element of each row lands on +-448 (rounding moves it by far less than an ulp)
     top = np.take_along_axis(codes, np.abs(x).argmax(-1)[..., None], -1)[..., 0]
-    assert np.all((top[nz] & 0x7F) == 0x7E)
+    assert np.all((top[live] & 0x7F) == 0x7E)
     y = fp8.dequantize_rows(codes, scale)
     tiny = np.abs(x) < scale[..., None].astype(np.float64) * 2.0 ** -6
     bound = np.where(tiny, scale[..., None] * 2.0 ** -10, np.abs(x) * 2.0 ** -4) * (1 + 1e-6)
-    assert np.all(np.abs(y - x) <= bound)
+    assert np.all(np.abs(y - x)[live] <= bound[live])
+    # the code is the E4M3 rounding of the float32 product x * fp32(448 / amax)
+    r = (np.float32(448) / amax[live]).astype(np.float32)
+    assert np.array_equal(codes[live], fp8.e4m3_encode((x[live] * r[:, None]).astype(np.float32)))
 
 
 def test_exact_values_survive_quantization():

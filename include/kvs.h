@@ -11,8 +11,9 @@
  *   kvs_topk_select       the kept token indices per KV head
  *   kvs_compact_paged     copy of the kept K/V rows into 16-token blocks through block tables
  *   kvs_paged_decode      attention of one new token per sequence over the paged cache
- * plus a host block allocator (free list, reference counts, copy-on-write) and the
- * device block copy that copy-on-write needs.
+ * with 8-bit (E4M3) variants of the cache calls (*_fp8), decode-time scoring and eviction,
+ * a host block allocator (free list, reference counts, copy-on-write) and the device
+ * block copy that copy-on-write needs.
  *
  * Conventions shared by every call
  *   - Return value: KVS_OK (0) or a negative KVS_E_* code; kvs_last_error() gives a
@@ -233,6 +234,46 @@ int kvs_paged_decode_scored(const void* q, void* k_pool, void* v_pool, int num_b
  */
 int kvs_copy_blocks(void* k_pool, void* v_pool, int num_blocks, int hkv, int d,
                     const int32_t* src_dst_pairs, int n_pairs, void* stream);
+
+/*
+ * 8-bit cache.  [PAG] "Related techniques": an FP8 cache keeps the cached keys and values at
+ * 8 bits, about half the memory of a 16-bit cache.  Format: OCP E4M3 (largest finite value
+ * 448), one fp32 scale per cached row (token, KV head):
+ *   scale = amax / 448,  code_c = E4M3(x_c * (448 / amax))  (round to nearest even,
+ *   saturating), with amax = max_c |x_c| and each quotient and product rounded once in fp32;
+ *   a row with amax < 2^-112 is stored as scale 0 and codes 0.  The value of a slot is
+ *   code * scale.
+ * Pools: k_pool [num_blocks][hkv][16][d] and v_pool [num_blocks][hkv][d][16] bytes (the same
+ * element order as the 16-bit pools), k_scale and v_scale [num_blocks][hkv][16] fp32.
+ */
+
+/*
+ * kvs_compact_paged_fp8 - kvs_compact_paged into an 8-bit cache: each written row is
+ * quantized as above and its scale stored at the same (block, head, slot).  Arguments,
+ * layout of the sources and tables, and errors as kvs_compact_paged.
+ */
+int kvs_compact_paged_fp8(const void* k_src, const void* v_src, const int32_t* cu_seqlens, int num_seqs, int hkv,
+                          int d, const int32_t* keep_idx, const int32_t* keep_offsets, int max_keep, void* k_pool,
+                          void* v_pool, float* k_scale, float* v_scale, int num_blocks, const int32_t* block_tables,
+                          int max_blocks, const int32_t* dst_slot_offset, void* stream);
+
+/*
+ * kvs_paged_decode_fp8 - kvs_paged_decode over an 8-bit cache: K_t and V_t are the slots'
+ * values code * scale, and new_k/new_v (bf16) are quantized into slot L-1 first.  The
+ * query and the output stay bf16.  Workspace: kvs_paged_decode_workspace_size(...) bytes,
+ * as for kvs_paged_decode.  Errors as kvs_paged_decode; KVS_E_INVAL also for a NULL scale
+ * array.
+ */
+int kvs_paged_decode_fp8(const void* q, void* k_pool, void* v_pool, float* k_scale, float* v_scale, int num_blocks,
+                         const int32_t* block_tables, int max_blocks, const int32_t* ctx_lens, int batch, int max_ctx,
+                         int hq, int hkv, int d, float scale, const void* new_k, const void* new_v, void* o,
+                         float* lse_opt, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kvs_copy_blocks_fp8 - kvs_copy_blocks for an 8-bit cache: code blocks and scale rows.
+ */
+int kvs_copy_blocks_fp8(void* k_pool, void* v_pool, float* k_scale, float* v_scale, int num_blocks, int hkv, int d,
+                        const int32_t* src_dst_pairs, int n_pairs, void* stream);
 
 /*
  * Host block allocator.  [PAG] "How paging works": a request gets a new block only when

@@ -10,7 +10,8 @@ from ._lib import lib, KvsError, BLOCK_SIZE, LIB_PATH
 from .ops import (kvs_prefill_attn_lse, kvs_window_score, kvs_topk_select, kvs_compact_paged,
                   kvs_paged_decode, kvs_paged_decode_workspace_size, kvs_copy_blocks, new_pools,
                   kvs_slot_init, kvs_decode_select_slot, kvs_paged_decode_scored,
-                  kvs_paged_decode_scored_workspace_size)
+                  kvs_paged_decode_scored_workspace_size, new_pools_fp8, kvs_compact_paged_fp8,
+                  kvs_paged_decode_fp8, kvs_copy_blocks_fp8)
 from .allocator import BlockAllocator
 from .pipeline import layer_policy, keep_counts, prefill_compress_layer
 
@@ -19,5 +20,6 @@ __all__ = [
     "kvs_prefill_attn_lse", "kvs_window_score", "kvs_topk_select", "kvs_compact_paged",
     "kvs_paged_decode", "kvs_paged_decode_workspace_size", "kvs_copy_blocks", "new_pools",
     "kvs_slot_init", "kvs_decode_select_slot", "kvs_paged_decode_scored", "kvs_paged_decode_scored_workspace_size",
+    "new_pools_fp8", "kvs_compact_paged_fp8", "kvs_paged_decode_fp8", "kvs_copy_blocks_fp8",
     "BlockAllocator", "layer_policy", "keep_counts", "prefill_compress_layer",
 ]

@@ -35,6 +35,11 @@ SIGNATURES = {
     "kvs_paged_decode_scored_workspace_size": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "kvs_paged_decode_scored": (_c_int, [_vp, _vp, _vp, _c_int, _vp, _c_int, _vp, _c_int, _c_int, _c_int, _c_int,
                                          _c_int, _c_float, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _c_size, _vp]),
+    "kvs_compact_paged_fp8": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _c_int, _vp, _vp, _vp, _vp,
+                                       _c_int, _vp, _c_int, _vp, _vp]),
+    "kvs_paged_decode_fp8": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _c_int, _vp, _c_int, _c_int, _c_int,
+                                      _c_int, _c_int, _c_float, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "kvs_copy_blocks_fp8": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _c_int, _vp]),
     "kvs_alloc_create": (_c_int, [_c_int, _i32p, _c_int, ctypes.POINTER(_vp)]),
     "kvs_alloc_destroy": (None, [_vp]),
     "kvs_alloc_block": (_c_int, [_vp, _i32p]),

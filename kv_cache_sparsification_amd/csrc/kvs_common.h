@@ -77,6 +77,63 @@ __device__ __forceinline__ u32x2 ds_read_tr16_b64(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, r);
 }
 
+// ---------------------------------------------------------------- 8-bit cache (OCP E4M3)
+// gfx950's fp8 conversions use the OCP E4M3 encoding (bias 7, 3 mantissa bits, largest finite
+// magnitude 448, no infinities) and round to nearest even; they do not saturate, so values
+// are clamped to +-448 first (fmed3 keeps the sign of zero).
+constexpr float kE4M3Max = 448.f;
+constexpr float kTinyRow = 0x1p-112f;   // rows whose largest magnitude is below this are stored as zeros
+
+// Per-row quantization parameters: the stored scale amax/448 and the multiplier 448/amax
+// (each one float32 division); both zero for a row stored as zeros.
+__device__ __forceinline__ void e4m3_row_params(float amax, float& scale, float& r) {
+  const bool live = amax >= kTinyRow;
+  scale = live ? amax / kE4M3Max : 0.f;
+  r = live ? kE4M3Max / amax : 0.f;
+}
+
+// Four values times r to four codes (byte i = value i).  r == 0 (a zero row) gives code 0.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d, float r) {
+  if (r == 0.f) return 0u;
+  a = __builtin_amdgcn_fmed3f(a * r, kE4M3Max, -kE4M3Max);
+  b = __builtin_amdgcn_fmed3f(b * r, kE4M3Max, -kE4M3Max);
+  c = __builtin_amdgcn_fmed3f(c * r, kE4M3Max, -kE4M3Max);
+  d = __builtin_amdgcn_fmed3f(d * r, kE4M3Max, -kE4M3Max);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+// Four codes to four bf16 (exact: every E4M3 value is a bf16 value): low word = bytes 0, 1.
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16(uint32_t c) {
+  const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)c, false);
+  const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)c, true);
+  u32x2 r;
+  r[0] = __builtin_amdgcn_perm(__float_as_uint(lo[1]), __float_as_uint(lo[0]), 0x07060302u);
+  r[1] = __builtin_amdgcn_perm(__float_as_uint(hi[1]), __float_as_uint(hi[0]), 0x07060302u);
+  return r;
+}
+
+// Eight bf16 (one 16-byte chunk) times r to eight codes.
+__device__ __forceinline__ u32x2 e4m3x8_from_bf16(u32x4 v, float r) {
+  u32x2 out;
+  out[0] = e4m3x4(bf16_bits_to_f32(v[0] & 0xffffu), bf16_bits_to_f32(v[0] >> 16), bf16_bits_to_f32(v[1] & 0xffffu),
+                  bf16_bits_to_f32(v[1] >> 16), r);
+  out[1] = e4m3x4(bf16_bits_to_f32(v[2] & 0xffffu), bf16_bits_to_f32(v[2] >> 16), bf16_bits_to_f32(v[3] & 0xffffu),
+                  bf16_bits_to_f32(v[3] >> 16), r);
+  return out;
+}
+
+__device__ __forceinline__ float absmax_bf16x8(u32x4 v) {
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m = fmaxf(m, fabsf(bf16_bits_to_f32(v[i] & 0xffffu)));
+    m = fmaxf(m, fabsf(bf16_bits_to_f32(v[i] >> 16)));
+  }
+  return m;
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

@@ -90,11 +90,25 @@ struct DecodeExtra {
   float* logits;              // [batch][hq][logit_stride], or NULL
   int logit_stride;
   int force_partials;
+  float* k_scale;             // 8-bit cache: per-row scales [num_blocks][hkv][16]
+  float* v_scale;
 };
 
-template <int D, int W, int kNB>
+// 8-bit cache operands of one block, as loaded: K codes (8 per lane and k-step), V^T codes (4
+// slots of one channel per lane and d tile) and the scales of the lane's 4 slots.
+template <int KS, int MT>
+struct F8Block {
+  u32x2 k[KS];
+  uint32_t v[MT];
+  f32x4 sk, sv;
+};
+
+// F8: the cache holds E4M3 codes with a fp32 scale per (slot, KV head) row; codes are widened
+// to bf16 (exact) for the same MFMAs, the K scale multiplies the slot's score and the V scale
+// its probability (before the bf16 rounding of P), and the appended token is quantized here.
+template <int D, int W, int kNB, bool F8>
 __global__ __launch_bounds__(W * kWave) void decode_kernel(
-    const uint16_t* __restrict__ q, uint16_t* __restrict__ k_pool, uint16_t* __restrict__ v_pool, int num_blocks,
+    const uint16_t* __restrict__ q, void* __restrict__ k_pool_v, void* __restrict__ v_pool_v, int num_blocks,
     const int32_t* __restrict__ tables, int max_blocks, const int32_t* __restrict__ ctx_lens, int hq, int hkv,
     float c_log2, const uint16_t* __restrict__ new_k, const uint16_t* __restrict__ new_v, uint16_t* __restrict__ o,
     float* __restrict__ lse_out, float* __restrict__ ws, int splits, int bps, DecodeExtra ex) {
@@ -102,6 +116,10 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
   constexpr int MT = D / 16;     // d tiles of the output product
   constexpr int NT = W * kWave;
   extern __shared__ float smem[];
+  uint16_t* k_pool = static_cast<uint16_t*>(k_pool_v);
+  uint16_t* v_pool = static_cast<uint16_t*>(v_pool_v);
+  uint8_t* k_pool8 = static_cast<uint8_t*>(k_pool_v);
+  uint8_t* v_pool8 = static_cast<uint8_t*>(v_pool_v);
 
   const int sp = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid % kWave;
@@ -157,26 +175,40 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
     }
     bf16x8 kf[kNB][KS];
     short4_t vf[kNB][MT];
+    F8Block<KS, MT> f8[kNB];
 #pragma unroll
     for (int j = 0; j < kNB; ++j) {
       const int bi = bi0 + W * j;
       const int blk = cur[j];
       if (bi >= blk_end || blk < 0 || blk >= num_blocks) continue;
-      const uint16_t* kb = k_pool + ((size_t)blk * hkv + g) * kBlock * D;
-      const uint16_t* vb = v_pool + ((size_t)blk * hkv + g) * D * kBlock;
+      const size_t bh = (size_t)blk * hkv + g;
       const bool app_blk = append && bi == last_blk;
-      // K rows (A operand): token = col, d = st*32 + grp*8 .. +8; the new token comes from new_k.
-      const uint16_t* ksrc = (app_blk && col == last_slot) ? nk : kb + col * D;
+      if constexpr (F8) {
+        const uint8_t* kb = k_pool8 + bh * kBlock * D;
+        const uint8_t* vb = v_pool8 + bh * D * kBlock;
 #pragma unroll
-      for (int st = 0; st < KS; ++st)
-        kf[j][st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ksrc + st * 32 + grp * 8));
-      // V^T (A operand of the output product): d = mt*16 + col, tokens grp*4 .. +4.
+        for (int st = 0; st < KS; ++st) f8[j].k[st] = *reinterpret_cast<const u32x2*>(kb + col * D + st * 32 + grp * 8);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        vf[j][mt] = *reinterpret_cast<const short4_t*>(vb + (size_t)(mt * 16 + col) * kBlock + grp * 4);
-      if (app_blk && grp == last_slot / 4) {
+        for (int mt = 0; mt < MT; ++mt)
+          f8[j].v[mt] = *reinterpret_cast<const uint32_t*>(vb + (size_t)(mt * 16 + col) * kBlock + grp * 4);
+        f8[j].sk = *reinterpret_cast<const f32x4*>(ex.k_scale + bh * kBlock + grp * 4);
+        f8[j].sv = *reinterpret_cast<const f32x4*>(ex.v_scale + bh * kBlock + grp * 4);
+      } else {
+        const uint16_t* kb = k_pool + bh * kBlock * D;
+        const uint16_t* vb = v_pool + bh * D * kBlock;
+        // K rows (A operand): token = col, d = st*32 + grp*8 .. +8; the new token comes from new_k.
+        const uint16_t* ksrc = (app_blk && col == last_slot) ? nk : kb + col * D;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) vf[j][mt][last_slot % 4] = (short)nv[mt * 16 + col];
+        for (int st = 0; st < KS; ++st)
+          kf[j][st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ksrc + st * 32 + grp * 8));
+        // V^T (A operand of the output product): d = mt*16 + col, tokens grp*4 .. +4.
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          vf[j][mt] = *reinterpret_cast<const short4_t*>(vb + (size_t)(mt * 16 + col) * kBlock + grp * 4);
+        if (app_blk && grp == last_slot / 4) {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) vf[j][mt][last_slot % 4] = (short)nv[mt * 16 + col];
+        }
       }
     }
 #pragma unroll
@@ -184,6 +216,71 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
       const int bi = bi0 + W * j;
       const int blk = cur[j];
       if (bi >= blk_end || blk < 0 || blk >= num_blocks) continue;
+      const size_t bh = (size_t)blk * hkv + g;
+      const bool app_blk = append && bi == last_blk;
+      if constexpr (F8) {
+        if (app_blk) {
+          // Quantize the new token's rows (amax over the whole wavefront, one scale per row) and
+          // put its codes and scales where the slot's loaded ones were; they are stored below.
+          float ak = 0.f, av = 0.f;
+          if (2 * lane < D) {
+            const uint32_t xk = *reinterpret_cast<const uint32_t*>(nk + 2 * lane);
+            const uint32_t xv = *reinterpret_cast<const uint32_t*>(nv + 2 * lane);
+            ak = fmaxf(fabsf(bf16_bits_to_f32(xk & 0xffffu)), fabsf(bf16_bits_to_f32(xk >> 16)));
+            av = fmaxf(fabsf(bf16_bits_to_f32(xv & 0xffffu)), fabsf(bf16_bits_to_f32(xv >> 16)));
+          }
+#pragma unroll
+          for (int m = 1; m < kWave; m <<= 1) {
+            ak = fmaxf(ak, wave_xor(ak, m));
+            av = fmaxf(av, wave_xor(av, m));
+          }
+          float ksc, kr, vsc, vr;
+          e4m3_row_params(ak, ksc, kr);
+          e4m3_row_params(av, vsc, vr);
+          if (col == last_slot) {
+#pragma unroll
+            for (int st = 0; st < KS; ++st)
+              f8[j].k[st] = e4m3x8_from_bf16(*reinterpret_cast<const u32x4*>(nk + st * 32 + grp * 8), kr);
+          }
+          if (grp == last_slot / 4) {
+            const int sh = 8 * (last_slot % 4);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+              const uint32_t code = e4m3x4(bf16_bits_to_f32(nv[mt * 16 + col]), 0.f, 0.f, 0.f, vr) & 0xffu;
+              f8[j].v[mt] = (f8[j].v[mt] & ~(0xffu << sh)) | (code << sh);
+            }
+            f8[j].sk[last_slot % 4] = ksc;
+            f8[j].sv[last_slot % 4] = vsc;
+          }
+          // keep the appended token in the pool for later steps
+          if (col == last_slot) {
+            uint8_t* kd = k_pool8 + bh * kBlock * D + last_slot * D;
+#pragma unroll
+            for (int st = 0; st < KS; ++st) *reinterpret_cast<u32x2*>(kd + st * 32 + grp * 8) = f8[j].k[st];
+          }
+          if (grp == last_slot / 4) {
+            uint8_t* vd = v_pool8 + bh * D * kBlock;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+              vd[(size_t)(mt * 16 + col) * kBlock + last_slot] = (uint8_t)(f8[j].v[mt] >> (8 * (last_slot % 4)));
+            if (col == 0) {
+              ex.k_scale[bh * kBlock + last_slot] = ksc;
+              ex.v_scale[bh * kBlock + last_slot] = vsc;
+            }
+          }
+        }
+#pragma unroll
+        for (int st = 0; st < KS; ++st) {
+          const u32x2 a = e4m3x4_to_bf16(f8[j].k[st][0]), b2 = e4m3x4_to_bf16(f8[j].k[st][1]);
+          kf[j][st] = __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b2[0], b2[1]});
+        }
+        // slots past the context (the last block's tail) hold stale codes: zero them
+        const int live = L - bi * kBlock - grp * 4;   // slots of the lane's 4 that are in the context
+        const uint32_t vmask = live >= 4 ? 0xffffffffu : (live <= 0 ? 0u : (0xffffffffu >> (8 * (4 - live))));
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          vf[j][mt] = __builtin_bit_cast(short4_t, e4m3x4_to_bf16(f8[j].v[mt] & vmask));
+      }
       f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int st = 0; st < KS; ++st) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[j][st], qf[st], sc, 0, 0, 0);
@@ -193,7 +290,8 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = bi * kBlock + grp * 4 + i;
-        x[i] = t < L ? sc[i] * c_log2 : -INFINITY;
+        const float si = F8 ? sc[i] * f8[j].sk[i] : sc[i];
+        x[i] = t < L ? si * c_log2 : -INFINITY;
         bm = fmaxf(bm, x[i]);
         if (ex.logits && col < G && t < L) ex.logits[((size_t)b * hq + g * G + col) * ex.logit_stride + t] = x[i];
       }
@@ -210,26 +308,30 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
       l_run = l_run * corr + psum;
       m_run = m_new;
       short4_t pb;
-      pb[0] = (short)f32_to_bf16_bits(p[0]);
-      pb[1] = (short)f32_to_bf16_bits(p[1]);
-      pb[2] = (short)f32_to_bf16_bits(p[2]);
-      pb[3] = (short)f32_to_bf16_bits(p[3]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float pi = p[i];
+        if constexpr (F8) pi = x[i] == -INFINITY ? 0.f : p[i] * f8[j].sv[i];   // stale tail scales stay out
+        pb[i] = (short)f32_to_bf16_bits(pi);
+      }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         acc_o[mt] *= corr;
         acc_o[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf[j][mt], pb, acc_o[mt], 0, 0, 0);
       }
-      if (append && bi == last_blk) {   // keep the appended token in the pool for later steps
-        if (col == last_slot) {
-          uint16_t* kd = k_pool + ((size_t)blk * hkv + g) * kBlock * D + last_slot * D;
+      if constexpr (!F8) {
+        if (app_blk) {   // keep the appended token in the pool for later steps
+          if (col == last_slot) {
+            uint16_t* kd = k_pool + bh * kBlock * D + last_slot * D;
 #pragma unroll
-          for (int st = 0; st < KS; ++st)
-            *reinterpret_cast<u32x4*>(kd + st * 32 + grp * 8) = *reinterpret_cast<const u32x4*>(nk + st * 32 + grp * 8);
-        }
-        if (grp == last_slot / 4) {
-          uint16_t* vd = v_pool + ((size_t)blk * hkv + g) * D * kBlock;
+            for (int st = 0; st < KS; ++st)
+              *reinterpret_cast<u32x4*>(kd + st * 32 + grp * 8) = *reinterpret_cast<const u32x4*>(nk + st * 32 + grp * 8);
+          }
+          if (grp == last_slot / 4) {
+            uint16_t* vd = v_pool + bh * D * kBlock;
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) vd[(size_t)(mt * 16 + col) * kBlock + last_slot] = (uint16_t)vf[j][mt][last_slot % 4];
+            for (int mt = 0; mt < MT; ++mt) vd[(size_t)(mt * 16 + col) * kBlock + last_slot] = (uint16_t)vf[j][mt][last_slot % 4];
+          }
         }
       }
     }
@@ -385,73 +487,82 @@ extern "C" size_t kvs_paged_decode_workspace_size(int batch, int hq, int hkv, in
   return (size_t)batch * hq * p.splits * (d + 2) * sizeof(float);
 }
 
-template <int D, int W, int NB>
-static void launch_one(const Plan& p, dim3 grid, size_t lds, hipStream_t st, const uint16_t* q, uint16_t* kp,
-                       uint16_t* vp, int num_blocks, const int32_t* tables, int max_blocks, const int32_t* ctx, int hq,
-                       int hkv, float c, const uint16_t* nk, const uint16_t* nv, uint16_t* o, float* lse, float* ws,
+template <int D, int W, int NB, bool F8>
+static void launch_one(const Plan& p, dim3 grid, size_t lds, hipStream_t st, const uint16_t* q, void* kp, void* vp,
+                       int num_blocks, const int32_t* tables, int max_blocks, const int32_t* ctx, int hq, int hkv,
+                       float c, const uint16_t* nk, const uint16_t* nv, uint16_t* o, float* lse, float* ws,
                        const DecodeExtra& ex) {
-  hipLaunchKernelGGL((decode_kernel<D, W, NB>), grid, dim3(W * kWave), lds, st, q, kp, vp, num_blocks, tables,
+  hipLaunchKernelGGL((decode_kernel<D, W, NB, F8>), grid, dim3(W * kWave), lds, st, q, kp, vp, num_blocks, tables,
                      max_blocks, ctx, hq, hkv, c, nk, nv, o, lse, ws, p.splits, p.bps, ex);
 }
 
-template <int D>
-static void launch_decode(const Plan& p, dim3 grid, size_t lds, hipStream_t st, const uint16_t* q, uint16_t* kp,
-                          uint16_t* vp, int num_blocks, const int32_t* tables, int max_blocks, const int32_t* ctx,
-                          int hq, int hkv, float c, const uint16_t* nk, const uint16_t* nv, uint16_t* o, float* lse,
-                          float* ws, const DecodeExtra& ex) {
+template <int D, bool F8>
+static void launch_decode(const Plan& p, dim3 grid, size_t lds, hipStream_t st, const uint16_t* q, void* kp, void* vp,
+                          int num_blocks, const int32_t* tables, int max_blocks, const int32_t* ctx, int hq, int hkv,
+                          float c, const uint16_t* nk, const uint16_t* nv, uint16_t* o, float* lse, float* ws,
+                          const DecodeExtra& ex) {
   constexpr int NB = D == 64 ? 2 : 4;
   if constexpr (D == 64) {   // 16 wavefronts only where their registers hold NB blocks
     if (p.waves == 16) {
-      launch_one<D, 16, NB>(p, grid, lds, st, q, kp, vp, num_blocks, tables, max_blocks, ctx, hq, hkv, c, nk, nv, o,
-                            lse, ws, ex);
+      launch_one<D, 16, NB, F8>(p, grid, lds, st, q, kp, vp, num_blocks, tables, max_blocks, ctx, hq, hkv, c, nk, nv,
+                                o, lse, ws, ex);
       return;
     }
   }
   if (p.waves == 8)
-    launch_one<D, 8, NB>(p, grid, lds, st, q, kp, vp, num_blocks, tables, max_blocks, ctx, hq, hkv, c, nk, nv, o,
-                         lse, ws, ex);
+    launch_one<D, 8, NB, F8>(p, grid, lds, st, q, kp, vp, num_blocks, tables, max_blocks, ctx, hq, hkv, c, nk, nv, o,
+                             lse, ws, ex);
   else
-    launch_one<D, 4, NB>(p, grid, lds, st, q, kp, vp, num_blocks, tables, max_blocks, ctx, hq, hkv, c, nk, nv, o,
-                         lse, ws, ex);
+    launch_one<D, 4, NB, F8>(p, grid, lds, st, q, kp, vp, num_blocks, tables, max_blocks, ctx, hq, hkv, c, nk, nv, o,
+                             lse, ws, ex);
 }
 
-extern "C" int kvs_paged_decode(const void* q, void* k_pool, void* v_pool, int num_blocks, const int32_t* block_tables,
-                                int max_blocks, const int32_t* ctx_lens, int batch, int max_ctx, int hq, int hkv, int d,
-                                float scale, const void* new_k, const void* new_v, void* o, float* lse_opt,
-                                void* workspace, size_t workspace_bytes, void* stream) {
-  if (!q || !k_pool || !v_pool || !block_tables || !ctx_lens || !o)
-    return fail(KVS_E_INVAL, "kvs_paged_decode: NULL tensor");
-  if ((new_k == nullptr) != (new_v == nullptr)) return fail(KVS_E_INVAL, "kvs_paged_decode: new_k and new_v go together");
+// Validation, plan and launches of the plain decode (16-bit or 8-bit cache).
+static int run_decode(const char* name, const void* q, void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                      bool f8, int num_blocks, const int32_t* block_tables, int max_blocks, const int32_t* ctx_lens,
+                      int batch, int max_ctx, int hq, int hkv, int d, float scale, const void* new_k,
+                      const void* new_v, void* o, float* lse_opt, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (!q || !k_pool || !v_pool || !block_tables || !ctx_lens || !o || (f8 && (!k_scale || !v_scale)))
+    return fail(KVS_E_INVAL, "%s: NULL tensor", name);
+  if ((new_k == nullptr) != (new_v == nullptr)) return fail(KVS_E_INVAL, "%s: new_k and new_v go together", name);
   if (batch < 0 || max_ctx < 1 || hq <= 0 || hkv <= 0 || hq % hkv || hq / hkv > 16 || (d != 64 && d != 128) ||
       num_blocks <= 0 || max_blocks <= 0 || !(scale > 0.f))
-    return fail(KVS_E_INVAL, "kvs_paged_decode: bad shape (batch=%d hq=%d hkv=%d d=%d max_ctx=%d)", batch, hq, hkv, d,
+    return fail(KVS_E_INVAL, "%s: bad shape (batch=%d hq=%d hkv=%d d=%d max_ctx=%d)", name, batch, hq, hkv, d,
                 max_ctx);
-  if ((long long)max_blocks * kBlock < max_ctx) return fail(KVS_E_INVAL, "kvs_paged_decode: max_blocks*16 < max_ctx");
+  if ((long long)max_blocks * kBlock < max_ctx) return fail(KVS_E_INVAL, "%s: max_blocks*16 < max_ctx", name);
   if (batch == 0) return KVS_OK;
   const Plan p = choose_plan(batch, hq, hkv, d, max_ctx);
   const size_t need = kvs_paged_decode_workspace_size(batch, hq, hkv, d, max_ctx);
   if (need > 0 && (!workspace || workspace_bytes < need))
-    return fail(KVS_E_INVAL, "kvs_paged_decode: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+    return fail(KVS_E_INVAL, "%s: workspace of %zu bytes needed, %zu given", name, need, workspace_bytes);
   const float c = scale * kLog2e;
   const int G = hq / hkv;
   const size_t lds = ((size_t)p.waves * G * d + 2 * (size_t)p.waves * 16) * sizeof(float);
   dim3 grid(p.splits, hkv, batch);
   auto* qq = static_cast<const uint16_t*>(q);
-  auto* kp = static_cast<uint16_t*>(k_pool);
-  auto* vp = static_cast<uint16_t*>(v_pool);
   auto* nk = static_cast<const uint16_t*>(new_k);
   auto* nv = static_cast<const uint16_t*>(new_v);
   auto* oo = static_cast<uint16_t*>(o);
   float* ws = static_cast<float*>(workspace);
   hipStream_t st = as_stream(stream);
-  const DecodeExtra ex{nullptr, nullptr, 0, 0};
-  if (d == 128)
-    launch_decode<128>(p, grid, lds, st, qq, kp, vp, num_blocks, block_tables, max_blocks, ctx_lens, hq, hkv, c, nk, nv,
-                       oo, lse_opt, ws, ex);
-  else
-    launch_decode<64>(p, grid, lds, st, qq, kp, vp, num_blocks, block_tables, max_blocks, ctx_lens, hq, hkv, c, nk, nv,
-                      oo, lse_opt, ws, ex);
-  int rc = launch_status("kvs_paged_decode");
+  const DecodeExtra ex{nullptr, nullptr, 0, 0, k_scale, v_scale};
+  if (d == 128) {
+    if (f8)
+      launch_decode<128, true>(p, grid, lds, st, qq, k_pool, v_pool, num_blocks, block_tables, max_blocks, ctx_lens,
+                               hq, hkv, c, nk, nv, oo, lse_opt, ws, ex);
+    else
+      launch_decode<128, false>(p, grid, lds, st, qq, k_pool, v_pool, num_blocks, block_tables, max_blocks, ctx_lens,
+                                hq, hkv, c, nk, nv, oo, lse_opt, ws, ex);
+  } else {
+    if (f8)
+      launch_decode<64, true>(p, grid, lds, st, qq, k_pool, v_pool, num_blocks, block_tables, max_blocks, ctx_lens,
+                              hq, hkv, c, nk, nv, oo, lse_opt, ws, ex);
+    else
+      launch_decode<64, false>(p, grid, lds, st, qq, k_pool, v_pool, num_blocks, block_tables, max_blocks, ctx_lens,
+                               hq, hkv, c, nk, nv, oo, lse_opt, ws, ex);
+  }
+  int rc = launch_status(name);
   if (rc != KVS_OK || p.splits == 1) return rc;
   if (d == 128)
     hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(hq, batch), dim3(128), 0, st, ws, ctx_lens, hq, hkv, max_blocks,
@@ -459,7 +570,26 @@ extern "C" int kvs_paged_decode(const void* q, void* k_pool, void* v_pool, int n
   else
     hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(hq, batch), dim3(64), 0, st, ws, ctx_lens, hq, hkv, max_blocks,
                        p.splits, p.bps, oo, lse_opt);
-  return launch_status("kvs_paged_decode (merge)");
+  return launch_status(name);
+}
+
+extern "C" int kvs_paged_decode(const void* q, void* k_pool, void* v_pool, int num_blocks, const int32_t* block_tables,
+                                int max_blocks, const int32_t* ctx_lens, int batch, int max_ctx, int hq, int hkv, int d,
+                                float scale, const void* new_k, const void* new_v, void* o, float* lse_opt,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  return run_decode("kvs_paged_decode", q, k_pool, v_pool, nullptr, nullptr, false, num_blocks, block_tables,
+                    max_blocks, ctx_lens, batch, max_ctx, hq, hkv, d, scale, new_k, new_v, o, lse_opt, workspace,
+                    workspace_bytes, stream);
+}
+
+extern "C" int kvs_paged_decode_fp8(const void* q, void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                                    int num_blocks, const int32_t* block_tables, int max_blocks,
+                                    const int32_t* ctx_lens, int batch, int max_ctx, int hq, int hkv, int d,
+                                    float scale, const void* new_k, const void* new_v, void* o, float* lse_opt,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  return run_decode("kvs_paged_decode_fp8", q, k_pool, v_pool, k_scale, v_scale, true, num_blocks, block_tables,
+                    max_blocks, ctx_lens, batch, max_ctx, hq, hkv, d, scale, new_k, new_v, o, lse_opt, workspace,
+                    workspace_bytes, stream);
 }
 
 // ---- Scored decode: partials (always, even for one split) then the logits.
@@ -502,20 +632,20 @@ extern "C" int kvs_paged_decode_scored(const void* q, void* k_pool, void* v_pool
   const size_t lds = ((size_t)p.waves * G * d + 2 * (size_t)p.waves * 16) * sizeof(float);
   dim3 grid(p.splits, hkv, batch);
   auto* qq = static_cast<const uint16_t*>(q);
-  auto* kp = static_cast<uint16_t*>(k_pool);
-  auto* vp = static_cast<uint16_t*>(v_pool);
+  void* kp = k_pool;
+  void* vp = v_pool;
   auto* nk = static_cast<const uint16_t*>(new_k);
   auto* nv = static_cast<const uint16_t*>(new_v);
   auto* oo = static_cast<uint16_t*>(o);
   float* ws = static_cast<float*>(workspace);
   float* logits = reinterpret_cast<float*>(static_cast<char*>(workspace) + scored_logits_offset(batch, hq, p.splits, d));
   hipStream_t st = as_stream(stream);
-  const DecodeExtra ex{dst_slots, logits, max_ctx, 1};
+  const DecodeExtra ex{dst_slots, logits, max_ctx, 1, nullptr, nullptr};
   if (d == 128)
-    launch_decode<128>(p, grid, lds, st, qq, kp, vp, num_blocks, block_tables, max_blocks, ctx_lens, hq, hkv, c, nk, nv,
+    launch_decode<128, false>(p, grid, lds, st, qq, kp, vp, num_blocks, block_tables, max_blocks, ctx_lens, hq, hkv, c, nk, nv,
                        oo, lse_opt, ws, ex);
   else
-    launch_decode<64>(p, grid, lds, st, qq, kp, vp, num_blocks, block_tables, max_blocks, ctx_lens, hq, hkv, c, nk, nv,
+    launch_decode<64, false>(p, grid, lds, st, qq, kp, vp, num_blocks, block_tables, max_blocks, ctx_lens, hq, hkv, c, nk, nv,
                       oo, lse_opt, ws, ex);
   int rc = launch_status("kvs_paged_decode_scored");
   if (rc != KVS_OK) return rc;

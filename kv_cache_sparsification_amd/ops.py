@@ -215,3 +215,76 @@ def new_pools(num_blocks: int, hkv: int, d: int, device="cuda"):
     k_pool = torch.empty(num_blocks, hkv, BLOCK_SIZE, d, device=device, dtype=torch.bfloat16)
     v_pool = torch.empty(num_blocks, hkv, d, BLOCK_SIZE, device=device, dtype=torch.bfloat16)
     return k_pool, v_pool
+
+
+# ---- 8-bit (E4M3) cache: uint8 code pools plus one fp32 scale per (block, head, slot)
+def new_pools_fp8(num_blocks: int, hkv: int, d: int, device="cuda"):
+    """Empty K codes [num_blocks][hkv][16][d], V codes [num_blocks][hkv][d][16] (uint8) and the
+    K and V scales [num_blocks][hkv][16] (fp32)."""
+    k_pool = torch.empty(num_blocks, hkv, BLOCK_SIZE, d, device=device, dtype=torch.uint8)
+    v_pool = torch.empty(num_blocks, hkv, d, BLOCK_SIZE, device=device, dtype=torch.uint8)
+    k_scale = torch.empty(num_blocks, hkv, BLOCK_SIZE, device=device, dtype=torch.float32)
+    v_scale = torch.empty(num_blocks, hkv, BLOCK_SIZE, device=device, dtype=torch.float32)
+    return k_pool, v_pool, k_scale, v_scale
+
+
+def _check_fp8_pools(k_pool, v_pool, k_scale, v_scale):
+    _dev(k_pool, torch.uint8, "k_pool"); _dev(v_pool, torch.uint8, "v_pool")
+    _dev(k_scale, torch.float32, "k_scale"); _dev(v_scale, torch.float32, "v_scale")
+    nb, hkv, bs, d = k_pool.shape
+    if (tuple(v_pool.shape) != (nb, hkv, d, bs) or tuple(k_scale.shape) != (nb, hkv, bs)
+            or tuple(v_scale.shape) != (nb, hkv, bs)):
+        raise ValueError("8-bit pools: K [nb][hkv][16][d], V [nb][hkv][d][16], scales [nb][hkv][16]")
+    return nb, hkv, d
+
+
+def kvs_compact_paged_fp8(k_src, v_src, cu_seqlens, keep_idx, keep_offsets, max_keep: int, k_pool, v_pool, k_scale,
+                          v_scale, block_tables, dst_slot_offset=None, stream=None):
+    """kvs_compact_paged into an 8-bit cache (rows quantized with one scale each)."""
+    _dev(k_src, torch.bfloat16, "k_src"); _dev(v_src, torch.bfloat16, "v_src")
+    _dev(cu_seqlens, torch.int32, "cu_seqlens"); _dev(block_tables, torch.int32, "block_tables")
+    nb, _, _ = _check_fp8_pools(k_pool, v_pool, k_scale, v_scale)
+    if keep_idx is not None:
+        _dev(keep_idx, torch.int32, "keep_idx"); _dev(keep_offsets, torch.int32, "keep_offsets")
+    if dst_slot_offset is not None:
+        _dev(dst_slot_offset, torch.int32, "dst_slot_offset")
+    T, hkv, d = k_src.shape
+    check(lib.kvs_compact_paged_fp8(k_src.data_ptr(), v_src.data_ptr(), cu_seqlens.data_ptr(),
+                                    cu_seqlens.numel() - 1, hkv, d, _ptr(keep_idx), _ptr(keep_offsets),
+                                    int(max_keep), k_pool.data_ptr(), v_pool.data_ptr(), k_scale.data_ptr(),
+                                    v_scale.data_ptr(), nb, block_tables.data_ptr(), block_tables.shape[1],
+                                    _ptr(dst_slot_offset), _stream(stream)))
+
+
+def kvs_paged_decode_fp8(q, k_pool, v_pool, k_scale, v_scale, block_tables, ctx_lens, max_ctx: int,
+                         scale: Optional[float] = None, new_k=None, new_v=None, o=None, lse=None, workspace=None,
+                         stream=None):
+    """kvs_paged_decode over an 8-bit cache; new_k/new_v (bf16) are quantized into slot L-1."""
+    _dev(q, torch.bfloat16, "q")
+    nb, hkv, _ = _check_fp8_pools(k_pool, v_pool, k_scale, v_scale)
+    _dev(block_tables, torch.int32, "block_tables"); _dev(ctx_lens, torch.int32, "ctx_lens")
+    B, hq, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if new_k is not None:
+        _dev(new_k, torch.bfloat16, "new_k"); _dev(new_v, torch.bfloat16, "new_v")
+    o = torch.empty_like(q) if o is None else _dev(o, torch.bfloat16, "o")
+    if lse is not None:
+        _dev(lse, torch.float32, "lse")
+    need = kvs_paged_decode_workspace_size(B, hq, hkv, d, int(max_ctx))
+    if need and workspace is None:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(lib.kvs_paged_decode_fp8(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), k_scale.data_ptr(),
+                                   v_scale.data_ptr(), nb, block_tables.data_ptr(), block_tables.shape[1],
+                                   ctx_lens.data_ptr(), B, int(max_ctx), hq, hkv, d, float(scale), _ptr(new_k),
+                                   _ptr(new_v), o.data_ptr(), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
+    return o
+
+
+def kvs_copy_blocks_fp8(k_pool, v_pool, k_scale, v_scale, src_dst_pairs, stream=None):
+    """Copy whole blocks of an 8-bit cache (codes and scales): src_dst_pairs [n][2] int32 device."""
+    nb, hkv, d = _check_fp8_pools(k_pool, v_pool, k_scale, v_scale)
+    _dev(src_dst_pairs, torch.int32, "src_dst_pairs")
+    check(lib.kvs_copy_blocks_fp8(k_pool.data_ptr(), v_pool.data_ptr(), k_scale.data_ptr(), v_scale.data_ptr(), nb,
+                                  hkv, d, src_dst_pairs.data_ptr(), src_dst_pairs.shape[0], _stream(stream)))

@@ -163,3 +163,31 @@ def test_eviction_calls_validate_on_the_host():
     assert call(nk=None, nv=None) == -1                 # dst_slots without a new token
     assert call(stride=399) == -1                       # slot rows shorter than the context
     assert call(wsb=ws - 1) == -1 and b"workspace" in L.kvs_last_error()
+
+
+def test_fp8_calls_validate_on_the_host():
+    L = kvs.lib
+    fake = 0x1000   # never dereferenced: the checks fail first
+    # compaction: the scale arrays are required, d is 64 or 128
+    comp = dict(k=fake, v=fake, cu=fake, ns=1, hkv=2, d=128, keep=None, ko=None, mk=64, kp=fake, vp=fake, ks=fake,
+                vs=fake, nb=8, tbl=fake, mb=4, off=None, st=None)
+
+    def compact(**kw):
+        return L.kvs_compact_paged_fp8(*dict(comp, **kw).values())
+    assert compact(ks=None) == -1 and b"NULL" in L.kvs_last_error()
+    assert compact(d=96) == -1
+    assert compact(ns=0) == 0 and compact(mk=0) == 0   # nothing to write: nothing launched
+    # decode: scales required, workspace as for the 16-bit decode
+    ws = L.kvs_paged_decode_workspace_size(1, 32, 8, 128, 400)
+    dec = dict(q=fake, kp=fake, vp=fake, ks=fake, vs=fake, nb=64, tbl=fake, mb=25, ctx=fake, B=1, mc=400, hq=32,
+               hkv=8, d=128, sc=0.1, nk=fake, nv=fake, o=fake, lse=None, ws=fake, wsb=ws, st=None)
+
+    def decode(**kw):
+        return L.kvs_paged_decode_fp8(*dict(dec, **kw).values())
+    assert decode(vs=None) == -1
+    assert decode(nv=None) == -1                         # new_k and new_v go together
+    assert decode(mb=24) == -1                           # table rows shorter than the context
+    assert decode(wsb=ws - 1) == -1 and b"workspace" in L.kvs_last_error()
+    assert decode(B=0) == 0
+    assert L.kvs_copy_blocks_fp8(fake, fake, None, fake, 8, 2, 128, fake, 1, None) == -1
+    assert L.kvs_copy_blocks_fp8(fake, fake, fake, fake, 8, 2, 128, None, 0, None) == 0

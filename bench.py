@@ -223,8 +223,7 @@ def main():
                          HBM_PEAK_GBS, "window_score.hip"),
         "topk_select": ("hbm", 4 * hkv * n + 4 * hkv * k_eff, "GB/s", HBM_PEAK_GBS, "topk_select.hip"),
         "compact_paged": ("hbm", 8 * k_eff * hkv * d, "GB/s", HBM_PEAK_GBS, "compact_paged.hip"),
-        "paged_decode": ("hbm", 4 * mean_L * hkv * d + 4 * hq * d + 8 * hkv * d + 4 * math.ceil(mean_L / 16),
-                         "GB/s", HBM_PEAK_GBS, "paged_decode.hip"),
+        "paged_decode": ("hbm", decode_bytes(mean_L, hq, hkv, d), "GB/s", HBM_PEAK_GBS, "paged_decode.hip"),
     }
     rooflines = {}
     for kname, (bound, amount, unit, peak, src) in work.items():
@@ -270,6 +269,8 @@ def main():
     }
 
     line["decode_at_scale"] = decode_at_scale(kvs, torch, wl, 100)
+    line["fp8_decode_at_scale"] = decode_at_scale(kvs, torch, wl, 100, fp8=True)
+    line["fp8_layer"] = fp8_layer(kvs, torch, wl, w, k, v, cu_d, keep, keep_off, steps_dec)
     # the prefill-side pass of the last step left the compressed cache in the pools
     kvs.kvs_compact_paged(k, v, cu_d, keep, keep_off, k_eff, k_pool, v_pool, tbl)
     line["decode_evict"] = decode_evict(kvs, torch, wl, w, k_pool, v_pool, tbl, S, cu_d, keep, keep_off, 200)
@@ -278,11 +279,12 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def decode_at_scale(kvs, torch, wl, steps):
+def decode_at_scale(kvs, torch, wl, steps, fp8=False):
     """Paged decode where the read volume, not the latency, sets the time: the long-context
     workload's compressed layers (4 sequences, 3000 kept tokens each plus the appended ones,
     8 KV heads, d=128), `steps` decode steps with append replayed as one HIP graph.  Reports
-    the HBM rate of the algorithmic K/V bytes against the peak."""
+    the HBM rate of the algorithmic bytes against the peak.  fp8: the same over the 8-bit
+    cache (codes plus one fp32 scale per row)."""
     import numpy as np
     w = wl.WORKLOADS[4]
     B, hq, hkv, d = w.num_seqs, w.hq, w.hkv, w.d
@@ -290,10 +292,18 @@ def decode_at_scale(kvs, torch, wl, steps):
     max_ctx = kept + steps
     nb_seq = -(-max_ctx // 16)
     dev = torch.device("cuda:0")
-    k_pool, v_pool = kvs.new_pools(B * nb_seq, hkv, d, device=dev)
     gen = torch.Generator(device=dev).manual_seed(4242)
-    k_pool.copy_(torch.randn(k_pool.shape, generator=gen, device=dev).to(torch.bfloat16))
-    v_pool.copy_(torch.randn(v_pool.shape, generator=gen, device=dev).to(torch.bfloat16))
+    if fp8:
+        pools = kvs.new_pools_fp8(B * nb_seq, hkv, d, device=dev)
+        for t in pools[:2]:       # finite codes of either sign (no NaN code)
+            t.copy_(torch.randint(0, 0x7F, t.shape, generator=gen, device=dev, dtype=torch.uint8)
+                    | (torch.randint(0, 2, t.shape, generator=gen, device=dev, dtype=torch.uint8) << 7))
+        for t in pools[2:]:
+            t.copy_(torch.rand(t.shape, generator=gen, device=dev) * 0.01 + 0.002)
+    else:
+        pools = kvs.new_pools(B * nb_seq, hkv, d, device=dev)
+        for t in pools:
+            t.copy_(torch.randn(t.shape, generator=gen, device=dev).to(torch.bfloat16))
     perm = np.random.default_rng(4242).permutation(B * nb_seq).astype(np.int32)
     tbl = torch.from_numpy(perm.reshape(B, nb_seq)).to(dev)
     lens = torch.tensor([[kept + s + 1] * B for s in range(steps)], dtype=torch.int32, device=dev)
@@ -301,12 +311,38 @@ def decode_at_scale(kvs, torch, wl, steps):
     ws = torch.empty(max(kvs.kvs_paged_decode_workspace_size(B, hq, hkv, d, max_ctx), 1), dtype=torch.uint8,
                      device=dev)
     od = torch.empty(steps, B, hq, d, dtype=torch.bfloat16, device=dev)
+    decode = kvs.kvs_paged_decode_fp8 if fp8 else kvs.kvs_paged_decode
 
     def run():
         for s in range(steps):
-            kvs.kvs_paged_decode(qs[s], k_pool, v_pool, tbl, lens[s], max_ctx, new_k=nks[s], new_v=nvs[s],
-                                 o=od[s], workspace=ws)
+            decode(qs[s], *pools, tbl, lens[s], max_ctx, new_k=nks[s], new_v=nvs[s], o=od[s], workspace=ws)
 
+    us = _graph_time_us(torch, run, steps)
+    mean_L = kept + (steps + 1) / 2.0
+    nbytes = B * decode_bytes(mean_L, hq, hkv, d, fp8)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"workload": f"{B} sequences x {kept}-{kept + steps} cached tokens, {hq}q/{hkv}kv heads, d={d}, "
+                        f"{steps} decode steps with append (HIP graph)" + (", 8-bit E4M3 cache" if fp8 else ""),
+            "us_per_step": round(us, 3), "algorithmic_bytes_per_step": int(nbytes),
+            "achieved_GBs": round(gbs, 1), "peak_GBs": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "tok_s": round(B / (us * 1e-6), 1)}
+
+
+def decode_bytes(mean_L, hq, hkv, d, fp8=False):
+    """Algorithmic HBM bytes of one sequence's decode step: the cached K and V (bf16, or codes
+    plus one fp32 scale per row), the query read and output written (bf16), the new K/V read
+    (bf16) and stored, and the block-table entries."""
+    if fp8:
+        cache = 2 * mean_L * hkv * (d + 4)
+        new = 4 * hkv * d + 2 * hkv * (d + 4)
+    else:
+        cache = 4 * mean_L * hkv * d
+        new = 8 * hkv * d
+    return cache + 4 * hq * d + new + 4 * math.ceil(mean_L / 16)
+
+
+def _graph_time_us(torch, run, steps, reps=3):
+    """Capture `run` (steps launches) as one HIP graph and time its replays: us per step."""
     stream = torch.cuda.current_stream()
     side = torch.cuda.Stream()
     side.wait_stream(stream)
@@ -320,21 +356,58 @@ def decode_at_scale(kvs, torch, wl, steps):
     graph.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = 3
     e0.record(stream)
     for _ in range(reps):
         graph.replay()
     e1.record(stream)
     torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / (reps * steps)
-    mean_L = kept + (steps + 1) / 2.0
-    nbytes = B * (4 * mean_L * hkv * d + 4 * hq * d + 8 * hkv * d + 4 * math.ceil(mean_L / 16))
-    gbs = nbytes / (us * 1e-6) / 1e9
-    return {"workload": f"{B} sequences x {kept}-{kept + steps} cached tokens, {hq}q/{hkv}kv heads, d={d}, "
-                        f"{steps} decode steps with append (HIP graph)",
-            "us_per_step": round(us, 3), "algorithmic_bytes_per_step": int(nbytes),
-            "achieved_GBs": round(gbs, 1), "peak_GBs": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4),
-            "tok_s": round(B / (us * 1e-6), 1)}
+    return e0.elapsed_time(e1) * 1e3 / (reps * steps)
+
+
+def fp8_layer(kvs, torch, wl, w, k, v, cu_d, keep, keep_off, steps):
+    """The bench layer with an 8-bit cache: the quantizing compaction of the kept rows (timed
+    per launch with events) and `steps` decode steps with append (one HIP graph)."""
+    dev = torch.device("cuda:0")
+    n, hq, hkv, d, kb = w.fixed_len, w.hq, w.hkv, w.d, w.budgets[0]
+    k_eff = min(kb, n)
+    max_ctx = k_eff + steps
+    nblk = -(-max_ctx // 16)
+    pools = kvs.new_pools_fp8(nblk, hkv, d, device=dev)
+    tbl = torch.arange(nblk, dtype=torch.int32, device=dev).flip(0).reshape(1, nblk).contiguous()
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        kvs.kvs_compact_paged_fp8(k, v, cu_d, keep, keep_off, k_eff, *pools, tbl)
+    reps = 20
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    evs[0].record(stream)
+    for i in range(reps):
+        kvs.kvs_compact_paged_fp8(k, v, cu_d, keep, keep_off, k_eff, *pools, tbl)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    comp_us = sum(evs[i].elapsed_time(evs[i + 1]) for i in range(reps)) * 1e3 / reps
+    comp_bytes = 4 * k_eff * hkv * d + 2 * k_eff * hkv * (d + 4) + 4 * hkv * k_eff
+    ctx = torch.arange(k_eff + 1, k_eff + steps + 1, dtype=torch.int32, device=dev).reshape(steps, 1)
+    qs, nks, nvs = zip(*[wl.device_decode_step(w, 0, 2000 + s, [0], device=dev) for s in range(steps)])
+    ws = torch.empty(max(kvs.kvs_paged_decode_workspace_size(1, hq, hkv, d, max_ctx), 1), dtype=torch.uint8,
+                     device=dev)
+    od = torch.empty(steps, 1, hq, d, dtype=torch.bfloat16, device=dev)
+
+    def run():
+        for s in range(steps):
+            kvs.kvs_paged_decode_fp8(qs[s], *pools, tbl, ctx[s], max_ctx, new_k=nks[s], new_v=nvs[s], o=od[s],
+                                     workspace=ws)
+
+    kvs.kvs_compact_paged_fp8(k, v, cu_d, keep, keep_off, k_eff, *pools, tbl)
+    us = _graph_time_us(torch, run, steps, reps=1)
+    mean_L = k_eff + (steps + 1) / 2.0
+    nbytes = decode_bytes(mean_L, hq, hkv, d, fp8=True)
+    return {"workload": f"bench layer, 8-bit E4M3 cache: compaction of k={k_eff} kept rows per KV head, "
+                        f"then {steps} decode steps with append (HIP graph)",
+            "compact_us": round(comp_us, 3), "compact_algorithmic_bytes": int(comp_bytes),
+            "compact_GBs": round(comp_bytes / (comp_us * 1e-6) / 1e9, 1),
+            "decode_us_per_step": round(us, 3), "decode_tok_s": round(1.0 / (us * 1e-6), 1),
+            "decode_algorithmic_bytes_per_step": int(nbytes),
+            "decode_GBs": round(nbytes / (us * 1e-6) / 1e9, 1)}
 
 
 def decode_evict(kvs, torch, wl, w, k_pool, v_pool, tbl, S, cu_d, keep, keep_off, steps):
@@ -359,26 +432,7 @@ def decode_evict(kvs, torch, wl, w, k_pool, v_pool, tbl, S, cu_d, keep, keep_off
             kvs.kvs_paged_decode_scored(qs[s], k_pool, v_pool, tbl, n_fill, cap, sl_sc, new_k=nks[s], new_v=nvs[s],
                                         dst_slots=dst, o=od[s], workspace=ws)
 
-    stream = torch.cuda.current_stream()
-    side = torch.cuda.Stream()
-    side.wait_stream(stream)
-    with torch.cuda.stream(side):
-        run()
-    stream.wait_stream(side)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        run()
-    graph.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = 3
-    e0.record(stream)
-    for _ in range(reps):
-        graph.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / (reps * steps)
+    us = _graph_time_us(torch, run, steps)
     return {"workload": f"bench layer, cache full at k={cap} (alpha={alpha}): every step evicts per KV head, "
                         f"{steps} steps (HIP graph)",
             "us_per_step": round(us, 3), "tok_s": round(1.0 / (us * 1e-6), 1),

@@ -4,7 +4,7 @@
 
 Every HIP and C++ source under csrc/ is compiled to an object file under _build/ and linked
 into kv_cache_sparsification_amd/libkvs.so.  All HIP code is built with the packed-fp32
-target feature switched off.
+target feature switched off and with MFMA results kept in VGPRs.
 """
 from __future__ import annotations
 
@@ -24,7 +24,10 @@ ARCH = "gfx950"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-function",
-          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # MFMA accumulators in VGPRs: otherwise the compiler may pick the AGPR form and copy
+          # every accumulator tile in and out around each MFMA
+          "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _hipcc() -> str:

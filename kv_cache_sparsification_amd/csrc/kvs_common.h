@@ -104,14 +104,20 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d, f
   return (uint32_t)w;
 }
 
-// Four codes to four bf16 (exact: every E4M3 value is a bf16 value): low word = bytes 0, 1.
-__device__ __forceinline__ u32x2 e4m3x4_to_bf16(uint32_t c) {
-  const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)c, false);
-  const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)c, true);
-  u32x2 r;
-  r[0] = __builtin_amdgcn_perm(__float_as_uint(lo[1]), __float_as_uint(lo[0]), 0x07060302u);
-  r[1] = __builtin_amdgcn_perm(__float_as_uint(hi[1]), __float_as_uint(hi[0]), 0x07060302u);
-  return r;
+// Codes to bf16 (exact: every E4M3 value is a bf16 value) with gfx950's scaled conversion at
+// scale 1: two codes per instruction, byte order kept (bytes 0, 1 with word_sel false).
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t c, bool hi) {
+  const bf16x2v r = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, 1.0f, true)
+                       : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, 1.0f, false);
+  return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ short4_t e4m3x4_to_bf16x4(uint32_t c) {
+  return __builtin_bit_cast(short4_t, u32x2{e4m3x2_to_bf16x2(c, false), e4m3x2_to_bf16x2(c, true)});
+}
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(u32x2 c) {
+  return __builtin_bit_cast(bf16x8, u32x4{e4m3x2_to_bf16x2(c[0], false), e4m3x2_to_bf16x2(c[0], true),
+                                          e4m3x2_to_bf16x2(c[1], false), e4m3x2_to_bf16x2(c[1], true)});
 }
 
 // Eight bf16 (one 16-byte chunk) times r to eight codes.

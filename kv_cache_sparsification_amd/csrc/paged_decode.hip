@@ -35,6 +35,7 @@ constexpr int kCUs = 256;
 constexpr int kTargetWGs = 2048;
 constexpr int kMaxSplitsMerge = 256;
 constexpr int kBandwidthBlocks = 4096;   // (sequence, KV head, block) triples per call
+constexpr float kLazy = 8.f;             // log2 headroom before the reference max moves
 
 struct Plan {
   int waves;    // wavefronts per workgroup
@@ -72,10 +73,14 @@ inline Plan choose_plan(int batch, int hq, int hkv, int d, int max_ctx) {
   const int want = (kTargetWGs + units - 1) / units;
   int bps = (nblk + want - 1) / want;
   if (bps < p.waves) bps = p.waves;
-  // Enough blocks overall for the read volume to set the time: give every wavefront a full
-  // round of blocks in flight instead (4 KV heads x 3000+ tokens, batch 4: 27.7 us per step at
-  // 4 blocks per split, 22.1 at 8, 17.6 at 16, 18.5 at 32).
-  if (units * nblk >= kBandwidthBlocks && bps < p.waves * p.nb) bps = p.waves * p.nb;
+  // Enough blocks overall for the read volume to set the time: eight wavefronts of two blocks
+  // in flight, two rounds each (8 KV heads x 3000+ tokens, batch 4, per step: 4 waves x 4
+  // blocks x 1 round 15.2 us, 8 x 4 x 1 14.4, 8 x 2 x 2 13.7, 8 x 2 x 3 15.1, 8 x 2 x 4 18.0).
+  if (units * nblk >= kBandwidthBlocks) {
+    p.waves = 8;
+    p.nb = 2;
+    if (bps < 2 * p.waves * p.nb) bps = 2 * p.waves * p.nb;
+  }
   if ((nblk + bps - 1) / bps > kMaxSplitsMerge) bps = (nblk + kMaxSplitsMerge - 1) / kMaxSplitsMerge;
   p.bps = bps;
   p.splits = (nblk + bps - 1) / bps;
@@ -93,6 +98,34 @@ struct DecodeExtra {
   float* k_scale;             // 8-bit cache: per-row scales [num_blocks][hkv][16]
   float* v_scale;
 };
+
+// Max / sum over the four lanes l, l^16, l^32, l^48 (the 16-lane rows that hold one column's
+// tokens), with the gfx950 row swaps instead of LDS shuffles.
+__device__ __forceinline__ float max_over_rows(float v) {
+  v = half_max(v);
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// Value of lane I of each group of four lanes (DPP quad permutation [I, I, I, I]).
+template <int I>
+__device__ __forceinline__ float quad_bcast(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), I * 0x55, 0xf, 0xf, false));
+}
+
+// Max over the 16 lanes of each row, left in the row's lane 15 (DPP row shifts; the lanes
+// shifted in read 0, so the values must be >= 0).
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, true)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, true)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, true)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, true)));
+  return v;
+}
+__device__ __forceinline__ float sum_over_rows(float v) {
+  v = half_sum(v);
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // 8-bit cache operands of one block, as loaded: K codes (8 per lane and k-step), V^T codes (4
 // slots of one channel per lane and d tile) and the scales of the lane's 4 slots.
@@ -160,6 +193,27 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
   const uint16_t* nk = new_k + ((size_t)b * hkv + g) * D;
   const uint16_t* nv = new_v + ((size_t)b * hkv + g) * D;
 
+  // 8-bit cache: the wavefront whose blocks include the new token's fetches that token right
+  // away (lane l: K and V values 2l, 2l+1), quantizes it while its first blocks are in flight
+  // and hands each lane the codes of its operand positions; they replace the slot's loaded
+  // codes when the wavefront reaches that block.
+  const bool owner = F8 && append && last_blk >= blk_begin && last_blk < blk_end && (last_blk - blk_begin) % W == w;
+  uint32_t nk2 = 0u, nv2 = 0u;
+  if constexpr (F8) {
+    if (owner && 2 * lane < D) {
+      nk2 = *reinterpret_cast<const uint32_t*>(nk + 2 * lane);
+      nv2 = *reinterpret_cast<const uint32_t*>(nv + 2 * lane);
+    }
+  }
+  u32x2 nkc[KS];                 // the new token's K codes at this lane's A positions (column last_slot)
+  uint32_t nvc[MT];              // its V code of channel mt*16 + col, low byte (row last_slot / 4)
+  float nks = 0.f, nvs = 0.f;    // and its scales
+  bool quantized = false;
+
+  // Online softmax per column against a lazily moved reference max m_run: a block whose
+  // column max exceeds m_run by at most 2^kLazy (log2 units) is accumulated against the old
+  // reference (its p stay <= 2^kLazy), so the accumulators are rescaled only when some
+  // column's max jumps further; one wave vote decides.
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 acc_o[MT];
 #pragma unroll
@@ -186,13 +240,16 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
       if constexpr (F8) {
         const uint8_t* kb = k_pool8 + bh * kBlock * D;
         const uint8_t* vb = v_pool8 + bh * D * kBlock;
+        // scales first (the scores wait for them, not for V): lane (col, grp) fetches the scale
+        // of slot grp*4 + col%4; the quad's four lanes then share theirs
+        f8[j].sk[0] = ex.k_scale[bh * kBlock + grp * 4 + (col & 3)];
+        f8[j].sv[0] = ex.v_scale[bh * kBlock + grp * 4 + (col & 3)];
 #pragma unroll
         for (int st = 0; st < KS; ++st) f8[j].k[st] = *reinterpret_cast<const u32x2*>(kb + col * D + st * 32 + grp * 8);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
           f8[j].v[mt] = *reinterpret_cast<const uint32_t*>(vb + (size_t)(mt * 16 + col) * kBlock + grp * 4);
-        f8[j].sk = *reinterpret_cast<const f32x4*>(ex.k_scale + bh * kBlock + grp * 4);
-        f8[j].sv = *reinterpret_cast<const f32x4*>(ex.v_scale + bh * kBlock + grp * 4);
+        (void)app_blk;
       } else {
         const uint16_t* kb = k_pool + bh * kBlock * D;
         const uint16_t* vb = v_pool + bh * D * kBlock;
@@ -211,6 +268,38 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
         }
       }
     }
+    if constexpr (F8) {
+      if (owner && !quantized) {
+        // The new token's rows: whole-wavefront amax, one scale each, two codes per lane, then
+        // each lane gathers the codes of its operand positions from the lanes that made them.
+        quantized = true;
+        const float k0 = bf16_bits_to_f32(nk2 & 0xffffu), k1 = bf16_bits_to_f32(nk2 >> 16);
+        const float v0 = bf16_bits_to_f32(nv2 & 0xffffu), v1 = bf16_bits_to_f32(nv2 >> 16);
+        float ak = row_max16(max_over_rows(fmaxf(fabsf(k0), fabsf(k1))));   // lane 15 of each row: the amax
+        float av = row_max16(max_over_rows(fmaxf(fabsf(v0), fabsf(v1))));
+        ak = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(ak), 15));
+        av = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(av), 15));
+        float kr, vr;
+        e4m3_row_params(ak, nks, kr);
+        e4m3_row_params(av, nvs, vr);
+        const int kc2 = (int)(e4m3x4(k0, k1, 0.f, 0.f, kr) & 0xffffu);   // codes of K values 2l, 2l+1
+        const int vc2 = (int)(e4m3x4(v0, v1, 0.f, 0.f, vr) & 0xffffu);
+#pragma unroll
+        for (int st = 0; st < KS; ++st) {   // K values st*32 + grp*8 .. +8 live in lanes st*16 + grp*4 .. +4
+          const int src = st * 16 + grp * 4;
+          const uint32_t c0 = __builtin_amdgcn_ds_bpermute(4 * src, kc2);
+          const uint32_t c1 = __builtin_amdgcn_ds_bpermute(4 * (src + 1), kc2);
+          const uint32_t c2 = __builtin_amdgcn_ds_bpermute(4 * (src + 2), kc2);
+          const uint32_t c3 = __builtin_amdgcn_ds_bpermute(4 * (src + 3), kc2);
+          nkc[st] = u32x2{c0 | (c1 << 16), c2 | (c3 << 16)};
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {   // V channel mt*16 + col lives in lane mt*8 + col/2
+          const uint32_t c = __builtin_amdgcn_ds_bpermute(4 * (mt * 8 + col / 2), vc2);
+          nvc[mt] = (c >> (8 * (col & 1))) & 0xffu;
+        }
+      }
+    }
 #pragma unroll
     for (int j = 0; j < kNB; ++j) {
       const int bi = bi0 + W * j;
@@ -219,94 +308,80 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
       const size_t bh = (size_t)blk * hkv + g;
       const bool app_blk = append && bi == last_blk;
       if constexpr (F8) {
-        if (app_blk) {
-          // Quantize the new token's rows (amax over the whole wavefront, one scale per row) and
-          // put its codes and scales where the slot's loaded ones were; they are stored below.
-          float ak = 0.f, av = 0.f;
-          if (2 * lane < D) {
-            const uint32_t xk = *reinterpret_cast<const uint32_t*>(nk + 2 * lane);
-            const uint32_t xv = *reinterpret_cast<const uint32_t*>(nv + 2 * lane);
-            ak = fmaxf(fabsf(bf16_bits_to_f32(xk & 0xffffu)), fabsf(bf16_bits_to_f32(xk >> 16)));
-            av = fmaxf(fabsf(bf16_bits_to_f32(xv & 0xffffu)), fabsf(bf16_bits_to_f32(xv >> 16)));
-          }
-#pragma unroll
-          for (int m = 1; m < kWave; m <<= 1) {
-            ak = fmaxf(ak, wave_xor(ak, m));
-            av = fmaxf(av, wave_xor(av, m));
-          }
-          float ksc, kr, vsc, vr;
-          e4m3_row_params(ak, ksc, kr);
-          e4m3_row_params(av, vsc, vr);
-          if (col == last_slot) {
-#pragma unroll
-            for (int st = 0; st < KS; ++st)
-              f8[j].k[st] = e4m3x8_from_bf16(*reinterpret_cast<const u32x4*>(nk + st * 32 + grp * 8), kr);
-          }
-          if (grp == last_slot / 4) {
-            const int sh = 8 * (last_slot % 4);
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-              const uint32_t code = e4m3x4(bf16_bits_to_f32(nv[mt * 16 + col]), 0.f, 0.f, 0.f, vr) & 0xffu;
-              f8[j].v[mt] = (f8[j].v[mt] & ~(0xffu << sh)) | (code << sh);
-            }
-            f8[j].sk[last_slot % 4] = ksc;
-            f8[j].sv[last_slot % 4] = vsc;
-          }
-          // keep the appended token in the pool for later steps
+        {
+          const float k0 = f8[j].sk[0], v0 = f8[j].sv[0];
+          f8[j].sk = f32x4{quad_bcast<0>(k0), quad_bcast<1>(k0), quad_bcast<2>(k0), quad_bcast<3>(k0)};
+          f8[j].sv = f32x4{quad_bcast<0>(v0), quad_bcast<1>(v0), quad_bcast<2>(v0), quad_bcast<3>(v0)};
+        }
+        if (app_blk) {   // the new token's codes and scales replace the slot's loaded ones, and are stored
           if (col == last_slot) {
             uint8_t* kd = k_pool8 + bh * kBlock * D + last_slot * D;
 #pragma unroll
-            for (int st = 0; st < KS; ++st) *reinterpret_cast<u32x2*>(kd + st * 32 + grp * 8) = f8[j].k[st];
-          }
-          if (grp == last_slot / 4) {
-            uint8_t* vd = v_pool8 + bh * D * kBlock;
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-              vd[(size_t)(mt * 16 + col) * kBlock + last_slot] = (uint8_t)(f8[j].v[mt] >> (8 * (last_slot % 4)));
-            if (col == 0) {
-              ex.k_scale[bh * kBlock + last_slot] = ksc;
-              ex.v_scale[bh * kBlock + last_slot] = vsc;
+            for (int st = 0; st < KS; ++st) {
+              f8[j].k[st] = nkc[st];
+              *reinterpret_cast<u32x2*>(kd + st * 32 + grp * 8) = nkc[st];
             }
           }
+          if (grp == last_slot / 4) {
+            const int sh = 8 * (last_slot % 4);
+            uint8_t* vd = v_pool8 + bh * D * kBlock;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+              f8[j].v[mt] = (f8[j].v[mt] & ~(0xffu << sh)) | (nvc[mt] << sh);
+              vd[(size_t)(mt * 16 + col) * kBlock + last_slot] = (uint8_t)nvc[mt];
+            }
+            f8[j].sk[last_slot % 4] = nks;
+            f8[j].sv[last_slot % 4] = nvs;
+          }
+          if (lane == 0) {
+            ex.k_scale[bh * kBlock + last_slot] = nks;
+            ex.v_scale[bh * kBlock + last_slot] = nvs;
+          }
         }
 #pragma unroll
-        for (int st = 0; st < KS; ++st) {
-          const u32x2 a = e4m3x4_to_bf16(f8[j].k[st][0]), b2 = e4m3x4_to_bf16(f8[j].k[st][1]);
-          kf[j][st] = __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b2[0], b2[1]});
+        for (int st = 0; st < KS; ++st) kf[j][st] = e4m3x8_to_bf16(f8[j].k[st]);
+        // slots past the context (the last block's tail) may hold stale codes: zero them
+        uint32_t vmask = 0xffffffffu;
+        if (bi * kBlock + kBlock > L) {
+          const int live = L - bi * kBlock - grp * 4;   // slots of the lane's 4 inside the context
+          vmask = live >= 4 ? 0xffffffffu : (live <= 0 ? 0u : (0xffffffffu >> (8 * (4 - live))));
         }
-        // slots past the context (the last block's tail) hold stale codes: zero them
-        const int live = L - bi * kBlock - grp * 4;   // slots of the lane's 4 that are in the context
-        const uint32_t vmask = live >= 4 ? 0xffffffffu : (live <= 0 ? 0u : (0xffffffffu >> (8 * (4 - live))));
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          vf[j][mt] = __builtin_bit_cast(short4_t, e4m3x4_to_bf16(f8[j].v[mt] & vmask));
+        for (int mt = 0; mt < MT; ++mt) vf[j][mt] = e4m3x4_to_bf16x4(f8[j].v[mt] & vmask);
       }
       f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int st = 0; st < KS; ++st) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[j][st], qf[st], sc, 0, 0, 0);
       // sc[i]: token grp*4 + i of this block against column col.
       float x[4];
-      float bm = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = bi * kBlock + grp * 4 + i;
         const float si = F8 ? sc[i] * f8[j].sk[i] : sc[i];
         x[i] = t < L ? si * c_log2 : -INFINITY;
-        bm = fmaxf(bm, x[i]);
-        if (ex.logits && col < G && t < L) ex.logits[((size_t)b * hq + g * G + col) * ex.logit_stride + t] = x[i];
       }
-      bm = fmaxf(bm, wave_xor(bm, 16));
-      bm = fmaxf(bm, wave_xor(bm, 32));
-      const float m_new = fmaxf(m_run, bm);
-      const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
-      float p[4], psum = 0.f;
+      if (ex.logits) {   // scored decode only (uniform branch)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = bi * kBlock + grp * 4 + i;
+          if (col < G && t < L) ex.logits[((size_t)b * hq + g * G + col) * ex.logit_stride + t] = x[i];
+        }
+      }
+      const float bm = max_over_rows(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+      if (__builtin_amdgcn_ballot_w64(bm > m_run + kLazy) != 0) {   // rare: move the reference
+        const float m_new = fmaxf(m_run, bm);
+        const float corr = __builtin_amdgcn_exp2f(m_run - m_new);  // first block: exp2(-inf) = 0
+        l_run *= corr;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc_o[mt] *= corr;
+        m_run = m_new;
+      }
+      float p[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        p[i] = __builtin_amdgcn_exp2f(x[i] - m_new);
-        psum += p[i];
+        p[i] = __builtin_amdgcn_exp2f(x[i] - m_run);
+        l_run += p[i];
       }
-      l_run = l_run * corr + psum;
-      m_run = m_new;
       short4_t pb;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -315,10 +390,7 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
         pb[i] = (short)f32_to_bf16_bits(pi);
       }
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        acc_o[mt] *= corr;
-        acc_o[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf[j][mt], pb, acc_o[mt], 0, 0, 0);
-      }
+      for (int mt = 0; mt < MT; ++mt) acc_o[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf[j][mt], pb, acc_o[mt], 0, 0, 0);
       if constexpr (!F8) {
         if (app_blk) {   // keep the appended token in the pool for later steps
           if (col == last_slot) {
@@ -336,8 +408,7 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
       }
     }
   }
-  l_run += wave_xor(l_run, 16);
-  l_run += wave_xor(l_run, 32);
+  l_run = sum_over_rows(l_run);
 
   // acc_o[mt][i] is output channel mt*16 + grp*4 + i of column col; only real columns are kept.
   if (col < G) {
@@ -381,29 +452,35 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
   }
 }
 
-// Merge of the split partials: one workgroup per (query head, sequence), a thread per output
-// channel.  Each thread takes splits 16 at a time and issues all their loads (its output
-// channel plus the (max, sum) pair, shared with its neighbours through L1) before using any,
-// then folds the chunk into a running (max, sum, output) - one memory round trip per 16
-// splits instead of one per split.
-// Fold the `used` split partials of one (sequence, query head) for output channel dd:
-// returns the running max M (log2 units), the sum l against it and the output numerator.
+// Merge of the split partials.  Each thread folds its output channel over the splits 16 at a
+// time, issuing all loads of a chunk (its channel plus the (max, sum) pair, shared with its
+// neighbours through L1) before using any: one memory round trip per 16 splits.  The loads
+// cover every split the launch has (a bound known on the host), so they do not wait for the
+// context length; the splits past the sequence's last non-empty one (`used`) hold stale data
+// and are masked out afterwards.
+// Returns the running max M (log2 units), the sum l against it and the output numerator.
 template <int D>
-__device__ __forceinline__ void merge_partials(const float* __restrict__ part, int used, int dd, float& M, float& l,
-                                               float& acc) {
+__device__ __forceinline__ void merge_partials(const float* __restrict__ part, int splits, int used, int dd, float& M,
+                                               float& l, float& acc) {
   constexpr int C = 16;
   M = -INFINITY;
   l = 0.f;
   acc = 0.f;
-  for (int sp0 = 0; sp0 < used; sp0 += C) {
+  for (int sp0 = 0; sp0 < splits; sp0 += C) {
     float mv[C], lv[C], ov[C];
 #pragma unroll
     for (int i = 0; i < C; ++i) {
+      const float* ps = part + (size_t)(sp0 + i < splits ? sp0 + i : 0) * (D + 2);
+      mv[i] = ps[0];
+      lv[i] = ps[1];
+      ov[i] = ps[2 + dd];
+    }
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
       const bool in = sp0 + i < used;
-      const float* ps = part + (size_t)(in ? sp0 + i : 0) * (D + 2);
-      mv[i] = in ? ps[0] : -INFINITY;
-      lv[i] = in ? ps[1] : 0.f;
-      ov[i] = in ? ps[2 + dd] : 0.f;
+      mv[i] = in ? mv[i] : -INFINITY;
+      lv[i] = in ? lv[i] : 0.f;
+      ov[i] = in ? ov[i] : 0.f;
     }
     float cm = M;
 #pragma unroll
@@ -430,10 +507,10 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict
   const int L = ctx_lens[b];
   const int nblk = min((L + kBlock - 1) / kBlock, max_blocks);
   const int used = min((nblk + bps - 1) / bps, splits);
-  if (used <= 1) return;                      // written directly by the decode kernel
   {
     float M, l, acc;
-    merge_partials<D>(ws + ((size_t)b * hq + h) * splits * (D + 2), used, dd, M, l, acc);
+    merge_partials<D>(ws + ((size_t)b * hq + h) * splits * (D + 2), splits, used, dd, M, l, acc);
+    if (used <= 1) return;                    // written directly by the decode kernel
     o[((size_t)b * hq + h) * D + dd] = (uint16_t)f32_to_bf16_bits(acc / l);
     if (lse_out && dd == 0) lse_out[(size_t)b * hq + h] = (M + log2f(l)) * kLn2;
   }
@@ -457,7 +534,7 @@ __global__ __launch_bounds__(256) void decode_merge_score_kernel(
     const int c = e / D, dd = e % D;
     const int h = g * G + c;
     float M, l, acc;
-    merge_partials<D>(ws + ((size_t)b * hq + h) * splits * (D + 2), used, dd, M, l, acc);
+    merge_partials<D>(ws + ((size_t)b * hq + h) * splits * (D + 2), splits, used, dd, M, l, acc);
     o[((size_t)b * hq + h) * D + dd] = (uint16_t)f32_to_bf16_bits(acc / l);
     if (dd == 0) {
       lse2[c] = M + log2f(l);
@@ -501,20 +578,25 @@ static void launch_decode(const Plan& p, dim3 grid, size_t lds, hipStream_t st, 
                           int num_blocks, const int32_t* tables, int max_blocks, const int32_t* ctx, int hq, int hkv,
                           float c, const uint16_t* nk, const uint16_t* nv, uint16_t* o, float* lse, float* ws,
                           const DecodeExtra& ex) {
-  constexpr int NB = D == 64 ? 2 : 4;
-  if constexpr (D == 64) {   // 16 wavefronts only where their registers hold NB blocks
-    if (p.waves == 16) {
-      launch_one<D, 16, NB, F8>(p, grid, lds, st, q, kp, vp, num_blocks, tables, max_blocks, ctx, hq, hkv, c, nk, nv,
-                                o, lse, ws, ex);
-      return;
-    }
+  // (wavefronts, blocks in flight per wavefront) pairs the plans use
+  if (p.waves == 8 && p.nb == 2)
+    launch_one<D, 8, 2, F8>(p, grid, lds, st, q, kp, vp, num_blocks, tables, max_blocks, ctx, hq, hkv, c, nk, nv, o,
+                            lse, ws, ex);
+  else if constexpr (D == 64) {
+    if (p.waves == 16)
+      launch_one<D, 16, 2, F8>(p, grid, lds, st, q, kp, vp, num_blocks, tables, max_blocks, ctx, hq, hkv, c, nk, nv, o,
+                               lse, ws, ex);
+    else
+      launch_one<D, 4, 2, F8>(p, grid, lds, st, q, kp, vp, num_blocks, tables, max_blocks, ctx, hq, hkv, c, nk, nv, o,
+                              lse, ws, ex);
+  } else {
+    if (p.waves == 8)
+      launch_one<D, 8, 4, F8>(p, grid, lds, st, q, kp, vp, num_blocks, tables, max_blocks, ctx, hq, hkv, c, nk, nv, o,
+                              lse, ws, ex);
+    else
+      launch_one<D, 4, 4, F8>(p, grid, lds, st, q, kp, vp, num_blocks, tables, max_blocks, ctx, hq, hkv, c, nk, nv, o,
+                              lse, ws, ex);
   }
-  if (p.waves == 8)
-    launch_one<D, 8, NB, F8>(p, grid, lds, st, q, kp, vp, num_blocks, tables, max_blocks, ctx, hq, hkv, c, nk, nv, o,
-                             lse, ws, ex);
-  else
-    launch_one<D, 4, NB, F8>(p, grid, lds, st, q, kp, vp, num_blocks, tables, max_blocks, ctx, hq, hkv, c, nk, nv, o,
-                             lse, ws, ex);
 }
 
 // Validation, plan and launches of the plain decode (16-bit or 8-bit cache).
@@ -532,7 +614,8 @@ static int run_decode(const char* name, const void* q, void* k_pool, void* v_poo
                 max_ctx);
   if ((long long)max_blocks * kBlock < max_ctx) return fail(KVS_E_INVAL, "%s: max_blocks*16 < max_ctx", name);
   if (batch == 0) return KVS_OK;
-  const Plan p = choose_plan(batch, hq, hkv, d, max_ctx);
+  Plan p = choose_plan(batch, hq, hkv, d, max_ctx);
+  if (f8 && p.waves == 16) p.waves = 8;   // one workgroup per pair: the 8-bit path's registers fit 8 wavefronts
   const size_t need = kvs_paged_decode_workspace_size(batch, hq, hkv, d, max_ctx);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(KVS_E_INVAL, "%s: workspace of %zu bytes needed, %zu given", name, need, workspace_bytes);

@@ -127,14 +127,19 @@ __device__ __forceinline__ float sum_over_rows(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// 8-bit cache operands of one block, as loaded: K codes (8 per lane and k-step), V^T codes (4
-// slots of one channel per lane and d tile) and the scales of the lane's 4 slots.
+// 8-bit cache operands of one block, as loaded: K codes (16-byte chunks c of the lane's token
+// row at bytes 64c + 16*grp, i.e. one 64-byte run per row and instruction; k-step st uses half
+// st%2 of chunk st/2, and the query fragments follow the same order of d), V^T codes (4 slots
+// of one channel per lane and d tile) and the scales of the lane's 4 slots.
 template <int KS, int MT>
 struct F8Block {
-  u32x2 k[KS];
+  u32x4 k[KS / 2];
   uint32_t v[MT];
   f32x4 sk, sv;
 };
+
+// d offset of the 8 values lane group grp supplies at k-step st of the 8-bit path's score product.
+__device__ __forceinline__ int f8_kofs(int st, int grp) { return (st / 2) * 64 + grp * 16 + (st % 2) * 8; }
 
 // F8: the cache holds E4M3 codes with a fp32 scale per (slot, KV head) row; codes are widened
 // to bf16 (exact) for the same MFMAs, the K scale multiplies the slot's score and the V scale
@@ -183,7 +188,8 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
 #pragma unroll
   for (int st = 0; st < KS; ++st) {
     u32x4 x = {0u, 0u, 0u, 0u};
-    if (col < G) x = *reinterpret_cast<const u32x4*>(q + ((size_t)b * hq + g * G + col) * D + st * 32 + grp * 8);
+    const int dofs = F8 ? f8_kofs(st, grp) : st * 32 + grp * 8;
+    if (col < G) x = *reinterpret_cast<const u32x4*>(q + ((size_t)b * hq + g * G + col) * D + dofs);
     qf[st] = __builtin_bit_cast(bf16x8, x);
   }
 
@@ -245,7 +251,7 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
         f8[j].sk[0] = ex.k_scale[bh * kBlock + grp * 4 + (col & 3)];
         f8[j].sv[0] = ex.v_scale[bh * kBlock + grp * 4 + (col & 3)];
 #pragma unroll
-        for (int st = 0; st < KS; ++st) f8[j].k[st] = *reinterpret_cast<const u32x2*>(kb + col * D + st * 32 + grp * 8);
+        for (int c = 0; c < KS / 2; ++c) f8[j].k[c] = *reinterpret_cast<const u32x4*>(kb + col * D + c * 64 + grp * 16);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
           f8[j].v[mt] = *reinterpret_cast<const uint32_t*>(vb + (size_t)(mt * 16 + col) * kBlock + grp * 4);
@@ -285,8 +291,8 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
         const int kc2 = (int)(e4m3x4(k0, k1, 0.f, 0.f, kr) & 0xffffu);   // codes of K values 2l, 2l+1
         const int vc2 = (int)(e4m3x4(v0, v1, 0.f, 0.f, vr) & 0xffffu);
 #pragma unroll
-        for (int st = 0; st < KS; ++st) {   // K values st*32 + grp*8 .. +8 live in lanes st*16 + grp*4 .. +4
-          const int src = st * 16 + grp * 4;
+        for (int st = 0; st < KS; ++st) {   // K values f8_kofs(st, grp) .. +8 live in lanes f8_kofs/2 .. +4
+          const int src = f8_kofs(st, grp) / 2;
           const uint32_t c0 = __builtin_amdgcn_ds_bpermute(4 * src, kc2);
           const uint32_t c1 = __builtin_amdgcn_ds_bpermute(4 * (src + 1), kc2);
           const uint32_t c2 = __builtin_amdgcn_ds_bpermute(4 * (src + 2), kc2);
@@ -318,8 +324,9 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
             uint8_t* kd = k_pool8 + bh * kBlock * D + last_slot * D;
 #pragma unroll
             for (int st = 0; st < KS; ++st) {
-              f8[j].k[st] = nkc[st];
-              *reinterpret_cast<u32x2*>(kd + st * 32 + grp * 8) = nkc[st];
+              f8[j].k[st / 2][2 * (st % 2)] = nkc[st][0];
+              f8[j].k[st / 2][2 * (st % 2) + 1] = nkc[st][1];
+              *reinterpret_cast<u32x2*>(kd + f8_kofs(st, grp)) = nkc[st];
             }
           }
           if (grp == last_slot / 4) {
@@ -339,7 +346,8 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
           }
         }
 #pragma unroll
-        for (int st = 0; st < KS; ++st) kf[j][st] = e4m3x8_to_bf16(f8[j].k[st]);
+        for (int st = 0; st < KS; ++st)
+          kf[j][st] = e4m3x8_to_bf16(u32x2{f8[j].k[st / 2][2 * (st % 2)], f8[j].k[st / 2][2 * (st % 2) + 1]});
         // slots past the context (the last block's tail) may hold stale codes: zero them
         uint32_t vmask = 0xffffffffu;
         if (bi * kBlock + kBlock > L) {

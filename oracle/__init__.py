@@ -32,8 +32,10 @@ Modules and the step each one follows:
   fp8           the 8-bit (E4M3) cache: encoding, per-row scales, the
                 quantized compaction and decode append ([PAG] "Related
                 techniques")
+  prefix        chunked prefill and the block-hash prefix match ([PAG]
+                "Sharing blocks between sequences"; [KVS] Conclusion)
 
-Readings taken where the pages are silent or garbled are named R1..R24 in the
+Readings taken where the pages are silent or garbled are named R1..R26 in the
 docstrings; each one is listed with its justification in the design notes.
 Every function is pinned by the CPU tests (``pytest -m "not gpu"``); none is
 "parity unpinned".
@@ -45,6 +47,7 @@ from .paged import BlockAllocator, blocks_for, write_rows, gather_rows, compact_
 from .decode import decode_attention
 from .eviction import SlotCache, init_cache, select_slot, decode_step
 from . import fp8
+from . import prefix
 
 __all__ = [
     "causal_attention", "attention_probs",
@@ -53,5 +56,5 @@ __all__ = [
     "BlockAllocator", "blocks_for", "write_rows", "gather_rows", "compact_into_pool",
     "decode_attention",
     "SlotCache", "init_cache", "select_slot", "decode_step",
-    "fp8",
+    "fp8", "prefix",
 ]

@@ -11,7 +11,8 @@
  *   kvs_topk_select       the kept token indices per KV head
  *   kvs_compact_paged     copy of the kept K/V rows into 16-token blocks through block tables
  *   kvs_paged_decode      attention of one new token per sequence over the paged cache
- * with 8-bit (E4M3) variants of the cache calls (*_fp8), decode-time scoring and eviction,
+ * with chunked-prefill variants (*_chunk) and a gather of cached blocks for prefix reuse,
+ * 8-bit (E4M3) variants of the cache calls (*_fp8), decode-time scoring and eviction,
  * a host block allocator (free list, reference counts, copy-on-write) and the device
  * block copy that copy-on-write needs.
  *
@@ -99,6 +100,53 @@ int kvs_prefill_attn_lse(const void* q, const void* k, const void* v, const int3
 int kvs_window_score(const void* q, const void* k, const float* lse, const int32_t* cu_seqlens,
                      int num_seqs, int total_tokens, int max_seqlen, int alpha, int hq, int hkv,
                      int d, float scale, float* scores, void* stream);
+
+/*
+ * Chunked prefill and prefix reuse.  [PAG] "Sharing blocks between sequences": sharing
+ * extends across requests by hashing full blocks (how vLLM caches prompts); [KVS]
+ * Conclusion lists chunked prefill and prefix caching as not yet supported there.  A chunk
+ * is the last m_s query rows of prompt s, whose keys K/V hold all n_s >= m_s prompt tokens
+ * (a reused prefix first gathered back from the cache): query row r sits at prompt position
+ * n_s - m_s + r and sees keys 0 .. n_s - m_s + r, so its O and LSE are those of the whole
+ * prompt's prefill and nothing is carried between chunks.
+ */
+
+/*
+ * kvs_prefill_attn_lse_chunk - kvs_prefill_attn_lse for chunks.
+ * In:  q [total_q][hq][d] (rows cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1), k, v
+ *      [total_k][hkv][d] (rows cu_seqlens_k[s] ..), bf16; both cu arrays [num_seqs+1] int32
+ *      (device); max_q >= every m_s, max_k >= every n_s, and n_s >= m_s (trusted).
+ * Out: o [total_q][hq][d]; lse, rowmax_opt, ell_opt [hq][total_q], as kvs_prefill_attn_lse.
+ * Errors: as kvs_prefill_attn_lse (the size limit applies to max_k); KVS_E_INVAL also if
+ *         cu_seqlens_k is NULL or max_k < max_q.
+ */
+int kvs_prefill_attn_lse_chunk(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                               const int32_t* cu_seqlens_k, int num_seqs, int total_q, int max_q, int max_k, int hq,
+                               int hkv, int d, float scale, void* o, float* lse, float* rowmax_opt, float* ell_opt,
+                               void* stream);
+
+/*
+ * kvs_window_score_chunk - kvs_window_score when q and lse hold only a prompt's last m_s rows
+ * (the chunk of kvs_prefill_attn_lse_chunk).  The window, a = min(alpha, n_s) rows, must lie
+ * inside the chunk (a <= m_s); window rows before the chunk would not be counted.
+ * In:  q [total_q][hq][d], lse [hq][total_q]; k [total_k][hkv][d]; cu arrays as above.
+ * Out: scores [hkv][total_k] fp32, indexed by the key's position in k.
+ * Errors: as kvs_window_score; KVS_E_INVAL also if cu_seqlens_k is NULL.
+ */
+int kvs_window_score_chunk(const void* q, const void* k, const float* lse, const int32_t* cu_seqlens_q,
+                           const int32_t* cu_seqlens_k, int num_seqs, int total_q, int total_k, int max_k, int alpha,
+                           int hq, int hkv, int d, float scale, float* scores, void* stream);
+
+/*
+ * kvs_gather_paged - tokens 0 .. counts[s]-1 of sequence s read back through its block table
+ * (layouts of kvs_compact_paged) into contiguous rows: k_dst[dst_start[s] + t][g][:] =
+ * K of slot t, and likewise v_dst.  counts, dst_start [num_seqs] int32 (device); max_count
+ * >= every count.  Used to put a reused prefix in front of a chunk's own K/V.
+ * Errors: KVS_E_INVAL on a NULL tensor or bad shape; KVS_E_HIP on launch failure.
+ */
+int kvs_gather_paged(const void* k_pool, const void* v_pool, int num_blocks, const int32_t* block_tables,
+                     int max_blocks, int num_seqs, int hkv, int d, const int32_t* counts, const int32_t* dst_start,
+                     int max_count, void* k_dst, void* v_dst, void* stream);
 
 /*
  * kvs_topk_select - the tokens each KV head keeps, per prompt.

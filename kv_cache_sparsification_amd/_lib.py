@@ -40,6 +40,12 @@ SIGNATURES = {
     "kvs_paged_decode_fp8": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _c_int, _vp, _c_int, _c_int, _c_int,
                                       _c_int, _c_int, _c_float, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
     "kvs_copy_blocks_fp8": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _c_int, _vp]),
+    "kvs_prefill_attn_lse_chunk": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                            _c_int, _c_float, _vp, _vp, _vp, _vp, _vp]),
+    "kvs_window_score_chunk": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                        _c_int, _c_int, _c_float, _vp, _vp]),
+    "kvs_gather_paged": (_c_int, [_vp, _vp, _c_int, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _c_int, _vp, _vp,
+                                  _vp]),
     "kvs_alloc_create": (_c_int, [_c_int, _i32p, _c_int, ctypes.POINTER(_vp)]),
     "kvs_alloc_destroy": (None, [_vp]),
     "kvs_alloc_block": (_c_int, [_vp, _i32p]),

@@ -1,5 +1,5 @@
-// Gather-compaction of kept K/V rows into 16-token blocks, and the block copy of
-// copy-on-write.
+// Gather-compaction of kept K/V rows into 16-token blocks, the reverse gather of cached
+// blocks into contiguous rows (a reused prefix), and the block copy of copy-on-write.
 //
 // [PAG] Ultralytics glossary, "PagedAttention", "How paging works": the cache is stored in
 // fixed 16-token blocks anywhere in GPU memory and a per-request block table gives their
@@ -118,6 +118,62 @@ __global__ __launch_bounds__(kWavesPerWG * kWave) void compact_kernel(
   }
 }
 
+// Gather: tokens 0..count-1 of a sequence read back through its block table into contiguous
+// token-major rows (the inverse of a keep-all compaction).  One wavefront per (table entry,
+// head): K rows move with 16-byte lanes; V comes channel-major, each lane reading the 16 slots
+// of a channel pair (two 32-byte runs) and writing them back as 4-byte pieces of 16 token rows.
+template <int D>
+__global__ __launch_bounds__(kWavesPerWG * kWave) void gather_kernel(
+    const uint16_t* __restrict__ k_pool, const uint16_t* __restrict__ v_pool, int num_blocks,
+    const int32_t* __restrict__ block_tables, int max_blocks, int hkv, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ dst_start, uint16_t* __restrict__ k_dst, uint16_t* __restrict__ v_dst,
+    int blocks_per_seq) {
+  const int lane = threadIdx.x % kWave;
+  const int unit = blockIdx.x * kWavesPerWG + threadIdx.x / kWave;
+  const int s = blockIdx.y;
+  if (unit >= blocks_per_seq * hkv) return;
+  const int bi = unit / hkv, g = unit % hkv;
+  const int cnt = counts[s];
+  const int d0 = dst_start[s];
+  if (bi * kBlock >= cnt || bi >= max_blocks) return;
+  const int blk = block_tables[(size_t)s * max_blocks + bi];
+  if (blk < 0 || blk >= num_blocks) return;
+  const int valid = min(kBlock, cnt - bi * kBlock);   // slots of this block inside the count
+
+  constexpr int kLanesPerRow = D * 2 / 16;
+  constexpr int kRowsPerIter = kWave / kLanesPerRow;
+  constexpr int kIters = kBlock / kRowsPerIter;
+  const uint16_t* ksrc = k_pool + ((size_t)blk * hkv + g) * kBlock * D;
+  {
+    const int c = lane % kLanesPerRow;
+    u32x4 val[kIters];
+#pragma unroll
+    for (int it = 0; it < kIters; ++it)
+      val[it] = *reinterpret_cast<const u32x4*>(ksrc + (it * kRowsPerIter + lane / kLanesPerRow) * D + c * 8);
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+      const int j = it * kRowsPerIter + lane / kLanesPerRow;
+      if (j < valid)
+        *reinterpret_cast<u32x4*>(k_dst + ((size_t)(d0 + bi * kBlock + j) * hkv + g) * D + c * 8) = val[it];
+    }
+  }
+  constexpr int kPairs = D / 2;
+  if (lane >= kPairs) return;
+  const uint16_t* vsrc = v_pool + ((size_t)blk * hkv + g) * D * kBlock;
+  const u32x4* c0 = reinterpret_cast<const u32x4*>(vsrc + (size_t)(2 * lane) * kBlock);
+  const u32x4* c1 = reinterpret_cast<const u32x4*>(vsrc + (size_t)(2 * lane + 1) * kBlock);
+  const u32x4 a0 = c0[0], a1 = c0[1], b0 = c1[0], b1 = c1[1];   // slots 0-7 and 8-15 of both channels
+#pragma unroll
+  for (int j = 0; j < kBlock; ++j) {
+    if (j >= valid) break;
+    const uint32_t wa = j < 8 ? a0[j / 2] : a1[(j - 8) / 2];
+    const uint32_t wb = j < 8 ? b0[j / 2] : b1[(j - 8) / 2];
+    const uint32_t lo = (j % 2 == 0) ? (wa & 0xffffu) : (wa >> 16);   // channel 2*lane, slot j
+    const uint32_t hi = (j % 2 == 0) ? (wb & 0xffffu) : (wb >> 16);   // channel 2*lane + 1
+    *reinterpret_cast<uint32_t*>(v_dst + ((size_t)(d0 + bi * kBlock + j) * hkv + g) * D + 2 * lane) = lo | (hi << 16);
+  }
+}
+
 // One workgroup copies one (src, dst) block pair in both pools.
 __global__ __launch_bounds__(256) void copy_blocks_kernel(uint16_t* __restrict__ k_pool,
                                                           uint16_t* __restrict__ v_pool, int num_blocks,
@@ -184,4 +240,27 @@ extern "C" int kvs_copy_blocks(void* k_pool, void* v_pool, int num_blocks, int h
                      static_cast<uint16_t*>(k_pool), static_cast<uint16_t*>(v_pool), num_blocks, block_elems,
                      src_dst_pairs);
   return launch_status("kvs_copy_blocks");
+}
+
+extern "C" int kvs_gather_paged(const void* k_pool, const void* v_pool, int num_blocks, const int32_t* block_tables,
+                                int max_blocks, int num_seqs, int hkv, int d, const int32_t* counts,
+                                const int32_t* dst_start, int max_count, void* k_dst, void* v_dst, void* stream) {
+  if (!k_pool || !v_pool || !block_tables || !counts || !dst_start || !k_dst || !v_dst)
+    return fail(KVS_E_INVAL, "kvs_gather_paged: NULL tensor");
+  if (num_seqs < 0 || hkv <= 0 || (d != 64 && d != 128) || max_count < 0 || num_blocks <= 0 || max_blocks <= 0)
+    return fail(KVS_E_INVAL, "kvs_gather_paged: bad shape (num_seqs=%d hkv=%d d=%d)", num_seqs, hkv, d);
+  if (num_seqs == 0 || max_count == 0) return KVS_OK;
+  const int blocks_per_seq = (max_count + kBlock - 1) / kBlock;
+  dim3 grid((blocks_per_seq * hkv + kWavesPerWG - 1) / kWavesPerWG, num_seqs);
+  auto* kp = static_cast<const uint16_t*>(k_pool);
+  auto* vp = static_cast<const uint16_t*>(v_pool);
+  auto* kd = static_cast<uint16_t*>(k_dst);
+  auto* vd = static_cast<uint16_t*>(v_dst);
+  if (d == 128)
+    hipLaunchKernelGGL(gather_kernel<128>, grid, dim3(kWavesPerWG * kWave), 0, as_stream(stream), kp, vp, num_blocks,
+                       block_tables, max_blocks, hkv, counts, dst_start, kd, vd, blocks_per_seq);
+  else
+    hipLaunchKernelGGL(gather_kernel<64>, grid, dim3(kWavesPerWG * kWave), 0, as_stream(stream), kp, vp, num_blocks,
+                       block_tables, max_blocks, hkv, counts, dst_start, kd, vd, blocks_per_seq);
+  return launch_status("kvs_gather_paged");
 }

@@ -62,9 +62,9 @@ __device__ __forceinline__ int kappa(int m) { return (m & ~12) | ((m & 4) << 1) 
 template <int D>
 __global__ __launch_bounds__(kWaves * kWave, 1) void prefill_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const int32_t* __restrict__ cu_seqlens, int num_seqs, int total_tokens, int hq, int hkv, float c_log2,
-    uint16_t* __restrict__ o, float* __restrict__ lse, float* __restrict__ rowmax, float* __restrict__ ell, int nqt,
-    int total_items) {
+    const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ cu_seqlens_k, int num_seqs, int total_tokens,
+    int hq, int hkv, float c_log2, uint16_t* __restrict__ o, float* __restrict__ lse, float* __restrict__ rowmax,
+    float* __restrict__ ell, int nqt, int total_items) {
   constexpr int KCU = D / 8;     // 16-byte chunks per tile row
   constexpr int ST1 = D / 16;    // k-steps of S^T = K Q^T
   constexpr int MT2 = D / 32;    // channel tiles of O^T
@@ -94,18 +94,23 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void prefill_kernel(
   const int s = rest % num_seqs;
   const int g = rest / num_seqs;
   const int h = g * G + hl;
+  // Query rows [base, base + m) of Q; keys [kbase_tok, kbase_tok + n) of K/V.  A chunk's row r
+  // sits at prompt position qoff + r (the chunk ends the keys), which the causal rule uses.
   const int base = cu_seqlens[s];
-  const int n = cu_seqlens[s + 1] - base;
+  const int m = cu_seqlens[s + 1] - base;
+  const int kbase_tok = cu_seqlens_k ? cu_seqlens_k[s] : base;
+  const int n = cu_seqlens_k ? cu_seqlens_k[s + 1] - kbase_tok : m;
+  const int qoff = n - m;
   const int r0 = qt * kBQ;
-  if (r0 >= n) return;
+  if (r0 >= m) return;
 
   const int tid = threadIdx.x, lane = tid % kWave;
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform: branches on it stay scalar
   const int col = lane % 32, half = lane / 32;
   const int grp = w / kGroupWaves;       // ping-pong group; wavefronts w and w +- 4 share a SIMD
   const int R = r0 + (2 * (w % kGroupWaves) + grp) * kRowsPerWave;   // first row of this wavefront's strip
-  const int row = R + col;               // this lane's query row (N index)
-  const int kend = min(r0 + kBQ, n);
+  const int row = R + col;               // this lane's query row (N index), chunk-local
+  const int kend = min(qoff + r0 + kBQ, n);
   const int ntiles = (kend + kBK - 1) / kBK;
 
   // B operand of S^T: Q^T[d][row] for each 16-wide d step.
@@ -113,7 +118,7 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void prefill_kernel(
 #pragma unroll
   for (int st = 0; st < ST1; ++st) {
     u32x4 x = {0u, 0u, 0u, 0u};
-    if (row < n) x = *reinterpret_cast<const u32x4*>(q + ((size_t)(base + row) * hq + h) * D + st * 16 + half * 8);
+    if (row < m) x = *reinterpret_cast<const u32x4*>(q + ((size_t)(base + row) * hq + h) * D + st * 16 + half * 8);
     qf[st] = __builtin_bit_cast(bf16x8, x);
   }
 
@@ -140,8 +145,8 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void prefill_kernel(
   const int row_pitch = hkv * kRowBytes;                           // bytes between consecutive keys
   const int seq_bytes = (n - 1) * row_pitch + kRowBytes;           // this head's rows of the prompt
   const int tile_bytes = kBK * row_pitch;
-  const char* kbase = reinterpret_cast<const char*>(k + ((size_t)base * hkv + g) * D);
-  const char* vbase = reinterpret_cast<const char*>(v + ((size_t)base * hkv + g) * D);
+  const char* kbase = reinterpret_cast<const char*>(k + ((size_t)kbase_tok * hkv + g) * D);
+  const char* vbase = reinterpret_cast<const char*>(v + ((size_t)kbase_tok * hkv + g) * D);
   int koff[KLD];
 #pragma unroll
   for (int it = 0; it < KLD; ++it) {
@@ -294,8 +299,8 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void prefill_kernel(
   bf16x8 pf[KS2];
   auto vector_phase = [&](int t) {                 // X(t)
     const int kb = t * kBK;
-    if (kb + kBK - 1 > R) {   // wave-uniform: mask keys past the row
-      const int lim = row - kb - 8 * half;
+    if (kb + kBK - 1 > qoff + R) {   // wave-uniform: mask keys past the row
+      const int lim = qoff + row - kb - 8 * half;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -357,7 +362,7 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void prefill_kernel(
 
   // ---- epilogue: O = acc / l, LSE = ln 2 * (m_ref + log2 l)
   const float l = half_sum(l_lane);   // sum of exp2(x - m_ref)
-  if (row < n) {
+  if (row < m) {
     const float inv = 1.f / l;
     uint16_t* orow = o + ((size_t)(base + row) * hq + h) * D;
 #pragma unroll
@@ -384,20 +389,20 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void prefill_kernel(
 
 using namespace kvs;
 
-extern "C" int kvs_prefill_attn_lse(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
-                                    int num_seqs, int total_tokens, int max_seqlen, int hq, int hkv, int d,
-                                    float scale, void* o, float* lse, float* rowmax_opt, float* ell_opt,
-                                    void* stream) {
-  if (!q || !k || !v || !cu_seqlens || !o || !lse) return fail(KVS_E_INVAL, "kvs_prefill_attn_lse: NULL tensor");
-  if (num_seqs < 0 || total_tokens < 0 || max_seqlen < 0 || hq <= 0 || hkv <= 0 || hq % hkv || hq / hkv > 16 ||
-      (d != 64 && d != 128) || !(scale > 0.f))
-    return fail(KVS_E_INVAL, "kvs_prefill_attn_lse: bad shape (hq=%d hkv=%d d=%d)", hq, hkv, d);
+static int run_prefill(const char* name, const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                       const int32_t* cu_seqlens_k, int num_seqs, int total_tokens, int max_seqlen, int max_seqlen_k,
+                       int hq, int hkv, int d, float scale, void* o, float* lse, float* rowmax_opt, float* ell_opt,
+                       void* stream) {
+  if (!q || !k || !v || !cu_seqlens || !o || !lse) return fail(KVS_E_INVAL, "%s: NULL tensor", name);
+  if (num_seqs < 0 || total_tokens < 0 || max_seqlen < 0 || max_seqlen_k < 0 || hq <= 0 || hkv <= 0 || hq % hkv ||
+      hq / hkv > 16 || (d != 64 && d != 128) || !(scale > 0.f))
+    return fail(KVS_E_INVAL, "%s: bad shape (hq=%d hkv=%d d=%d)", name, hq, hkv, d);
   if (num_seqs == 0 || max_seqlen == 0 || total_tokens == 0) return KVS_OK;
-  if ((long long)max_seqlen * hkv * d * 2 > 0x7fffffffll)   // K/V rows of one prompt are addressed with 32-bit offsets
-    return fail(KVS_E_INVAL, "kvs_prefill_attn_lse: prompt of %d tokens x %d KV heads too large", max_seqlen, hkv);
+  if ((long long)max_seqlen_k * hkv * d * 2 > 0x7fffffffll)   // K/V rows of one prompt are addressed with 32-bit offsets
+    return fail(KVS_E_INVAL, "%s: prompt of %d tokens x %d KV heads too large", name, max_seqlen_k, hkv);
   const int nqt = (max_seqlen + kBQ - 1) / kBQ;
   const long long items = (long long)hkv * num_seqs * nqt * (hq / hkv);
-  if (items > (1ll << 30)) return fail(KVS_E_INVAL, "kvs_prefill_attn_lse: grid too large");
+  if (items > (1ll << 30)) return fail(KVS_E_INVAL, "%s: grid too large", name);
   const int grid = (int)((items + kXcds - 1) / kXcds * kXcds);
   const float c = scale * kLog2e;
   auto* qq = static_cast<const uint16_t*>(q);
@@ -406,9 +411,29 @@ extern "C" int kvs_prefill_attn_lse(const void* q, const void* k, const void* v,
   auto* oo = static_cast<uint16_t*>(o);
   if (d == 128)
     hipLaunchKernelGGL(prefill_kernel<128>, dim3(grid), dim3(kWaves * kWave), 0, as_stream(stream), qq, kk, vv,
-                       cu_seqlens, num_seqs, total_tokens, hq, hkv, c, oo, lse, rowmax_opt, ell_opt, nqt, (int)items);
+                       cu_seqlens, cu_seqlens_k, num_seqs, total_tokens, hq, hkv, c, oo, lse, rowmax_opt, ell_opt, nqt,
+                       (int)items);
   else
     hipLaunchKernelGGL(prefill_kernel<64>, dim3(grid), dim3(kWaves * kWave), 0, as_stream(stream), qq, kk, vv,
-                       cu_seqlens, num_seqs, total_tokens, hq, hkv, c, oo, lse, rowmax_opt, ell_opt, nqt, (int)items);
-  return launch_status("kvs_prefill_attn_lse");
+                       cu_seqlens, cu_seqlens_k, num_seqs, total_tokens, hq, hkv, c, oo, lse, rowmax_opt, ell_opt, nqt,
+                       (int)items);
+  return launch_status(name);
+}
+
+extern "C" int kvs_prefill_attn_lse(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                                    int num_seqs, int total_tokens, int max_seqlen, int hq, int hkv, int d,
+                                    float scale, void* o, float* lse, float* rowmax_opt, float* ell_opt,
+                                    void* stream) {
+  return run_prefill("kvs_prefill_attn_lse", q, k, v, cu_seqlens, nullptr, num_seqs, total_tokens, max_seqlen,
+                     max_seqlen, hq, hkv, d, scale, o, lse, rowmax_opt, ell_opt, stream);
+}
+
+extern "C" int kvs_prefill_attn_lse_chunk(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                                          const int32_t* cu_seqlens_k, int num_seqs, int total_q, int max_q,
+                                          int max_k, int hq, int hkv, int d, float scale, void* o, float* lse,
+                                          float* rowmax_opt, float* ell_opt, void* stream) {
+  if (!cu_seqlens_k) return fail(KVS_E_INVAL, "kvs_prefill_attn_lse_chunk: NULL tensor");
+  if (max_k < max_q) return fail(KVS_E_INVAL, "kvs_prefill_attn_lse_chunk: max_k < max_q");
+  return run_prefill("kvs_prefill_attn_lse_chunk", q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, max_q,
+                     max_k, hq, hkv, d, scale, o, lse, rowmax_opt, ell_opt, stream);
 }

@@ -34,16 +34,20 @@ constexpr int kRowChunk = 128;  // window rows staged in LDS at a time (4 M tile
 template <int D>
 __global__ __launch_bounds__(kWaves * kWave) void window_score_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ lse,
-    const int32_t* __restrict__ cu_seqlens, int total_tokens, int alpha, int hq, int hkv, float c_log2,
-    float* __restrict__ S) {
+    const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ cu_seqlens_k, int total_tokens, int total_k,
+    int alpha, int hq, int hkv, float c_log2, float* __restrict__ S) {
   constexpr int kStride = D + 8;                       // bf16 per LDS row (16-byte pad)
   __shared__ __attribute__((aligned(16))) uint16_t qs[kRowChunk * kStride];
   __shared__ float lse2[kRowChunk];
   __shared__ int jlim[kRowChunk];
 
+  // Q rows and LSE of prompt s: [base, base + m); its keys and scores: [kbase, kbase + n).  The
+  // Q rows are the prompt's last m positions (a chunk that ends the prompt, or all of it).
   const int g = blockIdx.y, s = blockIdx.z;
   const int base = cu_seqlens[s];
-  const int n = cu_seqlens[s + 1] - base;
+  const int m = cu_seqlens[s + 1] - base;
+  const int kbase = cu_seqlens_k ? cu_seqlens_k[s] : base;
+  const int n = cu_seqlens_k ? cu_seqlens_k[s + 1] - kbase : m;
   const int kb_wg = blockIdx.x * kKeysPerWG;
   if (kb_wg >= n) return;
   const int G = hq / hkv;
@@ -59,7 +63,7 @@ __global__ __launch_bounds__(kWaves * kWave) void window_score_kernel(
 #pragma unroll
   for (int st = 0; st < D / 16; ++st) {
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (key < n) v = *reinterpret_cast<const u32x4*>(k + ((size_t)(base + key) * hkv + g) * D + st * 16 + half * 8);
+    if (key < n) v = *reinterpret_cast<const u32x4*>(k + ((size_t)(kbase + key) * hkv + g) * D + st * 16 + half * 8);
     kf[st] = __builtin_bit_cast(bf16x8, v);
   }
 
@@ -70,18 +74,18 @@ __global__ __launch_bounds__(kWaves * kWave) void window_score_kernel(
       const int r = e / (D / 8), cc = e % (D / 8);
       const int rr = r0 + r;
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (rr < rows) {
-        const int h = g * G + rr / a, j = n - a + rr % a;
+      if (rr < rows && m - a + rr % a >= 0) {   // a window row before the chunk is not counted
+        const int h = g * G + rr / a, j = m - a + rr % a;   // chunk-local row of window position n - a + rr % a
         v = *reinterpret_cast<const u32x4*>(q + ((size_t)(base + j) * hq + h) * D + cc * 8);
       }
       *reinterpret_cast<u32x4*>(&qs[r * kStride + cc * 8]) = v;
     }
     if (tid < kRowChunk) {
       const int rr = r0 + tid;
-      if (rr < rows) {
-        const int h = g * G + rr / a, j = n - a + rr % a;
+      if (rr < rows && m - a + rr % a >= 0) {
+        const int h = g * G + rr / a, j = m - a + rr % a;
         lse2[tid] = lse[(size_t)h * total_tokens + base + j] * kLog2e;
-        jlim[tid] = j;
+        jlim[tid] = n - a + rr % a;                     // the row's prompt position: keys up to it count
       } else {
         lse2[tid] = 0.f;
         jlim[tid] = -1;                                 // padding row: masks every key
@@ -107,7 +111,7 @@ __global__ __launch_bounds__(kWaves * kWave) void window_score_kernel(
     __syncthreads();
   }
   acc_sum += wave_xor(acc_sum, 32);
-  if (half == 0 && key < n) S[(size_t)g * total_tokens + base + key] = acc_sum;
+  if (half == 0 && key < n) S[(size_t)g * total_k + kbase + key] = acc_sum;
 }
 
 }  // namespace
@@ -115,24 +119,39 @@ __global__ __launch_bounds__(kWaves * kWave) void window_score_kernel(
 
 using namespace kvs;
 
-extern "C" int kvs_window_score(const void* q, const void* k, const float* lse, const int32_t* cu_seqlens,
-                                int num_seqs, int total_tokens, int max_seqlen, int alpha, int hq, int hkv, int d,
-                                float scale, float* scores, void* stream) {
-  if (!q || !k || !lse || !cu_seqlens || !scores) return fail(KVS_E_INVAL, "kvs_window_score: NULL tensor");
-  if (num_seqs < 0 || total_tokens < 0 || max_seqlen < 0 || hq <= 0 || hkv <= 0 || hq % hkv || hq / hkv > 16 ||
-      (d != 64 && d != 128) || !(scale > 0.f))
-    return fail(KVS_E_INVAL, "kvs_window_score: bad shape (hq=%d hkv=%d d=%d)", hq, hkv, d);
-  if (alpha < 1) return fail(KVS_E_INVAL, "kvs_window_score: alpha must be >= 1");
-  if (num_seqs == 0 || max_seqlen == 0) return KVS_OK;
-  dim3 grid((max_seqlen + kKeysPerWG - 1) / kKeysPerWG, hkv, num_seqs);
+static int run_window(const char* name, const void* q, const void* k, const float* lse, const int32_t* cu_seqlens,
+                      const int32_t* cu_seqlens_k, int num_seqs, int total_tokens, int total_k, int max_seqlen_k,
+                      int alpha, int hq, int hkv, int d, float scale, float* scores, void* stream) {
+  if (!q || !k || !lse || !cu_seqlens || !scores) return fail(KVS_E_INVAL, "%s: NULL tensor", name);
+  if (num_seqs < 0 || total_tokens < 0 || total_k < 0 || max_seqlen_k < 0 || hq <= 0 || hkv <= 0 || hq % hkv ||
+      hq / hkv > 16 || (d != 64 && d != 128) || !(scale > 0.f))
+    return fail(KVS_E_INVAL, "%s: bad shape (hq=%d hkv=%d d=%d)", name, hq, hkv, d);
+  if (alpha < 1) return fail(KVS_E_INVAL, "%s: alpha must be >= 1", name);
+  if (num_seqs == 0 || max_seqlen_k == 0) return KVS_OK;
+  dim3 grid((max_seqlen_k + kKeysPerWG - 1) / kKeysPerWG, hkv, num_seqs);
   const float c = scale * kLog2e;
   auto* qq = static_cast<const uint16_t*>(q);
   auto* kk = static_cast<const uint16_t*>(k);
   if (d == 128)
     hipLaunchKernelGGL(window_score_kernel<128>, grid, dim3(kWaves * kWave), 0, as_stream(stream), qq, kk, lse,
-                       cu_seqlens, total_tokens, alpha, hq, hkv, c, scores);
+                       cu_seqlens, cu_seqlens_k, total_tokens, total_k, alpha, hq, hkv, c, scores);
   else
     hipLaunchKernelGGL(window_score_kernel<64>, grid, dim3(kWaves * kWave), 0, as_stream(stream), qq, kk, lse,
-                       cu_seqlens, total_tokens, alpha, hq, hkv, c, scores);
-  return launch_status("kvs_window_score");
+                       cu_seqlens, cu_seqlens_k, total_tokens, total_k, alpha, hq, hkv, c, scores);
+  return launch_status(name);
+}
+
+extern "C" int kvs_window_score(const void* q, const void* k, const float* lse, const int32_t* cu_seqlens,
+                                int num_seqs, int total_tokens, int max_seqlen, int alpha, int hq, int hkv, int d,
+                                float scale, float* scores, void* stream) {
+  return run_window("kvs_window_score", q, k, lse, cu_seqlens, nullptr, num_seqs, total_tokens, total_tokens,
+                    max_seqlen, alpha, hq, hkv, d, scale, scores, stream);
+}
+
+extern "C" int kvs_window_score_chunk(const void* q, const void* k, const float* lse, const int32_t* cu_seqlens_q,
+                                      const int32_t* cu_seqlens_k, int num_seqs, int total_q, int total_k, int max_k,
+                                      int alpha, int hq, int hkv, int d, float scale, float* scores, void* stream) {
+  if (!cu_seqlens_k) return fail(KVS_E_INVAL, "kvs_window_score_chunk: NULL tensor");
+  return run_window("kvs_window_score_chunk", q, k, lse, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k,
+                    max_k, alpha, hq, hkv, d, scale, scores, stream);
 }

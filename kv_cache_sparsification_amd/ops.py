@@ -288,3 +288,55 @@ def kvs_copy_blocks_fp8(k_pool, v_pool, k_scale, v_scale, src_dst_pairs, stream=
     _dev(src_dst_pairs, torch.int32, "src_dst_pairs")
     check(lib.kvs_copy_blocks_fp8(k_pool.data_ptr(), v_pool.data_ptr(), k_scale.data_ptr(), v_scale.data_ptr(), nb,
                                   hkv, d, src_dst_pairs.data_ptr(), src_dst_pairs.shape[0], _stream(stream)))
+
+
+# ---- chunked prefill and prefix reuse
+def kvs_prefill_attn_lse_chunk(q, k, v, cu_seqlens_q, cu_seqlens_k, max_q: int, max_k: int,
+                               scale: Optional[float] = None, o=None, lse=None, rowmax=None, ell=None, stream=None):
+    """Causal attention of chunks: q [Tq][Hq][d] holds each prompt's last m_s rows, k/v [Tk][Hkv][d]
+    all n_s tokens; returns (o [Tq][Hq][d], lse [Hq][Tq])."""
+    _dev(q, torch.bfloat16, "q"); _dev(k, torch.bfloat16, "k"); _dev(v, torch.bfloat16, "v")
+    _dev(cu_seqlens_q, torch.int32, "cu_seqlens_q"); _dev(cu_seqlens_k, torch.int32, "cu_seqlens_k")
+    Tq, hq, d = q.shape
+    hkv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if o is None else _dev(o, torch.bfloat16, "o")
+    lse = torch.empty(hq, Tq, device=q.device, dtype=torch.float32) if lse is None else _dev(lse, torch.float32, "lse")
+    for name, t in (("rowmax", rowmax), ("ell", ell)):
+        if t is not None:
+            _dev(t, torch.float32, name)
+    check(lib.kvs_prefill_attn_lse_chunk(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens_q.data_ptr(),
+                                         cu_seqlens_k.data_ptr(), cu_seqlens_q.numel() - 1, Tq, int(max_q),
+                                         int(max_k), hq, hkv, d, float(scale), o.data_ptr(), lse.data_ptr(),
+                                         _ptr(rowmax), _ptr(ell), _stream(stream)))
+    return o, lse
+
+
+def kvs_window_score_chunk(q, k, lse, cu_seqlens_q, cu_seqlens_k, max_k: int, alpha: int,
+                           scale: Optional[float] = None, scores=None, stream=None):
+    """Window score S [Hkv][Tk] when q/lse hold only each prompt's last rows (the window inside them)."""
+    _dev(q, torch.bfloat16, "q"); _dev(k, torch.bfloat16, "k"); _dev(lse, torch.float32, "lse")
+    _dev(cu_seqlens_q, torch.int32, "cu_seqlens_q"); _dev(cu_seqlens_k, torch.int32, "cu_seqlens_k")
+    Tq, hq, d = q.shape
+    Tk, hkv = k.shape[0], k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    scores = torch.empty(hkv, Tk, device=q.device, dtype=torch.float32) if scores is None else \
+        _dev(scores, torch.float32, "scores")
+    check(lib.kvs_window_score_chunk(q.data_ptr(), k.data_ptr(), lse.data_ptr(), cu_seqlens_q.data_ptr(),
+                                     cu_seqlens_k.data_ptr(), cu_seqlens_q.numel() - 1, Tq, Tk, int(max_k),
+                                     int(alpha), hq, hkv, d, float(scale), scores.data_ptr(), _stream(stream)))
+    return scores
+
+
+def kvs_gather_paged(k_pool, v_pool, block_tables, counts, dst_start, max_count: int, k_dst, v_dst, stream=None):
+    """Read tokens 0..counts[s]-1 of each sequence back from the pools into rows dst_start[s]+t."""
+    _dev(k_pool, torch.bfloat16, "k_pool"); _dev(v_pool, torch.bfloat16, "v_pool")
+    _dev(block_tables, torch.int32, "block_tables"); _dev(counts, torch.int32, "counts")
+    _dev(dst_start, torch.int32, "dst_start")
+    _dev(k_dst, torch.bfloat16, "k_dst"); _dev(v_dst, torch.bfloat16, "v_dst")
+    nb, hkv, _, d = k_pool.shape
+    check(lib.kvs_gather_paged(k_pool.data_ptr(), v_pool.data_ptr(), nb, block_tables.data_ptr(),
+                               block_tables.shape[1], counts.numel(), hkv, d, counts.data_ptr(), dst_start.data_ptr(),
+                               int(max_count), k_dst.data_ptr(), v_dst.data_ptr(), _stream(stream)))

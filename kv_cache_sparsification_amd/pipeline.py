@@ -77,3 +77,51 @@ def prefill_compress_layer(q, k, v, cu_seqlens, lengths: Sequence[int], alpha: i
 
 def default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
+
+
+def prefill_compress_layer_chunked(q, k, v, cu_q, cu_k, q_lengths: Sequence[int], k_lengths: Sequence[int],
+                                   alpha: int, k_budget: Optional[int], k_pool, v_pool, tables: List[List[int]],
+                                   max_blocks: int, cached: Optional[Sequence[int]] = None,
+                                   scale: Optional[float] = None, stream=None):
+    """One layer's step for prompts whose query rows are only their last q_lengths[s] rows (a
+    chunk, or everything after a reused prefix); k/v hold all k_lengths[s] tokens.
+
+    Compressed layers select over all n_s tokens and compact into `tables` from slot 0; a full
+    layer writes only rows cached[s] .. n_s-1 (the reused prefix keeps its shared blocks), from
+    slot cached[s].  Returns o, lse (chunk rows), scores, keep_idx, keep_offsets, tables_dev.
+    """
+    dev = q.device
+    max_q, max_k = max(q_lengths), max(k_lengths)
+    o, lse = ops.kvs_prefill_attn_lse_chunk(q, k, v, cu_q, cu_k, max_q, max_k, scale=scale, stream=stream)
+    tbl = torch.full((len(k_lengths), max_blocks), -1, dtype=torch.int32)
+    for i, t in enumerate(tables):
+        if len(t) > max_blocks:
+            raise ValueError("block table longer than max_blocks")
+        tbl[i, :len(t)] = torch.tensor(t, dtype=torch.int32)
+    tbl_dev = tbl.to(dev)
+    scores = keep_idx = None
+    if k_budget is None:
+        cached = [0] * len(k_lengths) if cached is None else list(cached)
+        kept = [n - c for n, c in zip(k_lengths, cached)]
+        # every head keeps rows cached[s] .. n_s-1, in order
+        keep = torch.cat([torch.arange(c, n, dtype=torch.int32).repeat(k.shape[1])
+                          for c, n in zip(cached, k_lengths)]).to(dev)
+        keep_off = [0]
+        for c in kept:
+            keep_off.append(keep_off[-1] + c)
+        keep_off_dev = torch.tensor(keep_off, dtype=torch.int32).to(dev)
+        ops.kvs_compact_paged(k, v, cu_k, keep, keep_off_dev, max(kept), k_pool, v_pool, tbl_dev,
+                              dst_slot_offset=torch.tensor(cached, dtype=torch.int32).to(dev), stream=stream)
+        keep_idx = keep
+    else:
+        kept = keep_counts(k_lengths, k_budget)
+        scores = ops.kvs_window_score_chunk(q, k, lse, cu_q, cu_k, max_k, alpha, scale=scale, stream=stream)
+        keep_off = [0]
+        for c in kept:
+            keep_off.append(keep_off[-1] + c)
+        keep_off_dev = torch.tensor(keep_off, dtype=torch.int32).to(dev)
+        keep_idx = ops.kvs_topk_select(scores, cu_k, max_k, alpha, k_budget, keep_off_dev, total_keep=keep_off[-1],
+                                       stream=stream)
+        ops.kvs_compact_paged(k, v, cu_k, keep_idx, keep_off_dev, max(kept), k_pool, v_pool, tbl_dev, stream=stream)
+    return dict(o=o, lse=lse, scores=scores, keep_idx=keep_idx, keep_offsets=keep_off_dev, kept=kept,
+                tables_dev=tbl_dev)

@@ -191,3 +191,24 @@ def test_fp8_calls_validate_on_the_host():
     assert decode(B=0) == 0
     assert L.kvs_copy_blocks_fp8(fake, fake, None, fake, 8, 2, 128, fake, 1, None) == -1
     assert L.kvs_copy_blocks_fp8(fake, fake, fake, fake, 8, 2, 128, None, 0, None) == 0
+
+
+def test_chunk_and_gather_calls_validate_on_the_host():
+    L = kvs.lib
+    fake = 0x1000   # never dereferenced: the checks fail first
+    # chunk prefill: key offsets required, max_k >= max_q
+    assert L.kvs_prefill_attn_lse_chunk(fake, fake, fake, fake, None, 1, 10, 10, 20, 8, 2, 128, 0.1, fake, fake,
+                                        None, None, None) == -1
+    assert L.kvs_prefill_attn_lse_chunk(fake, fake, fake, fake, fake, 1, 10, 30, 20, 8, 2, 128, 0.1, fake, fake,
+                                        None, None, None) == -1 and b"max_k" in L.kvs_last_error()
+    assert L.kvs_prefill_attn_lse_chunk(fake, fake, fake, fake, fake, 1, 10, 10, 20, 8, 3, 128, 0.1, fake, fake,
+                                        None, None, None) == -1     # hq % hkv
+    assert L.kvs_prefill_attn_lse_chunk(fake, fake, fake, fake, fake, 0, 0, 0, 0, 8, 2, 128, 0.1, fake, fake,
+                                        None, None, None) == 0
+    # window score on chunks
+    assert L.kvs_window_score_chunk(fake, fake, fake, fake, None, 1, 10, 20, 20, 4, 8, 2, 128, 0.1, fake, None) == -1
+    assert L.kvs_window_score_chunk(fake, fake, fake, fake, fake, 1, 10, 20, 20, 0, 8, 2, 128, 0.1, fake, None) == -1
+    # gather
+    assert L.kvs_gather_paged(fake, fake, 8, fake, 4, 1, 2, 96, fake, fake, 16, fake, fake, None) == -1
+    assert L.kvs_gather_paged(fake, fake, 8, fake, 4, 1, 2, 128, None, fake, 16, fake, fake, None) == -1
+    assert L.kvs_gather_paged(fake, fake, 8, fake, 4, 1, 2, 128, fake, fake, 0, fake, fake, None) == 0

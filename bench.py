@@ -271,6 +271,9 @@ def main():
     line["decode_at_scale"] = decode_at_scale(kvs, torch, wl, 100)
     line["fp8_decode_at_scale"] = decode_at_scale(kvs, torch, wl, 100, fp8=True)
     line["fp8_layer"] = fp8_layer(kvs, torch, wl, w, k, v, cu_d, keep, keep_off, steps_dec)
+    line["prefix_reuse"] = prefix_reuse(kvs, torch, wl, w, q, k, v)
+    line["decode_32_layers"] = decode_32_layers(kvs, torch, wl, 10)
+    line["fp8_decode_32_layers"] = decode_32_layers(kvs, torch, wl, 10, fp8=True)
     # the prefill-side pass of the last step left the compressed cache in the pools
     kvs.kvs_compact_paged(k, v, cu_d, keep, keep_off, k_eff, k_pool, v_pool, tbl)
     line["decode_evict"] = decode_evict(kvs, torch, wl, w, k_pool, v_pool, tbl, S, cu_d, keep, keep_off, 200)
@@ -408,6 +411,134 @@ def fp8_layer(kvs, torch, wl, w, k, v, cu_d, keep, keep_off, steps):
             "decode_us_per_step": round(us, 3), "decode_tok_s": round(1.0 / (us * 1e-6), 1),
             "decode_algorithmic_bytes_per_step": int(nbytes),
             "decode_GBs": round(nbytes / (us * 1e-6) / 1e9, 1)}
+
+
+def decode_32_layers(kvs, torch, wl, steps, fp8=False):
+    """One decode step of a whole 32-layer model's attention (the concurrency-20 workload: 20
+    prompts of 1000-4000 tokens, layers 0-2 full, 3-31 at k=512), each layer with its own pools
+    and tables, `steps` steps captured as one HIP graph and also launched eagerly."""
+    import numpy as np
+    w = wl.WORKLOADS[3]
+    B, hq, hkv, d = w.num_seqs, w.hq, w.hkv, w.d
+    lengths = w.seq_lengths()
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(3232)
+    layers = []
+    for layer in range(w.n_layers):
+        k_l = w.budgets[layer]
+        ctx0 = [n if k_l is None else min(k_l, n) for n in lengths]
+        max_ctx = max(ctx0) + steps
+        nbs = [-(-(c + steps) // 16) for c in ctx0]
+        nb_total = sum(nbs)
+        if fp8:
+            pools = kvs.new_pools_fp8(nb_total, hkv, d, device=dev)
+            for t in pools[:2]:
+                t.copy_(torch.randint(0, 0x7F, t.shape, generator=gen, device=dev, dtype=torch.uint8))
+            for t in pools[2:]:
+                t.copy_(torch.rand(t.shape, generator=gen, device=dev) * 0.01 + 0.002)
+        else:
+            pools = kvs.new_pools(nb_total, hkv, d, device=dev)
+            for t in pools:
+                t.copy_(torch.randn(t.shape, generator=gen, device=dev).to(torch.bfloat16))
+        max_blocks = max(nbs)
+        tbl = np.full((B, max_blocks), -1, np.int32)
+        perm = np.random.default_rng(layer).permutation(nb_total).astype(np.int32)
+        used = 0
+        for s_, nb in enumerate(nbs):
+            tbl[s_, :nb] = perm[used:used + nb]
+            used += nb
+        lens = torch.tensor([[c + st + 1 for c in ctx0] for st in range(steps)], dtype=torch.int32, device=dev)
+        ws = torch.empty(max(kvs.kvs_paged_decode_workspace_size(B, hq, hkv, d, max_ctx), 1), dtype=torch.uint8,
+                         device=dev)
+        layers.append((pools, torch.from_numpy(tbl).to(dev), lens, max_ctx, ws))
+    qs = torch.randn(steps, B, hq, d, generator=gen, device=dev).to(torch.bfloat16)
+    nks = torch.randn(steps, B, hkv, d, generator=gen, device=dev).to(torch.bfloat16)
+    nvs = torch.randn(steps, B, hkv, d, generator=gen, device=dev).to(torch.bfloat16)
+    od = torch.empty(w.n_layers, B, hq, d, dtype=torch.bfloat16, device=dev)
+    decode = kvs.kvs_paged_decode_fp8 if fp8 else kvs.kvs_paged_decode
+
+    def run():
+        for st in range(steps):
+            for li, (pools, tbl, lens, max_ctx, ws) in enumerate(layers):
+                decode(qs[st], *pools, tbl, lens[st], max_ctx, new_k=nks[st], new_v=nvs[st], o=od[li], workspace=ws)
+
+    graph_us = _graph_time_us(torch, run, steps)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    eager_us = e0.elapsed_time(e1) * 1e3 / steps
+    cached = sum(sum(n if k_l is None else min(k_l, n) for n in lengths) for k_l in w.budgets)
+    return {"workload": f"{B} sequences x {min(lengths)}-{max(lengths)} prompt tokens, {w.n_layers} layers "
+                        f"(3 full, 29 at k=512), {hq}q/{hkv}kv heads, d={d}: one decode step of every layer"
+                        + (", 8-bit E4M3 cache" if fp8 else ""),
+            "graph_us_per_step": round(graph_us, 2), "eager_us_per_step": round(eager_us, 2),
+            "launches_per_step": sum(2 if kvs.kvs_paged_decode_workspace_size(B, hq, hkv, d, l[3]) else 1
+                                     for l in layers),
+            "cached_tokens_per_head": cached,
+            "tok_s": round(B / (graph_us * 1e-6), 1)}
+
+
+def prefix_reuse(kvs, torch, wl, w, q, k, v, reps=10):
+    """The bench layer when the first 2048 prompt tokens are found in the cache (block-hash
+    match): their K/V come back from the blocks (gather) and only rows 2048-3999 are prefilled
+    against all 4000 keys, then window score, top-k and compaction as usual.  Per-launch HIP
+    event times against the whole-prompt step."""
+    dev = torch.device("cuda:0")
+    n, hq, hkv, d, alpha, kb = w.fixed_len, w.hq, w.hkv, w.d, w.alpha, w.budgets[0]
+    P = 2048
+    nblk_p = P // 16
+    k_pool, v_pool = kvs.new_pools(nblk_p + 32, hkv, d, device=dev)
+    tbl_p = torch.arange(nblk_p, dtype=torch.int32, device=dev).reshape(1, nblk_p)
+    cu_full = torch.tensor([0, n], dtype=torch.int32, device=dev)
+    kvs.kvs_compact_paged(k, v, torch.tensor([0, P], dtype=torch.int32, device=dev), None, None, P, k_pool, v_pool,
+                          tbl_p)
+    k_all = torch.empty_like(k)
+    v_all = torch.empty_like(v)
+    k_all[P:] = k[P:]
+    v_all[P:] = v[P:]
+    q_rows = q[P:].contiguous()
+    cu_q = torch.tensor([0, n - P], dtype=torch.int32, device=dev)
+    k_eff = min(kb, n)
+    keep_off = torch.tensor([0, k_eff], dtype=torch.int32, device=dev)
+    ctbl = torch.arange(nblk_p, nblk_p + (-(-k_eff // 16)), dtype=torch.int32, device=dev).reshape(1, -1)
+    counts = torch.tensor([P], dtype=torch.int32, device=dev)
+    start = torch.tensor([0], dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    marks = ["gather", "prefill_chunk", "window", "topk", "compact"]
+
+    def step(ev):
+        ev[0].record(stream)
+        kvs.kvs_gather_paged(k_pool, v_pool, tbl_p, counts, start, P, k_all, v_all)
+        ev[1].record(stream)
+        o, lse = kvs.kvs_prefill_attn_lse_chunk(q_rows, k_all, v_all, cu_q, cu_full, n - P, n)
+        ev[2].record(stream)
+        S = kvs.kvs_window_score_chunk(q_rows, k_all, lse, cu_q, cu_full, n, alpha)
+        ev[3].record(stream)
+        keep = kvs.kvs_topk_select(S, cu_full, n, alpha, kb, keep_off, total_keep=k_eff)
+        ev[4].record(stream)
+        kvs.kvs_compact_paged(k_all, v_all, cu_full, keep, keep_off, k_eff, k_pool, v_pool, ctbl)
+        ev[5].record(stream)
+
+    warm = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    step(warm)
+    runs = []
+    for _ in range(reps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        step(ev)
+        runs.append(ev)
+    torch.cuda.synchronize()
+    per = {m: sum(r[i].elapsed_time(r[i + 1]) for r in runs) * 1e3 / reps for i, m in enumerate(marks)}
+    total = sum(per.values())
+    flops = 2.0 * d * hq * sum(2 * (i + 1) for i in range(P, n))
+    return {"workload": f"bench layer n={n} with the first {P} tokens reused from the cache: gather, prefill of "
+                        f"rows {P}-{n - 1} against {n} keys, window score, top-k, compaction",
+            "us": {m: round(v_, 2) for m, v_ in per.items()}, "total_us": round(total, 2),
+            "prefill_chunk_TFLOPs": round(flops / (per["prefill_chunk"] * 1e-6) / 1e12, 1),
+            "prompt_tok_s": round(n / (total * 1e-6), 1)}
+
 
 
 def decode_evict(kvs, torch, wl, w, k_pool, v_pool, tbl, S, cu_d, keep, keep_off, steps):

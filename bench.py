@@ -50,6 +50,9 @@ def parse():
     p.add_argument("--decode-mode", choices=("graph", "loop"), default="graph",
                    help="graph: the 500 decode steps replay as one captured HIP graph (the launch mode of the "
                         "pages' serving system); loop: one host launch per step")
+    p.add_argument("--sections", default="all",
+                   help="comma list of the reports to add after the timed step: scale, fp8, prefix, layers32, "
+                        "evict (default all); the timed step and its roofline always run")
     return p.parse_args()
 
 
@@ -268,15 +271,22 @@ def main():
         "kernel_share_ms_per_step": {kk: round(vv, 4) for kk, vv in per_step_ms.items()},
     }
 
-    line["decode_at_scale"] = decode_at_scale(kvs, torch, wl, 100)
-    line["fp8_decode_at_scale"] = decode_at_scale(kvs, torch, wl, 100, fp8=True)
-    line["fp8_layer"] = fp8_layer(kvs, torch, wl, w, k, v, cu_d, keep, keep_off, steps_dec)
-    line["prefix_reuse"] = prefix_reuse(kvs, torch, wl, w, q, k, v)
-    line["decode_32_layers"] = decode_32_layers(kvs, torch, wl, 10)
-    line["fp8_decode_32_layers"] = decode_32_layers(kvs, torch, wl, 10, fp8=True)
-    # the prefill-side pass of the last step left the compressed cache in the pools
-    kvs.kvs_compact_paged(k, v, cu_d, keep, keep_off, k_eff, k_pool, v_pool, tbl)
-    line["decode_evict"] = decode_evict(kvs, torch, wl, w, k_pool, v_pool, tbl, S, cu_d, keep, keep_off, 200)
+    sections = {"scale", "fp8", "prefix", "layers32", "evict"} if args.sections == "all" else \
+        set(x.strip() for x in args.sections.split(",") if x.strip())
+    if "scale" in sections:
+        line["decode_at_scale"] = decode_at_scale(kvs, torch, wl, 100)
+    if "fp8" in sections:
+        line["fp8_decode_at_scale"] = decode_at_scale(kvs, torch, wl, 100, fp8=True)
+        line["fp8_layer"] = fp8_layer(kvs, torch, wl, w, k, v, cu_d, keep, keep_off, steps_dec)
+    if "prefix" in sections:
+        line["prefix_reuse"] = prefix_reuse(kvs, torch, wl, w, q, k, v)
+    if "layers32" in sections:
+        line["decode_32_layers"] = decode_32_layers(kvs, torch, wl, 10)
+        line["fp8_decode_32_layers"] = decode_32_layers(kvs, torch, wl, 10, fp8=True)
+    if "evict" in sections:
+        # the prefill-side pass of the last step left the compressed cache in the pools
+        kvs.kvs_compact_paged(k, v, cu_d, keep, keep_off, k_eff, k_pool, v_pool, tbl)
+        line["decode_evict"] = decode_evict(kvs, torch, wl, w, k_pool, v_pool, tbl, S, cu_d, keep, keep_off, 200)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, qb, kbits, vb, dec, args.cpu_budget_s)
     print(json.dumps(line), flush=True)

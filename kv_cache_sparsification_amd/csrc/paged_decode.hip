@@ -35,6 +35,8 @@ constexpr int kCUs = 256;
 constexpr int kTargetWGs = 2048;
 constexpr int kMaxSplitsMerge = 256;
 constexpr int kBandwidthBlocks = 4096;   // (sequence, KV head, block) triples per call
+constexpr int kManyBlocks = 16384;
+constexpr int kNoSplitBlocks = 64;       // blocks one 8-wavefront workgroup walks without a split
 constexpr float kLazy = 8.f;             // log2 headroom before the reference max moves
 
 struct Plan {
@@ -52,7 +54,7 @@ struct Plan {
 // Measured on MI355X for one 8B layer (1 sequence, 8 KV heads, 400..900 cached tokens, graph
 // replay): 4 blocks per split 9.0 us per step, 8: 9.6, 16: 11.2, 32: 13.4, one workgroup per
 // pair: 11.7 - a single sequence's cache is read fastest by many CUs at once.
-inline Plan choose_plan(int batch, int hq, int hkv, int d, int max_ctx) {
+inline Plan choose_plan(int batch, int hq, int hkv, int d, int max_ctx, bool f8) {
   const int G = hq / hkv;
   const int nblk = (max_ctx + kBlock - 1) / kBlock;
   const int units = batch * hkv;
@@ -69,14 +71,32 @@ inline Plan choose_plan(int batch, int hq, int hkv, int d, int max_ctx) {
     p.splits = 1;
     return p;
   }
+  // Short contexts in a batch wide enough for 1024+ wavefronts: one 8-wavefront workgroup per
+  // pair walks its blocks in a few rounds, and the merge launch is saved (20 sequences x 8 KV
+  // heads x 528 tokens: 10.8 us per step, against 15.2-22 us for any split plan).
+  if (nblk <= kNoSplitBlocks && units * 8 >= 4 * kCUs) {
+    p.waves = 8;
+    p.nb = 2;
+    p.bps = nblk;
+    p.splits = 1;
+    return p;
+  }
   p.waves = 4;
   const int want = (kTargetWGs + units - 1) / units;
   int bps = (nblk + want - 1) / want;
   if (bps < p.waves) bps = p.waves;
-  // Enough blocks overall for the read volume to set the time: eight wavefronts of two blocks
-  // in flight, two rounds each (8 KV heads x 3000+ tokens, batch 4, per step: 4 waves x 4
-  // blocks x 1 round 15.2 us, 8 x 4 x 1 14.4, 8 x 2 x 2 13.7, 8 x 2 x 3 15.1, 8 x 2 x 4 18.0).
-  if (units * nblk >= kBandwidthBlocks) {
+  const int total = units * nblk;
+  if (total >= kManyBlocks) {
+    // Read volume far beyond one wave generation: four wavefronts of two blocks, one round
+    // each, many generations (20 x 8 heads x 1100-3900 tokens: 41.5 us per step, against
+    // 50.7 at 8 x 2 x 2 rounds); the 8-bit cache, half the bytes per block, keeps four blocks
+    // in flight for two rounds (43.8 us against 48.3).
+    p.nb = f8 ? 4 : 2;
+    bps = f8 ? 2 * p.waves * p.nb : p.waves * p.nb;
+  } else if (total >= kBandwidthBlocks) {
+    // Enough blocks for the read volume to set the time: eight wavefronts of two blocks in
+    // flight, two rounds each (8 KV heads x 3000+ tokens, batch 4, per step: 4 waves x 4
+    // blocks x 1 round 15.2 us, 8 x 4 x 1 14.4, 8 x 2 x 2 13.7, 8 x 2 x 3 15.1, 8 x 2 x 4 18.0).
     p.waves = 8;
     p.nb = 2;
     if (bps < 2 * p.waves * p.nb) bps = 2 * p.waves * p.nb;
@@ -567,9 +587,11 @@ using namespace kvs;
 // Workspace: partials [batch][hq][splits][d + 2] fp32 = (max, sum, unnormalised output).
 extern "C" size_t kvs_paged_decode_workspace_size(int batch, int hq, int hkv, int d, int max_ctx) {
   if (batch <= 0 || hq <= 0 || hkv <= 0 || hq % hkv || max_ctx <= 0 || d <= 0) return 0;
-  const Plan p = choose_plan(batch, hq, hkv, d, max_ctx);
-  if (p.splits <= 1) return 0;
-  return (size_t)batch * hq * p.splits * (d + 2) * sizeof(float);
+  // the 16- and 8-bit caches may split differently: room for either
+  const Plan p = choose_plan(batch, hq, hkv, d, max_ctx, false), p8 = choose_plan(batch, hq, hkv, d, max_ctx, true);
+  const int splits = p.splits > p8.splits ? p.splits : p8.splits;
+  if (splits <= 1) return 0;
+  return (size_t)batch * hq * splits * (d + 2) * sizeof(float);
 }
 
 template <int D, int W, int NB, bool F8>
@@ -598,7 +620,10 @@ static void launch_decode(const Plan& p, dim3 grid, size_t lds, hipStream_t st, 
       launch_one<D, 4, 2, F8>(p, grid, lds, st, q, kp, vp, num_blocks, tables, max_blocks, ctx, hq, hkv, c, nk, nv, o,
                               lse, ws, ex);
   } else {
-    if (p.waves == 8)
+    if (p.waves == 4 && p.nb == 2)
+      launch_one<D, 4, 2, F8>(p, grid, lds, st, q, kp, vp, num_blocks, tables, max_blocks, ctx, hq, hkv, c, nk, nv, o,
+                              lse, ws, ex);
+    else if (p.waves == 8)
       launch_one<D, 8, 4, F8>(p, grid, lds, st, q, kp, vp, num_blocks, tables, max_blocks, ctx, hq, hkv, c, nk, nv, o,
                               lse, ws, ex);
     else
@@ -622,7 +647,7 @@ static int run_decode(const char* name, const void* q, void* k_pool, void* v_poo
                 max_ctx);
   if ((long long)max_blocks * kBlock < max_ctx) return fail(KVS_E_INVAL, "%s: max_blocks*16 < max_ctx", name);
   if (batch == 0) return KVS_OK;
-  Plan p = choose_plan(batch, hq, hkv, d, max_ctx);
+  Plan p = choose_plan(batch, hq, hkv, d, max_ctx, f8);
   if (f8 && p.waves == 16) p.waves = 8;   // one workgroup per pair: the 8-bit path's registers fit 8 wavefronts
   const size_t need = kvs_paged_decode_workspace_size(batch, hq, hkv, d, max_ctx);
   if (need > 0 && (!workspace || workspace_bytes < need))
@@ -691,7 +716,7 @@ static size_t scored_logits_offset(int batch, int hq, int splits, int d) {
 
 extern "C" size_t kvs_paged_decode_scored_workspace_size(int batch, int hq, int hkv, int d, int max_ctx) {
   if (batch <= 0 || hq <= 0 || hkv <= 0 || hq % hkv || max_ctx <= 0 || d <= 0) return 0;
-  const Plan p = choose_plan(batch, hq, hkv, d, max_ctx);
+  const Plan p = choose_plan(batch, hq, hkv, d, max_ctx, false);
   return scored_logits_offset(batch, hq, p.splits, d) + (size_t)batch * hq * max_ctx * sizeof(float);
 }
 
@@ -713,7 +738,7 @@ extern "C" int kvs_paged_decode_scored(const void* q, void* k_pool, void* v_pool
   if ((long long)max_blocks * kBlock < max_ctx)
     return fail(KVS_E_INVAL, "kvs_paged_decode_scored: max_blocks*16 < max_ctx");
   if (batch == 0) return KVS_OK;
-  const Plan p = choose_plan(batch, hq, hkv, d, max_ctx);
+  const Plan p = choose_plan(batch, hq, hkv, d, max_ctx, false);
   const size_t need = kvs_paged_decode_scored_workspace_size(batch, hq, hkv, d, max_ctx);
   if (!workspace || workspace_bytes < need)
     return fail(KVS_E_INVAL, "kvs_paged_decode_scored: workspace of %zu bytes needed, %zu given", need,

@@ -1,0 +1,128 @@
+"""A multi-layer decode step captured as one HIP graph (next row f4) gives the eager results on
+every replay, with the program's own eager work and synchronisations between replays; the
+eager results themselves match the fp64 oracle.
+
+Three layers of different shapes (a full layer of ragged contexts, a compressed layer, an
+8-bit compressed layer) and four batched decode steps with append per replay.  Appends are
+idempotent across replays (the same tokens go to the same slots), so every replay must
+reproduce the eager outputs bit for bit.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import fp8 as ofp8
+import workloads as wl
+from tests._parity import bf16_to_f64, i32, assert_rows_close
+
+pytestmark = pytest.mark.gpu
+
+kvs = pytest.importorskip("kv_cache_sparsification_amd")
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+
+
+def _layer(rng, lengths, hkv, d, steps, fp8):
+    nbs = [-(-(n + steps) // 16) for n in lengths]
+    nb = sum(nbs) + 2
+    perm = rng.permutation(nb)
+    tables = np.full((len(lengths), max(nbs)), -1, np.int32)
+    used = 0
+    for s, c in enumerate(nbs):
+        tables[s, :c] = perm[used:used + c]
+        used += c
+    T = sum(lengths)
+    kb = wl.f32_to_bf16_bits(rng.standard_normal((T, hkv, d), dtype=np.float32))
+    vb = wl.f32_to_bf16_bits(rng.standard_normal((T, hkv, d), dtype=np.float32))
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    up = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).cuda()
+    if fp8:
+        pools = kvs.new_pools_fp8(nb, hkv, d)
+        kvs.kvs_compact_paged_fp8(up(kb), up(vb), i32(cu), None, None, max(lengths), *pools, i32(tables))
+    else:
+        pools = kvs.new_pools(nb, hkv, d)
+        kvs.kvs_compact_paged(up(kb), up(vb), i32(cu), None, None, max(lengths), *pools, i32(tables))
+    return dict(pools=pools, tables=tables, tbl=i32(tables), lengths=list(lengths), fp8=fp8, kb=kb, vb=vb, cu=cu,
+                max_ctx=max(lengths) + steps)
+
+
+def test_decode_graph_replays_match_eager_and_oracle():
+    _say("three-layer decode step as a HIP graph, 4 steps, 5 replays")
+    rng = np.random.default_rng(21)
+    B, hq, hkv, d, steps = 6, 32, 8, 128, 4
+    full_lens = [int(x) for x in rng.integers(300, 1500, B)]
+    layers = [_layer(rng, full_lens, hkv, d, steps, False),
+              _layer(rng, [min(256, n) for n in full_lens], hkv, d, steps, False),
+              _layer(rng, [min(256, n) for n in full_lens], hkv, d, steps, True)]
+    q = torch.from_numpy(rng.standard_normal((steps, B, hq, d), dtype=np.float32)).to(torch.bfloat16).cuda()
+    nk = torch.from_numpy(rng.standard_normal((steps, B, hkv, d), dtype=np.float32)).to(torch.bfloat16).cuda()
+    nv = torch.from_numpy(rng.standard_normal((steps, B, hkv, d), dtype=np.float32)).to(torch.bfloat16).cuda()
+    for L in layers:
+        L["lens"] = i32([[n + st + 1 for n in L["lengths"]] for st in range(steps)])
+        L["ws"] = torch.empty(max(kvs.kvs_paged_decode_workspace_size(B, hq, hkv, d, L["max_ctx"]), 1),
+                              dtype=torch.uint8, device="cuda")
+        L["out"] = torch.empty(steps, B, hq, d, dtype=torch.bfloat16, device="cuda")
+
+    def run():
+        for st in range(steps):
+            for L in layers:
+                fn = kvs.kvs_paged_decode_fp8 if L["fp8"] else kvs.kvs_paged_decode
+                fn(q[st], *L["pools"], L["tbl"], L["lens"][st], L["max_ctx"], new_k=nk[st], new_v=nv[st],
+                   o=L["out"][st], workspace=L["ws"])
+
+    run()                                   # eager
+    torch.cuda.synchronize()
+    eager = [L["out"].clone() for L in layers]
+
+    # the eager results against the oracle (last step, every sequence)
+    qf = bf16_to_f64(q[steps - 1])
+    for li, L in enumerate(layers):
+        for s in range(B):
+            n = L["lengths"][s]
+            rows_k = wl.bf16_bits_to_f64(L["kb"][L["cu"][s]:L["cu"][s + 1]])
+            rows_v = wl.bf16_bits_to_f64(L["vb"][L["cu"][s]:L["cu"][s + 1]])
+            new_k = bf16_to_f64(nk[:, s])
+            new_v = bf16_to_f64(nv[:, s])
+            if L["fp8"]:
+                rows_k = ofp8.dequantize_rows(*ofp8.quantize_rows(rows_k))
+                rows_v = ofp8.dequantize_rows(*ofp8.quantize_rows(rows_v))
+                new_k = ofp8.dequantize_rows(*ofp8.quantize_rows(new_k))
+                new_v = ofp8.dequantize_rows(*ofp8.quantize_rows(new_v))
+            kc = np.concatenate([rows_k, new_k])
+            vc = np.concatenate([rows_v, new_v])
+            o_ref, _ = oracle.decode_attention(qf[s], kc, vc)
+            assert_rows_close(bf16_to_f64(eager[li][steps - 1, s]), o_ref, what=f"layer {li} seq {s}")
+
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        run()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    for rep in range(5):
+        for L in layers:
+            L["out"].zero_()               # eager work between replays
+        scratch = torch.randn(1 << 20, device="cuda").sum()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for li, L in enumerate(layers):
+            assert torch.equal(L["out"].view(torch.int16), eager[li].view(torch.int16)), f"replay {rep} layer {li}"
+        del scratch

@@ -246,3 +246,53 @@ def test_fp8_decode_wide_batch():
     """64 short sequences: one workgroup per (sequence, KV head), no split."""
     rng = np.random.default_rng(4)
     _decode_case("wide batch", 32, 8, 128, list(rng.integers(1, 60, 64)), 3, seed=4, prompt_extra=8)
+
+
+@pytest.mark.parametrize("B,lo,hi", [(20, 400, 700), (16, 2000, 2300)])
+def test_fp8_decode_wide_batch_plans(B, lo, hi):
+    """Wide batches in the plans without a split (short contexts, one workgroup per sequence
+    and head) and with many one-round splits (long contexts): outputs and LSE against the
+    oracle attending over the quantized rows, two steps with append."""
+    _say(f"fp8 decode wide batch B={B} lengths {lo}..{hi}")
+    rng = np.random.default_rng(B)
+    hq, hkv, d, steps = 32, 8, 128, 2
+    lengths = [int(x) for x in rng.integers(lo, hi, B)]
+    T = sum(lengths)
+    kb = wl.f32_to_bf16_bits(rng.standard_normal((T, hkv, d), dtype=np.float32))
+    vb = wl.f32_to_bf16_bits(rng.standard_normal((T, hkv, d), dtype=np.float32))
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    max_ctx = max(lengths) + steps
+    nbs = [-(-(n + steps) // 16) for n in lengths]
+    nb = sum(nbs)
+    perm = rng.permutation(nb)
+    tables = np.full((B, max(nbs)), -1, np.int32)
+    used = 0
+    for s, c in enumerate(nbs):
+        tables[s, :c] = perm[used:used + c]
+        used += c
+    pools = kvs.new_pools_fp8(nb, hkv, d)
+    tbl = i32(tables)
+    kvs.kvs_compact_paged_fp8(to_dev_bf16(kb), to_dev_bf16(vb), i32(cu), None, None, max(lengths), *pools, tbl)
+    kq = ofp8.dequantize_rows(*ofp8.quantize_rows(wl.bf16_bits_to_f64(kb)))   # the cached values
+    vq = ofp8.dequantize_rows(*ofp8.quantize_rows(wl.bf16_bits_to_f64(vb)))
+    ws_bytes = kvs.kvs_paged_decode_workspace_size(B, hq, hkv, d, max_ctx)
+    ws = torch.empty(max(ws_bytes, 1), device="cuda", dtype=torch.uint8)
+    new_k, new_v = [[] for _ in range(B)], [[] for _ in range(B)]
+    for step in range(steps):
+        L = np.array(lengths) + step + 1
+        q = wl.f32_to_bf16_bits(rng.standard_normal((B, hq, d), dtype=np.float32))
+        nk = wl.f32_to_bf16_bits(rng.standard_normal((B, hkv, d), dtype=np.float32))
+        nv = wl.f32_to_bf16_bits(rng.standard_normal((B, hkv, d), dtype=np.float32))
+        lse = torch.empty(B, hq, device="cuda", dtype=torch.float32)
+        o = kvs.kvs_paged_decode_fp8(to_dev_bf16(q), *pools, tbl, i32(L), max_ctx, new_k=to_dev_bf16(nk),
+                                     new_v=to_dev_bf16(nv), lse=lse, workspace=ws)
+        og, lg = bf16_to_f64(o), lse.cpu().numpy()
+        qf = wl.bf16_bits_to_f64(q)
+        for s in range(B):
+            new_k[s].append(ofp8.dequantize_rows(*ofp8.quantize_rows(wl.bf16_bits_to_f64(nk[s]))))
+            new_v[s].append(ofp8.dequantize_rows(*ofp8.quantize_rows(wl.bf16_bits_to_f64(nv[s]))))
+            kc = np.concatenate([kq[cu[s]:cu[s + 1]], np.stack(new_k[s])])
+            vc = np.concatenate([vq[cu[s]:cu[s + 1]], np.stack(new_v[s])])
+            o_ref, l_ref = oracle.decode_attention(qf[s], kc, vc)
+            assert_rows_close(og[s], o_ref, what=f"wide batch step {step} seq {s}")
+            assert_lse_close(lg[s], l_ref, what=f"wide batch step {step} seq {s}")

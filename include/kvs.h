@@ -318,6 +318,18 @@ int kvs_paged_decode_fp8(const void* q, void* k_pool, void* v_pool, float* k_sca
                          float* lse_opt, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kvs_paged_decode_scored_fp8 - kvs_paged_decode_scored over an 8-bit cache: the new token
+ * is quantized into its chosen slot, the logits and scores use the slots' values code *
+ * scale.  Workspace: kvs_paged_decode_scored_workspace_size(...) bytes.  Errors as
+ * kvs_paged_decode_scored; KVS_E_INVAL also for a NULL scale array.
+ */
+int kvs_paged_decode_scored_fp8(const void* q, void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                                int num_blocks, const int32_t* block_tables, int max_blocks, const int32_t* ctx_lens,
+                                int batch, int max_ctx, int hq, int hkv, int d, float scale, const void* new_k,
+                                const void* new_v, const int32_t* dst_slots, float* slot_scores, int slot_stride,
+                                void* o, float* lse_opt, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * kvs_copy_blocks_fp8 - kvs_copy_blocks for an 8-bit cache: code blocks and scale rows.
  */
 int kvs_copy_blocks_fp8(void* k_pool, void* v_pool, float* k_scale, float* v_scale, int num_blocks, int hkv, int d,

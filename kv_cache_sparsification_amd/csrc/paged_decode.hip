@@ -720,50 +720,54 @@ extern "C" size_t kvs_paged_decode_scored_workspace_size(int batch, int hq, int 
   return scored_logits_offset(batch, hq, p.splits, d) + (size_t)batch * hq * max_ctx * sizeof(float);
 }
 
-extern "C" int kvs_paged_decode_scored(const void* q, void* k_pool, void* v_pool, int num_blocks,
-                                       const int32_t* block_tables, int max_blocks, const int32_t* ctx_lens, int batch,
-                                       int max_ctx, int hq, int hkv, int d, float scale, const void* new_k,
-                                       const void* new_v, const int32_t* dst_slots, float* slot_scores,
-                                       int slot_stride, void* o, float* lse_opt, void* workspace,
-                                       size_t workspace_bytes, void* stream) {
-  if (!q || !k_pool || !v_pool || !block_tables || !ctx_lens || !o || !slot_scores)
-    return fail(KVS_E_INVAL, "kvs_paged_decode_scored: NULL tensor");
-  if ((new_k == nullptr) != (new_v == nullptr))
-    return fail(KVS_E_INVAL, "kvs_paged_decode_scored: new_k and new_v go together");
-  if (dst_slots && !new_k) return fail(KVS_E_INVAL, "kvs_paged_decode_scored: dst_slots without a new token");
+static int run_scored(const char* name, const void* q, void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                      bool f8, int num_blocks, const int32_t* block_tables, int max_blocks, const int32_t* ctx_lens,
+                      int batch, int max_ctx, int hq, int hkv, int d, float scale, const void* new_k,
+                      const void* new_v, const int32_t* dst_slots, float* slot_scores, int slot_stride, void* o,
+                      float* lse_opt, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k_pool || !v_pool || !block_tables || !ctx_lens || !o || !slot_scores || (f8 && (!k_scale || !v_scale)))
+    return fail(KVS_E_INVAL, "%s: NULL tensor", name);
+  if ((new_k == nullptr) != (new_v == nullptr)) return fail(KVS_E_INVAL, "%s: new_k and new_v go together", name);
+  if (dst_slots && !new_k) return fail(KVS_E_INVAL, "%s: dst_slots without a new token", name);
   if (batch < 0 || max_ctx < 1 || hq <= 0 || hkv <= 0 || hq % hkv || hq / hkv > 16 || (d != 64 && d != 128) ||
       num_blocks <= 0 || max_blocks <= 0 || !(scale > 0.f) || slot_stride < max_ctx)
-    return fail(KVS_E_INVAL, "kvs_paged_decode_scored: bad shape (batch=%d hq=%d hkv=%d d=%d max_ctx=%d stride=%d)",
-                batch, hq, hkv, d, max_ctx, slot_stride);
-  if ((long long)max_blocks * kBlock < max_ctx)
-    return fail(KVS_E_INVAL, "kvs_paged_decode_scored: max_blocks*16 < max_ctx");
+    return fail(KVS_E_INVAL, "%s: bad shape (batch=%d hq=%d hkv=%d d=%d max_ctx=%d stride=%d)", name, batch, hq, hkv,
+                d, max_ctx, slot_stride);
+  if ((long long)max_blocks * kBlock < max_ctx) return fail(KVS_E_INVAL, "%s: max_blocks*16 < max_ctx", name);
   if (batch == 0) return KVS_OK;
-  const Plan p = choose_plan(batch, hq, hkv, d, max_ctx, false);
+  Plan p = choose_plan(batch, hq, hkv, d, max_ctx, false);   // the 16-bit plan for both: it sizes the workspace
+  if (f8 && p.waves == 16) p.waves = 8;
   const size_t need = kvs_paged_decode_scored_workspace_size(batch, hq, hkv, d, max_ctx);
   if (!workspace || workspace_bytes < need)
-    return fail(KVS_E_INVAL, "kvs_paged_decode_scored: workspace of %zu bytes needed, %zu given", need,
-                workspace_bytes);
+    return fail(KVS_E_INVAL, "%s: workspace of %zu bytes needed, %zu given", name, need, workspace_bytes);
   const float c = scale * kLog2e;
   const int G = hq / hkv;
   const size_t lds = ((size_t)p.waves * G * d + 2 * (size_t)p.waves * 16) * sizeof(float);
   dim3 grid(p.splits, hkv, batch);
   auto* qq = static_cast<const uint16_t*>(q);
-  void* kp = k_pool;
-  void* vp = v_pool;
   auto* nk = static_cast<const uint16_t*>(new_k);
   auto* nv = static_cast<const uint16_t*>(new_v);
   auto* oo = static_cast<uint16_t*>(o);
   float* ws = static_cast<float*>(workspace);
   float* logits = reinterpret_cast<float*>(static_cast<char*>(workspace) + scored_logits_offset(batch, hq, p.splits, d));
   hipStream_t st = as_stream(stream);
-  const DecodeExtra ex{dst_slots, logits, max_ctx, 1, nullptr, nullptr};
-  if (d == 128)
-    launch_decode<128, false>(p, grid, lds, st, qq, kp, vp, num_blocks, block_tables, max_blocks, ctx_lens, hq, hkv, c, nk, nv,
-                       oo, lse_opt, ws, ex);
-  else
-    launch_decode<64, false>(p, grid, lds, st, qq, kp, vp, num_blocks, block_tables, max_blocks, ctx_lens, hq, hkv, c, nk, nv,
-                      oo, lse_opt, ws, ex);
-  int rc = launch_status("kvs_paged_decode_scored");
+  const DecodeExtra ex{dst_slots, logits, max_ctx, 1, k_scale, v_scale};
+  if (d == 128) {
+    if (f8)
+      launch_decode<128, true>(p, grid, lds, st, qq, k_pool, v_pool, num_blocks, block_tables, max_blocks, ctx_lens,
+                               hq, hkv, c, nk, nv, oo, lse_opt, ws, ex);
+    else
+      launch_decode<128, false>(p, grid, lds, st, qq, k_pool, v_pool, num_blocks, block_tables, max_blocks, ctx_lens,
+                                hq, hkv, c, nk, nv, oo, lse_opt, ws, ex);
+  } else {
+    if (f8)
+      launch_decode<64, true>(p, grid, lds, st, qq, k_pool, v_pool, num_blocks, block_tables, max_blocks, ctx_lens,
+                              hq, hkv, c, nk, nv, oo, lse_opt, ws, ex);
+    else
+      launch_decode<64, false>(p, grid, lds, st, qq, k_pool, v_pool, num_blocks, block_tables, max_blocks, ctx_lens,
+                               hq, hkv, c, nk, nv, oo, lse_opt, ws, ex);
+  }
+  int rc = launch_status(name);
   if (rc != KVS_OK) return rc;
   if (d == 128)
     hipLaunchKernelGGL(decode_merge_score_kernel<128>, dim3(hkv, batch), dim3(256), 0, st, ws, logits, max_ctx,
@@ -771,5 +775,27 @@ extern "C" int kvs_paged_decode_scored(const void* q, void* k_pool, void* v_pool
   else
     hipLaunchKernelGGL(decode_merge_score_kernel<64>, dim3(hkv, batch), dim3(256), 0, st, ws, logits, max_ctx,
                        ctx_lens, hq, hkv, max_blocks, p.splits, p.bps, oo, lse_opt, slot_scores, slot_stride);
-  return launch_status("kvs_paged_decode_scored (merge and score)");
+  return launch_status(name);
+}
+
+extern "C" int kvs_paged_decode_scored(const void* q, void* k_pool, void* v_pool, int num_blocks,
+                                       const int32_t* block_tables, int max_blocks, const int32_t* ctx_lens, int batch,
+                                       int max_ctx, int hq, int hkv, int d, float scale, const void* new_k,
+                                       const void* new_v, const int32_t* dst_slots, float* slot_scores,
+                                       int slot_stride, void* o, float* lse_opt, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  return run_scored("kvs_paged_decode_scored", q, k_pool, v_pool, nullptr, nullptr, false, num_blocks, block_tables,
+                    max_blocks, ctx_lens, batch, max_ctx, hq, hkv, d, scale, new_k, new_v, dst_slots, slot_scores,
+                    slot_stride, o, lse_opt, workspace, workspace_bytes, stream);
+}
+
+extern "C" int kvs_paged_decode_scored_fp8(const void* q, void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                                           int num_blocks, const int32_t* block_tables, int max_blocks,
+                                           const int32_t* ctx_lens, int batch, int max_ctx, int hq, int hkv, int d,
+                                           float scale, const void* new_k, const void* new_v,
+                                           const int32_t* dst_slots, float* slot_scores, int slot_stride, void* o,
+                                           float* lse_opt, void* workspace, size_t workspace_bytes, void* stream) {
+  return run_scored("kvs_paged_decode_scored_fp8", q, k_pool, v_pool, k_scale, v_scale, true, num_blocks,
+                    block_tables, max_blocks, ctx_lens, batch, max_ctx, hq, hkv, d, scale, new_k, new_v, dst_slots,
+                    slot_scores, slot_stride, o, lse_opt, workspace, workspace_bytes, stream);
 }

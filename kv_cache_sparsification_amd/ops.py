@@ -340,3 +340,33 @@ def kvs_gather_paged(k_pool, v_pool, block_tables, counts, dst_start, max_count:
     check(lib.kvs_gather_paged(k_pool.data_ptr(), v_pool.data_ptr(), nb, block_tables.data_ptr(),
                                block_tables.shape[1], counts.numel(), hkv, d, counts.data_ptr(), dst_start.data_ptr(),
                                int(max_count), k_dst.data_ptr(), v_dst.data_ptr(), _stream(stream)))
+
+
+def kvs_paged_decode_scored_fp8(q, k_pool, v_pool, k_scale, v_scale, block_tables, ctx_lens, max_ctx: int,
+                                slot_scores, new_k=None, new_v=None, dst_slots=None, scale: Optional[float] = None,
+                                o=None, lse=None, workspace=None, stream=None):
+    """kvs_paged_decode_scored over an 8-bit cache (the new token quantized into its slot)."""
+    _dev(q, torch.bfloat16, "q")
+    nb, hkv, _ = _check_fp8_pools(k_pool, v_pool, k_scale, v_scale)
+    _dev(block_tables, torch.int32, "block_tables"); _dev(ctx_lens, torch.int32, "ctx_lens")
+    _dev(slot_scores, torch.float32, "slot_scores")
+    B, hq, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if new_k is not None:
+        _dev(new_k, torch.bfloat16, "new_k"); _dev(new_v, torch.bfloat16, "new_v")
+    if dst_slots is not None:
+        _dev(dst_slots, torch.int32, "dst_slots")
+    o = torch.empty_like(q) if o is None else _dev(o, torch.bfloat16, "o")
+    if lse is not None:
+        _dev(lse, torch.float32, "lse")
+    need = kvs_paged_decode_scored_workspace_size(B, hq, hkv, d, int(max_ctx))
+    if workspace is None:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    check(lib.kvs_paged_decode_scored_fp8(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), k_scale.data_ptr(),
+                                          v_scale.data_ptr(), nb, block_tables.data_ptr(), block_tables.shape[1],
+                                          ctx_lens.data_ptr(), B, int(max_ctx), hq, hkv, d, float(scale), _ptr(new_k),
+                                          _ptr(new_v), _ptr(dst_slots), slot_scores.data_ptr(), slot_scores.shape[2],
+                                          o.data_ptr(), _ptr(lse), workspace.data_ptr(), ws_bytes, _stream(stream)))
+    return o

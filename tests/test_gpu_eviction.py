@@ -14,6 +14,7 @@ import pytest
 import torch
 
 import oracle
+from oracle import fp8 as ofp8
 import workloads as wl
 from tests._parity import bf16_to_f64, bf16_bits, i32, assert_rows_close, assert_lse_close, gather_pools
 
@@ -172,3 +173,65 @@ def test_eviction_batch_appends_then_evicts():
             np.testing.assert_allclose(sl_sc.cpu().numpy()[s, :, :c.n].astype(np.float64), c.score[:, :c.n],
                                        rtol=1e-4, atol=1e-6, err_msg=f"scores step {step} seq {s}")
     assert all(c.n == cap for c in caches)
+
+
+def _q(x):
+    """The values an 8-bit cache row holds for x (oracle quantization, R23)."""
+    return ofp8.dequantize_rows(*ofp8.quantize_rows(x))
+
+
+def test_eviction_llama8b_layer_fp8():
+    """Decode-time scoring and eviction over the 8-bit cache: same rules, the oracle's cache
+    holding the quantized values; the pools hold exactly the oracle's slots at the end."""
+    w = wl.WORKLOADS[2]
+    n, alpha, cap, steps, check_every = w.fixed_len, w.alpha, w.budgets[0], 30, 7
+    _say(f"eviction fp8: n={n} hq={w.hq} hkv={w.hkv} d={w.d} alpha={alpha} cap={cap} steps={steps}")
+    qb, kbits, vb, cu = wl.prefill_batch(w, 0, [n])
+    up = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v = up(qb), up(kbits), up(vb)
+    cu_d = i32(cu)
+    nblk = -(-cap // 16)
+    alloc = kvs.BlockAllocator(nblk + 3, list(np.random.default_rng(9).permutation(nblk + 3)))
+    k16, v16 = kvs.new_pools(nblk + 3, w.hkv, w.d)
+    res = kvs.prefill_compress_layer(q, k, v, cu_d, [n], alpha, cap, alloc, k16, v16, nblk)
+    pools = kvs.new_pools_fp8(nblk + 3, w.hkv, w.d)
+    pools[0].fill_(0x7F); pools[1].fill_(0x7F); pools[2].fill_(float("nan")); pools[3].fill_(float("nan"))
+    tbl = res["tables_dev"]
+    kvs.kvs_compact_paged_fp8(k, v, cu_d, res["keep_idx"], res["keep_offsets"], cap, *pools, tbl)
+    stride = nblk * 16
+    sl_sc, sl_pos = kvs.kvs_slot_init(res["scores"], cu_d, res["keep_idx"], res["keep_offsets"], stride)
+    torch.cuda.synchronize()
+    keep = res["keep_idx"].cpu().numpy().reshape(w.hkv, cap)
+    S = res["scores"].cpu().numpy().astype(np.float64)
+    c = oracle.init_cache(_q(bf16_to_f64(k)), _q(bf16_to_f64(v)), S, keep, cap)
+    n_filled, ctx = i32(np.array([cap])), i32(np.array([cap]))
+    ws = torch.empty(kvs.kvs_paged_decode_scored_workspace_size(1, w.hq, w.hkv, w.d, cap), dtype=torch.uint8,
+                     device="cuda")
+    for step in range(steps):
+        new_pos = n + step
+        dq, dk, dv = wl.device_decode_step(w, 0, step, [0])
+        sc_before = sl_sc.cpu().numpy()[0].astype(np.float64)
+        pos_before = sl_pos.cpu().numpy()[0]
+        dst = kvs.kvs_decode_select_slot(sl_sc, sl_pos, n_filled, i32(np.array([new_pos])), cap, alpha)
+        lse = torch.empty(1, w.hq, device="cuda")
+        o = kvs.kvs_paged_decode_scored_fp8(dq, *pools, tbl, ctx, cap, sl_sc, new_k=dk, new_v=dv, dst_slots=dst,
+                                            lse=lse, workspace=ws)
+        torch.cuda.synchronize()
+        dst_h = dst.cpu().numpy()[0]
+        for g in range(w.hkv):
+            assert dst_h[g] == oracle.select_slot(sc_before[g], pos_before[g], cap, cap, new_pos, alpha)
+        o_ref, lse_ref, _ = oracle.decode_step(c, bf16_to_f64(dq)[0], _q(bf16_to_f64(dk)[0]), _q(bf16_to_f64(dv)[0]),
+                                               new_pos, alpha, dst=dst_h)
+        if step % check_every == 0 or step == steps - 1:
+            assert_rows_close(bf16_to_f64(o)[0], o_ref, what=f"eviction fp8 o step {step}")
+            assert_lse_close(lse.cpu().numpy()[0], lse_ref, what=f"eviction fp8 lse step {step}")
+            np.testing.assert_allclose(sl_sc.cpu().numpy()[0, :, :cap].astype(np.float64), c.score, rtol=1e-4,
+                                       atol=1e-6, err_msg=f"scores step {step}")
+            np.testing.assert_array_equal(sl_pos.cpu().numpy()[0, :, :cap], c.pos)
+    kp, vp, ks, vs = (t.cpu().numpy() for t in pools)
+    table = res["tables"][0]
+    gk = ofp8.gather_rows_fp8(kp, ks, table, cap)
+    gv = ofp8.gather_rows_fp8(vp.transpose(0, 1, 3, 2), vs, table, cap)
+    for g in range(w.hkv):
+        np.testing.assert_array_equal(gk[:, g], c.k[g], err_msg=f"K head {g}")
+        np.testing.assert_array_equal(gv[:, g], c.v[g], err_msg=f"V head {g}")

@@ -67,21 +67,38 @@ __global__ __launch_bounds__(kThreads) void select_slot_kernel(float* __restrict
       best_slot = -1;
     }
     __syncthreads();
+    // Slots are read kPer per thread at a time, all loads of a round in flight together; with
+    // cap <= kThreads * kPer (one round) the second pass reuses the registers.
+    constexpr int kPer = 8;
+    auto key_of = [&](int p, float v) {
+      return (p >= 0 && p < np - alpha) ? (((unsigned long long)__float_as_uint(v) << 32) | (unsigned)p) : ~0ull;
+    };
+    unsigned long long keys[kPer];
     unsigned long long mine = ~0ull;
-    for (int t = tid; t < cap; t += kThreads) {
-      const int p = ps[t];
-      if (p >= 0 && p < np - alpha) {
-        const unsigned long long key = ((unsigned long long)__float_as_uint(sc[t]) << 32) | (unsigned)p;
-        mine = key < mine ? key : mine;
+    for (int c0 = 0; c0 < cap; c0 += kThreads * kPer) {
+      int p[kPer];
+      float v[kPer];
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int t = c0 + j * kThreads + tid;
+        p[j] = t < cap ? ps[t] : -1;
+        v[j] = t < cap ? sc[t] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        keys[j] = key_of(p[j], v[j]);
+        mine = keys[j] < mine ? keys[j] : mine;
       }
     }
     atomicMin(&best, mine);
     __syncthreads();
-    for (int t = tid; t < cap; t += kThreads) {   // positions are distinct: one slot matches
-      const int p = ps[t];
-      if (p >= 0 && p < np - alpha &&
-          (((unsigned long long)__float_as_uint(sc[t]) << 32) | (unsigned)p) == best)
-        best_slot = t;
+    if (cap <= kThreads * kPer) {                 // the registers hold the only round
+#pragma unroll
+      for (int j = 0; j < kPer; ++j)
+        if (keys[j] != ~0ull && keys[j] == best) best_slot = j * kThreads + tid;
+    } else {
+      for (int t = tid; t < cap; t += kThreads)   // positions are distinct: one slot matches
+        if (key_of(ps[t], sc[t]) == best && best != ~0ull) best_slot = t;
     }
     __syncthreads();
     dst = best_slot;                              // -1 only if no slot may go (cap <= alpha: refused on the host)

@@ -79,7 +79,22 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   const uint32_t* bits = reinterpret_cast<const uint32_t*>(scores + (size_t)g * total_tokens + base);
   const bool in_lds = n_cand <= kLdsCap;   // block-uniform
   if (in_lds) {
-    for (int i = tid; i < n_cand; i += kThreads) cand[i] = bits[i];
+    // Eight loads per thread in flight before the LDS stores: one memory round trip per
+    // 4096 candidates instead of one per 512.
+    constexpr int kBatch = 8;
+    for (int i0 = 0; i0 < n_cand; i0 += kThreads * kBatch) {
+      uint32_t vals[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int i = i0 + j * kThreads + tid;
+        vals[j] = i < n_cand ? bits[i] : 0u;
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int i = i0 + j * kThreads + tid;
+        if (i < n_cand) cand[i] = vals[j];
+      }
+    }
   }
   auto at = [&](int i) { return in_lds ? cand[i] : bits[i]; };
 

@@ -69,16 +69,26 @@ __global__ __launch_bounds__(kWaves * kWave) void window_score_kernel(
 
   float acc_sum = 0.f;
   for (int r0 = 0; r0 < rows; r0 += kRowChunk) {
-    // Stage 64 window rows: row r = (local head r / a, window position r % a).
-    for (int e = tid; e < kRowChunk * (D / 8); e += kWaves * kWave) {
+    // Stage kRowChunk window rows: row r = (local head r / a, window position r % a).  All of
+    // a thread's loads are issued before any LDS store, so the staging costs one memory round
+    // trip, not one per load.
+    constexpr int kStage = kRowChunk * (D / 8) / (kWaves * kWave);
+    u32x4 staged[kStage];
+#pragma unroll
+    for (int i = 0; i < kStage; ++i) {
+      const int e = tid + i * kWaves * kWave;
       const int r = e / (D / 8), cc = e % (D / 8);
       const int rr = r0 + r;
-      u32x4 v = {0u, 0u, 0u, 0u};
+      staged[i] = u32x4{0u, 0u, 0u, 0u};
       if (rr < rows && m - a + rr % a >= 0) {   // a window row before the chunk is not counted
         const int h = g * G + rr / a, j = m - a + rr % a;   // chunk-local row of window position n - a + rr % a
-        v = *reinterpret_cast<const u32x4*>(q + ((size_t)(base + j) * hq + h) * D + cc * 8);
+        staged[i] = *reinterpret_cast<const u32x4*>(q + ((size_t)(base + j) * hq + h) * D + cc * 8);
       }
-      *reinterpret_cast<u32x4*>(&qs[r * kStride + cc * 8]) = v;
+    }
+#pragma unroll
+    for (int i = 0; i < kStage; ++i) {
+      const int e = tid + i * kWaves * kWave;
+      *reinterpret_cast<u32x4*>(&qs[(e / (D / 8)) * kStride + (e % (D / 8)) * 8]) = staged[i];
     }
     if (tid < kRowChunk) {
       const int rr = r0 + tid;

@@ -12,7 +12,8 @@
 //   * causality and the window bound mean only window rows are visited (about n * alpha
 //     pairs instead of n * n).
 //
-// MI355X form.  A workgroup (4 wavefronts) owns 128 consecutive keys of one KV head; each
+// MI355X form.  A workgroup (4 wavefronts) owns 128 consecutive keys of one KV head (mapped to
+// the XCD that ran that head's prefill, whose L2 holds the keys); each
 // wavefront owns 32 keys, which are the N dimension of a bf16 32x32x16 MFMA, while the
 // G * a window rows of the group's query heads are the M dimension, staged through LDS in
 // chunks of 128 rows (one chunk for 4 query heads x a 32-token window) together with
@@ -30,12 +31,13 @@ constexpr int kWaves = 4;
 constexpr int kKeysPerWave = 32;
 constexpr int kKeysPerWG = kWaves * kKeysPerWave;
 constexpr int kRowChunk = 128;  // window rows staged in LDS at a time (4 M tiles)
+constexpr int kXcds = 8;
 
 template <int D>
 __global__ __launch_bounds__(kWaves * kWave) void window_score_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ lse,
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ cu_seqlens_k, int total_tokens, int total_k,
-    int alpha, int hq, int hkv, float c_log2, float* __restrict__ S) {
+    int alpha, int hq, int hkv, float c_log2, float* __restrict__ S, int nkt, int num_seqs, int total_items) {
   constexpr int kStride = D + 8;                       // bf16 per LDS row (16-byte pad)
   __shared__ __attribute__((aligned(16))) uint16_t qs[kRowChunk * kStride];
   __shared__ float lse2[kRowChunk];
@@ -43,12 +45,20 @@ __global__ __launch_bounds__(kWaves * kWave) void window_score_kernel(
 
   // Q rows and LSE of prompt s: [base, base + m); its keys and scores: [kbase, kbase + n).  The
   // Q rows are the prompt's last m positions (a chunk that ends the prompt, or all of it).
-  const int g = blockIdx.y, s = blockIdx.z;
+  // XCD-aware mapping (workgroups go to the 8 XCDs round robin): XCD x takes a contiguous run
+  // of items ordered (KV head, prompt, key tile), the order the prefill gives its XCDs, so a
+  // head's keys are read where the prefill just left them in L2.
+  const int per_xcd = gridDim.x / kXcds;
+  const int item = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (item >= total_items) return;
+  const int kt = item % nkt;
+  const int s = (item / nkt) % num_seqs;
+  const int g = item / nkt / num_seqs;
   const int base = cu_seqlens[s];
   const int m = cu_seqlens[s + 1] - base;
   const int kbase = cu_seqlens_k ? cu_seqlens_k[s] : base;
   const int n = cu_seqlens_k ? cu_seqlens_k[s + 1] - kbase : m;
-  const int kb_wg = blockIdx.x * kKeysPerWG;
+  const int kb_wg = kt * kKeysPerWG;
   if (kb_wg >= n) return;
   const int G = hq / hkv;
   const int a = alpha < n ? alpha : n;
@@ -138,16 +148,21 @@ static int run_window(const char* name, const void* q, const void* k, const floa
     return fail(KVS_E_INVAL, "%s: bad shape (hq=%d hkv=%d d=%d)", name, hq, hkv, d);
   if (alpha < 1) return fail(KVS_E_INVAL, "%s: alpha must be >= 1", name);
   if (num_seqs == 0 || max_seqlen_k == 0) return KVS_OK;
-  dim3 grid((max_seqlen_k + kKeysPerWG - 1) / kKeysPerWG, hkv, num_seqs);
+  const int nkt = (max_seqlen_k + kKeysPerWG - 1) / kKeysPerWG;
+  const long long items = (long long)nkt * hkv * num_seqs;
+  if (items > (1ll << 30)) return fail(KVS_E_INVAL, "%s: grid too large", name);
+  const dim3 grid((unsigned)((items + kXcds - 1) / kXcds * kXcds));
   const float c = scale * kLog2e;
   auto* qq = static_cast<const uint16_t*>(q);
   auto* kk = static_cast<const uint16_t*>(k);
   if (d == 128)
     hipLaunchKernelGGL(window_score_kernel<128>, grid, dim3(kWaves * kWave), 0, as_stream(stream), qq, kk, lse,
-                       cu_seqlens, cu_seqlens_k, total_tokens, total_k, alpha, hq, hkv, c, scores);
+                       cu_seqlens, cu_seqlens_k, total_tokens, total_k, alpha, hq, hkv, c, scores, nkt, num_seqs,
+                       (int)items);
   else
     hipLaunchKernelGGL(window_score_kernel<64>, grid, dim3(kWaves * kWave), 0, as_stream(stream), qq, kk, lse,
-                       cu_seqlens, cu_seqlens_k, total_tokens, total_k, alpha, hq, hkv, c, scores);
+                       cu_seqlens, cu_seqlens_k, total_tokens, total_k, alpha, hq, hkv, c, scores, nkt, num_seqs,
+                       (int)items);
   return launch_status(name);
 }
 

@@ -55,7 +55,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
                                                         int total_tokens, int hkv, int alpha, int k_budget,
                                                         const int32_t* __restrict__ keep_offsets,
                                                         int32_t* __restrict__ keep_idx) {
-  extern __shared__ uint32_t cand[];    // up to kLdsCap candidate bit patterns
+  extern __shared__ __attribute__((aligned(16))) uint32_t cand[];   // up to kLdsCap candidate bit patterns (+4 spare)
   __shared__ int hist[2][2048];    // alternate passes: one is cleared while the other is read
   __shared__ int tot[2][kWaves];
   __shared__ int sel_bin, sel_rem;
@@ -144,7 +144,40 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   const uint32_t T = prefix;
   const int ties = remaining;   // copies of T to take, lowest index first
 
-  // Contiguous chunk per thread, in index order.
+  // Contiguous chunk per thread, in index order.  With the candidates in LDS, a chunk is a
+  // multiple of four (16-byte aligned) and read once into registers with 16-byte reads: one
+  // word at a time, a wavefront's lanes would hit LDS words a chunk apart, all in the same
+  // few banks.
+  if (in_lds) {
+    const int per = ((n_cand + kThreads - 1) / kThreads + 3) & ~3;
+    const int c0 = min(tid * per, n_cand), c1 = min(c0 + per, n_cand);
+    // may read up to 3 words past the candidates: the allocation has 4 spare words
+    auto group = [&](int i) { return *reinterpret_cast<const u32x4*>(&cand[i]); };
+    int gt = 0, eq = 0;
+    for (int i = c0; i < c1; i += 4) {
+      const u32x4 x = group(i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool in = i + j < c1;
+        gt += in && x[j] > T;
+        eq += in && x[j] == T;
+      }
+    }
+    const int eq_before = block_incl_scan(eq, tot[1]) - eq;   // tot[1] was last read in pass 1
+    const int take_eq = min(max(ties - eq_before, 0), eq);
+    const int sel = gt + take_eq;
+    int pos = block_incl_scan(sel, tot[0]) - sel;             // tot[0] was last read in pass 2
+    int e = eq_before;
+    for (int i = c0; i < c1; i += 4) {
+      const u32x4 x = group(i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t u = x[j];
+        if (i + j < c1 && (u > T || (u == T && e++ < ties))) out[pos++] = i + j;
+      }
+    }
+    return;
+  }
   const int per = (n_cand + kThreads - 1) / kThreads;
   const int c0 = min(tid * per, n_cand), c1 = min(c0 + per, n_cand);
   int gt = 0, eq = 0;
@@ -178,7 +211,7 @@ extern "C" int kvs_topk_select(const float* scores, const int32_t* cu_seqlens, i
   if (alpha < 1 || k_budget < alpha)
     return fail(KVS_E_INVAL, "kvs_topk_select: need 1 <= alpha <= k_budget (alpha=%d k=%d)", alpha, k_budget);
   if (num_seqs == 0 || total_tokens == 0) return KVS_OK;
-  const size_t lds = (size_t)min(max(max_seqlen, 1), kLdsCap) * sizeof(uint32_t);
+  const size_t lds = ((size_t)min(max(max_seqlen, 1), kLdsCap) + 4) * sizeof(uint32_t);
   hipLaunchKernelGGL(topk_kernel, dim3(hkv, num_seqs), dim3(kThreads), lds, as_stream(stream), scores, cu_seqlens,
                      total_tokens, hkv, alpha, k_budget, keep_offsets, keep_idx);
   return launch_status("kvs_topk_select");

@@ -510,6 +510,7 @@ def decode_32_layers(kvs, torch, wl, steps, fp8=False):
     torch.cuda.synchronize()
     eager_us = e0.elapsed_time(e1) * 1e3 / steps
     cached = sum(sum(n if k_l is None else min(k_l, n) for n in lengths) for k_l in w.budgets)
+    kv_bytes = cached * hkv * (2 * d + 8 if fp8 else 4 * d)
     return {"workload": f"{B} sequences x {min(lengths)}-{max(lengths)} prompt tokens, {w.n_layers} layers "
                         f"(3 full, 29 at k=512), {hq}q/{hkv}kv heads, d={d}: one decode step of every layer"
                         + (", 8-bit E4M3 cache" if fp8 else ""),
@@ -517,6 +518,12 @@ def decode_32_layers(kvs, torch, wl, steps, fp8=False):
             "launches_per_step": sum(2 if kvs.kvs_paged_decode_workspace_size(B, hq, hkv, d, l[3]) else 1
                                      for l in layers),
             "cached_tokens_per_head": cached,
+            # K/V bytes read per step (about 1.8 GB: more than the 256 MB Infinity Cache holds,
+            # so this is an HBM rate); 8-bit rows carry one fp32 scale each for K and V
+            "kv_bytes_per_step": kv_bytes,
+            "achieved_GBs": round(kv_bytes / (graph_us * 1e-6) / 1e9, 1),
+            "peak_GBs": HBM_PEAK_GBS,
+            "frac": round(kv_bytes / (graph_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "tok_s": round(B / (graph_us * 1e-6), 1)}
 
 

@@ -21,7 +21,7 @@
 namespace kvs {
 namespace {
 
-constexpr int kThreads = 512;
+constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kLdsCap = 16384;   // candidates held in LDS (64 KB); longer prompts read L2 each pass
 

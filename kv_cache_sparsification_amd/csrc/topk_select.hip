@@ -80,7 +80,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   const bool in_lds = n_cand <= kLdsCap;   // block-uniform
   if (in_lds) {
     // Eight loads per thread in flight before the LDS stores: one memory round trip per
-    // 4096 candidates instead of one per 512.
+    // 8 * kThreads candidates instead of one per kThreads.
     constexpr int kBatch = 8;
     for (int i0 = 0; i0 < n_cand; i0 += kThreads * kBatch) {
       uint32_t vals[kBatch];

@@ -376,6 +376,15 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
         }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) vf[j][mt] = e4m3x4_to_bf16x4(f8[j].v[mt] & vmask);
+      } else if (bi * kBlock + kBlock > L) {
+        // the last block's slots past the context were never written (they may hold NaN bit
+        // patterns, and P = 0 does not cancel those in the product): zero them
+        const int live = L - bi * kBlock - grp * 4;   // slots of the lane's 4 inside the context
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (i >= live) vf[j][mt][i] = 0;
       }
       f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll

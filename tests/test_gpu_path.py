@@ -306,3 +306,65 @@ def test_single_token_and_window_only():
         keep = kvs.kvs_topk_select(S, cu, n, alpha, kb, i32([0, k_eff]), total_keep=k_eff).cpu().numpy()
         for g in range(hkv):
             np.testing.assert_array_equal(keep[g * k_eff:(g + 1) * k_eff], np.arange(n - k_eff, n))
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("d,hq,hkv,lens", [(128, 32, 8, [32, 17, 1, 400]), (64, 4, 2, [16, 3000])])
+def test_decode_ignores_unwritten_slots(fp8, d, hq, hkv, lens):
+    """Slots past the context in a sequence's last block were never written and may hold any bit
+    pattern: here NaN (and NaN codes and scales in the 8-bit cache).  Masked scores give P = 0,
+    which does not cancel a NaN in the P.V product, so the kernel must keep those values out.
+    Covers contexts ending mid-block and an appended token that opens a fresh block."""
+    _say(f"decode over NaN-filled tails fp8={fp8} d={d} hq={hq} hkv={hkv} lens={lens}")
+    from oracle import fp8 as ofp8
+    r = np.random.default_rng(d + 7 * len(lens) + fp8)
+    B = len(lens)
+    max_ctx = max(lens) + 1
+    max_blocks = oracle.blocks_for(max_ctx)
+    nb = B * max_blocks + 3
+    perm = list(r.permutation(nb))
+    tbl = np.full((B, max_blocks), -1, np.int32)
+    for b, L in enumerate(lens):
+        t = [perm.pop() for _ in range(oracle.blocks_for(L + 1))]
+        tbl[b, :len(t)] = t
+    pools = kvs.new_pools_fp8(nb, hkv, d) if fp8 else kvs.new_pools(nb, hkv, d)
+    caches = []
+    for b, L in enumerate(lens):
+        kc = wl.f32_to_bf16_bits(r.standard_normal((L, hkv, d), dtype=np.float32))
+        vc = wl.f32_to_bf16_bits(r.standard_normal((L, hkv, d), dtype=np.float32))
+        compact = kvs.kvs_compact_paged_fp8 if fp8 else kvs.kvs_compact_paged
+        compact(to_dev_bf16(kc), to_dev_bf16(vc), i32([0, L]), None, None, L, *pools, i32(tbl[b:b + 1]))
+        caches.append((kc, vc))
+    torch.cuda.synchronize()
+    # every slot at or past each context, in the sequence's blocks, as never written: NaN
+    for b, L in enumerate(lens):
+        for p in range(L, oracle.blocks_for(L + 1) * 16):
+            blk, slot = int(tbl[b, p // 16]), p % 16
+            if fp8:
+                pools[0][blk, :, slot, :] = 0x7F
+                pools[1][blk, :, :, slot] = 0x7F
+                pools[2][blk, :, slot] = float("nan")
+                pools[3][blk, :, slot] = float("nan")
+            else:
+                pools[0][blk, :, slot, :].view(torch.int16).fill_(0x7FC0)
+                pools[1][blk, :, :, slot].view(torch.int16).fill_(0x7FC0)
+    qb = wl.f32_to_bf16_bits(r.standard_normal((B, hq, d), dtype=np.float32))
+    nk = wl.f32_to_bf16_bits(r.standard_normal((B, hkv, d), dtype=np.float32))
+    nv = wl.f32_to_bf16_bits(r.standard_normal((B, hkv, d), dtype=np.float32))
+    cached = lambda x: ofp8.dequantize_rows(*ofp8.quantize_rows(x)) if fp8 else x
+    decode = kvs.kvs_paged_decode_fp8 if fp8 else kvs.kvs_paged_decode
+    for append in (False, True):   # L = len (the tail after it is NaN), then len + 1 with the new token
+        ctx = i32([L + append for L in lens])
+        lse = torch.empty(B, hq, device="cuda", dtype=torch.float32)
+        o = decode(to_dev_bf16(qb), *pools, i32(tbl), ctx, max_ctx, new_k=to_dev_bf16(nk) if append else None,
+                   new_v=to_dev_bf16(nv) if append else None, lse=lse)
+        og, lg = bf16_to_f64(o), lse.cpu().numpy()
+        assert np.isfinite(og).all() and np.isfinite(lg).all()
+        for b, L in enumerate(lens):
+            kc, vc = cached(_f64(caches[b][0])), cached(_f64(caches[b][1]))
+            if append:
+                kc = np.concatenate([kc, cached(_f64(nk[b:b + 1]))])
+                vc = np.concatenate([vc, cached(_f64(nv[b:b + 1]))])
+            o_ref, l_ref = oracle.decode_attention(_f64(qb[b]), kc, vc)
+            assert_rows_close(og[b], o_ref, what=f"decode b={b} append={append}")
+            assert_lse_close(lg[b], l_ref, what=f"decode lse b={b} append={append}")

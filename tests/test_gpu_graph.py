@@ -87,11 +87,10 @@ def test_decode_graph_replays_match_eager_and_oracle():
     torch.cuda.synchronize()
     eager = [L["out"].clone() for L in layers]
 
-    # the eager results against the oracle (last step, every sequence)
-    qf = bf16_to_f64(q[steps - 1])
+    # the eager results against the oracle (every step, every sequence): step st attends over
+    # the cached rows and the new tokens of steps 0..st
     for li, L in enumerate(layers):
         for s in range(B):
-            n = L["lengths"][s]
             rows_k = wl.bf16_bits_to_f64(L["kb"][L["cu"][s]:L["cu"][s + 1]])
             rows_v = wl.bf16_bits_to_f64(L["vb"][L["cu"][s]:L["cu"][s + 1]])
             new_k = bf16_to_f64(nk[:, s])
@@ -101,10 +100,11 @@ def test_decode_graph_replays_match_eager_and_oracle():
                 rows_v = ofp8.dequantize_rows(*ofp8.quantize_rows(rows_v))
                 new_k = ofp8.dequantize_rows(*ofp8.quantize_rows(new_k))
                 new_v = ofp8.dequantize_rows(*ofp8.quantize_rows(new_v))
-            kc = np.concatenate([rows_k, new_k])
-            vc = np.concatenate([rows_v, new_v])
-            o_ref, _ = oracle.decode_attention(qf[s], kc, vc)
-            assert_rows_close(bf16_to_f64(eager[li][steps - 1, s]), o_ref, what=f"layer {li} seq {s}")
+            for st in range(steps):
+                kc = np.concatenate([rows_k, new_k[:st + 1]])
+                vc = np.concatenate([rows_v, new_v[:st + 1]])
+                o_ref, _ = oracle.decode_attention(bf16_to_f64(q[st])[s], kc, vc)
+                assert_rows_close(bf16_to_f64(eager[li][st, s]), o_ref, what=f"layer {li} seq {s} step {st}")
 
     stream = torch.cuda.current_stream()
     side = torch.cuda.Stream()

@@ -205,7 +205,7 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void prefill_kernel(
   // O^T A operand, fragment f = ks2*MT2 + mt: lane l reads V^T row 32*mt + l%32 (a channel),
   // keys 16*ks2 + 8*half + 0..7.
   const int vofs = col * VSTR + half * 8;
-  constexpr int NF2 = MT2 * KS2, NG2 = NF2 / 4;
+  constexpr int NF2 = MT2 * KS2;
   auto vfrag = [&](const uint16_t* vt, int f) {
     return *reinterpret_cast<const u32x4*>(&vt[(f % MT2) * 32 * VSTR + (f / MT2) * 16 + vofs]);
   };

@@ -73,6 +73,18 @@ def measured_traffic(kernel_key: str, source: str):
     return rec.get("bytes_per_launch")
 
 
+def measured_mfma(kernel_key: str, source: str):
+    """MFMA counters of a launch (rocprofv3: executed bf16 flops, MFMA-busy share of the SIMDs' active
+    cycles) from the committed summary, or None if the kernel changed since."""
+    path = os.path.join(ROOT, "profiles", "mfma.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(kernel_key)
+    if not rec or rec.get("source_sha256_16") != kernel_source_hash(source):
+        return None
+    return {"mfma_util": rec["mfma_util"], "executed_flops_per_launch": rec["executed_bf16_flops_per_launch"]}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -266,6 +278,8 @@ def main():
                             "traffic": measured_traffic(kname, src),
                             "avg_launch_us": round(avg_ms[kname] * 1e3, 2),
                             "algorithmic_per_launch": amount}
+        if bound == "mfma":
+            rooflines[kname]["counters"] = measured_mfma(kname, src)
     dominant = max(per_step_ms, key=per_step_ms.get)
 
     prefill_ms = float(np.mean(pre_phase))

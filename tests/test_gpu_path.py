@@ -2,6 +2,7 @@
 
 Each test prints the case it is about to run (flushed) so a failing GPU step is named.
 """
+import dataclasses
 import math
 import sys
 
@@ -139,7 +140,19 @@ def test_llama8b_layer_full_path():
     assert sum(0 in set(out["keep"][g]) for g in range(w.hkv)) >= 6
 
 
-@pytest.mark.parametrize("d,hq,hkv", [(128, 8, 2), (64, 4, 4), (128, 16, 1)])
+@pytest.mark.parametrize("hq,hkv,d,n,alpha,k", [(16, 2, 64, 600, 32, 96), (16, 1, 128, 777, 16, 64)])
+def test_wide_groups_full_path(hq, hkv, d, n, alpha, k):
+    """Groups of 8 and 16 query heads per KV head through every step: 256 window rows (two row
+    chunks of the score), and decode plans of 8 wavefronts in one workgroup (d=64) and of
+    4-wavefront splits with a merge (d=128)."""
+    w = dataclasses.replace(wl.WORKLOADS[1], hq=hq, hkv=hkv, d=d, alpha=alpha, budgets=(k,), fixed_len=n,
+                            decode_steps=20)
+    _say(f"wide groups: n={n} Hq={hq} Hkv={hkv} d={d} alpha={alpha} k={k}, 20 decode steps")
+    out = run_full_path(w, 0, check_decode_steps={0, 1, 2, 7, 11, 12, 19}, decode_steps=20)
+    assert all(0 in set(out["keep"][g]) for g in range(hkv))
+
+
+@pytest.mark.parametrize("d,hq,hkv", [(128, 8, 2), (64, 4, 4), (128, 16, 1), (64, 16, 2)])
 def test_prefill_ragged_batch(d, hq, hkv):
     lengths = [1, 17, 130, 255, 64, 300]
     _say(f"ragged prefill d={d} hq={hq} hkv={hkv} lengths={lengths}")
@@ -227,7 +240,8 @@ def test_compaction_offsets_keep_all_and_partial_blocks():
 
 
 @pytest.mark.parametrize("d,hq,hkv,lens", [(128, 32, 8, [5000, 1, 17, 900]), (64, 4, 2, [3, 2000]),
-                                           (128, 8, 8, [16, 32, 48])])
+                                           (128, 8, 8, [16, 32, 48]), (64, 16, 2, [700, 5]),
+                                           (64, 16, 1, [300, 2500]), (128, 16, 1, [1200, 7])])
 def test_decode_batch_splits_and_merge(d, hq, hkv, lens):
     """Full-cache decode over several contexts, with and without append; long contexts split and merge."""
     _say(f"decode batch d={d} hq={hq} hkv={hkv} lens={lens}")

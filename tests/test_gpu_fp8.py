@@ -242,6 +242,14 @@ def test_fp8_decode_long_context_batch():
     _decode_case("long context", 32, 8, 128, [3000, 2950, 3001, 2990], 3, seed=3, prompt_extra=200)
 
 
+@pytest.mark.parametrize("hq,hkv,d,k_effs", [(16, 2, 64, [700, 5]), (16, 1, 64, [300, 2500]),
+                                             (16, 1, 128, [1200, 7])])
+def test_fp8_decode_wide_groups(hq, hkv, d, k_effs):
+    """Groups of 8 and 16 query heads per KV head over the 8-bit cache: the 8- and 4-wavefront
+    launch shapes at d = 64 and 128, contexts split and merged or walked by one workgroup."""
+    _decode_case(f"G={hq // hkv} d={d}", hq, hkv, d, k_effs, 5, seed=hq * d + hkv, check_every=2)
+
+
 def test_fp8_decode_wide_batch():
     """64 short sequences: one workgroup per (sequence, KV head), no split."""
     rng = np.random.default_rng(4)

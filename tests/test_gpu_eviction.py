@@ -7,6 +7,7 @@ chosen slots must be exactly what the oracle's rule picks on the GPU's own fp32 
 accumulated scores are compared within the usual tolerances.  The pools' contents are
 checked bit-exactly against the oracle's cache at the end.
 """
+import dataclasses
 import sys
 
 import numpy as np
@@ -107,6 +108,16 @@ def test_eviction_tiny_many_steps():
 
 def test_eviction_llama8b_layer():
     c = _run(wl.WORKLOADS[2], steps=40, check_every=13)
+    assert c.n == c.cap
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(16, 2, 64), (16, 1, 128)])
+def test_eviction_wide_groups(hq, hkv, d):
+    """Groups of 8 and 16 query heads per KV head: the merge-and-score kernel adds every query
+    head's probability to its KV head's slot scores."""
+    w = dataclasses.replace(wl.WORKLOADS[1], hq=hq, hkv=hkv, d=d, alpha=16, budgets=(96,), fixed_len=500,
+                            decode_steps=30)
+    c = _run(w, steps=30, check_every=5)
     assert c.n == c.cap
 
 

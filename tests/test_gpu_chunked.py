@@ -39,7 +39,7 @@ def _bits(rng, shape, scale=1.0):
     return wl.f32_to_bf16_bits((rng.standard_normal(shape) * scale).astype(np.float32))
 
 
-@pytest.mark.parametrize("hq,hkv,d", [(4, 2, 64), (32, 8, 128)])
+@pytest.mark.parametrize("hq,hkv,d", [(4, 2, 64), (32, 8, 128), (16, 2, 64), (16, 1, 128)])
 def test_chunk_rows_and_window_score(hq, hkv, d):
     """Three prompts, each with only its last m_s rows as queries (one is the whole prompt)."""
     _say(f"chunked prefill hq={hq} hkv={hkv} d={d}")

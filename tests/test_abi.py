@@ -212,3 +212,19 @@ def test_chunk_and_gather_calls_validate_on_the_host():
     assert L.kvs_gather_paged(fake, fake, 8, fake, 4, 1, 2, 96, fake, fake, 16, fake, fake, None) == -1
     assert L.kvs_gather_paged(fake, fake, 8, fake, 4, 1, 2, 128, None, fake, 16, fake, fake, None) == -1
     assert L.kvs_gather_paged(fake, fake, 8, fake, 4, 1, 2, 128, fake, fake, 0, fake, fake, None) == 0
+
+
+def test_package_refuses_to_import_without_the_library(tmp_path):
+    """No CPU fallback: a copy of the package without libkvs.so fails at import, naming the build."""
+    import shutil
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    pkg = os.path.join(root, "kv_cache_sparsification_amd")
+    dst = tmp_path / "kv_cache_sparsification_amd"
+    shutil.copytree(pkg, dst, ignore=shutil.ignore_patterns("*.so", "__pycache__", "csrc"))
+    r = subprocess.run([sys.executable, "-c", "import kv_cache_sparsification_amd"], cwd=tmp_path,
+                       capture_output=True, text=True, timeout=300,
+                       env=dict(os.environ, PYTHONPATH=str(tmp_path)))
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "is not built" in r.stderr

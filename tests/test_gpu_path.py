@@ -154,7 +154,7 @@ def test_wide_groups_full_path(hq, hkv, d, n, alpha, k):
 
 @pytest.mark.parametrize("d,hq,hkv", [(128, 8, 2), (64, 4, 4), (128, 16, 1), (64, 16, 2)])
 def test_prefill_ragged_batch(d, hq, hkv):
-    lengths = [1, 17, 130, 255, 64, 300]
+    lengths = [1, 17, 130, 255, 64, 300, 256, 257, 513]
     _say(f"ragged prefill d={d} hq={hq} hkv={hkv} lengths={lengths}")
     r = np.random.default_rng(d + hq)
     T = sum(lengths)

@@ -188,7 +188,7 @@ def test_prefill_ragged_batch(d, hq, hkv):
 def test_topk_exact_with_ties_and_budgets():
     """Constructed scores with many ties: the kernel's kept set equals the oracle's exactly."""
     r = np.random.default_rng(3)
-    lengths = [5, 40, 600, 1000, 4097, 33]
+    lengths = [5, 40, 600, 1000, 4097, 33, 20000]   # the last beyond the 16384 candidates held in LDS
     hkv = 3
     T = sum(lengths)
     cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)

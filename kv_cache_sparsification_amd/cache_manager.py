@@ -14,12 +14,16 @@ them (kvs_compact_paged for prompts and shared prefixes, kvs_paged_decode for ap
 
 Prefix sharing.  Sequences of one group share a prefix of `prefix_len` tokens (whole blocks)
 when their prompt is longer than it.  While any such member is live the group holds one
-reference to the prefix blocks of every layer; each member adds its own:
-  * full layers: the member keeps the shared blocks and writes only its suffix, from slot
-    prefix_len on (a block boundary, so no shared block is ever written);
-  * compressed layers: the compaction overwrites slots 0..k_eff-1, so the member takes
-    copy-on-write replacements for those ceil(k_eff/16) table entries (no data copy: every
-    live slot is overwritten) and drops its references to the remaining prefix entries.
+reference to the prefix blocks of every layer that carries them; each member adds its own:
+  * full layers always carry the prefix: the member keeps the shared blocks and writes only
+    its suffix, from slot prefix_len on (a block boundary, so no shared block is written);
+  * compressed layers carry it only with `prefix_in_compressed` (the prefix is then a prompt
+    cache: a later member reads its first prefix_len keys and values back from those blocks
+    instead of recomputing them).  The compaction overwrites slots 0..k_eff-1, so the member
+    takes copy-on-write replacements for those ceil(k_eff/16) table entries (no data copy:
+    every live slot is overwritten) and drops its references to the remaining prefix entries.
+    Without it a compressed layer holds nothing of the prefix: each member takes
+    ceil(k_eff/16) fresh blocks, so the layer holds only the compressed caches.
 When the group's last sharing member finishes, the group's references go too.
 """
 from __future__ import annotations
@@ -47,13 +51,14 @@ class LayerPlan:
 
 class PagedKVCache:
     def __init__(self, budgets: Sequence[Optional[int]], num_blocks: Sequence[int], prefix_len: int = 0,
-                 record: bool = False):
+                 record: bool = False, prefix_in_compressed: bool = True):
         if prefix_len % BLOCK_SIZE:
             raise ValueError("the shared prefix must be whole blocks")
         self.budgets = list(budgets)
         self.n_layers = len(self.budgets)
         self.alloc = [BlockAllocator(nb) for nb in num_blocks]
         self.prefix_len = prefix_len
+        self.prefix_in_compressed = prefix_in_compressed
         self.prefix_blocks: List[Dict[int, List[int]]] = [dict() for _ in range(self.n_layers)]
         self.sharers: Dict[int, int] = {}                      # group -> live sharing members
         self.tables: Dict[Tuple[int, int], List[int]] = {}     # (seq, layer) -> block ids
@@ -85,6 +90,10 @@ class PagedKVCache:
         return nb
 
     # --- lifecycle -----------------------------------------------------------------------
+    def carries_prefix(self, layer: int) -> bool:
+        """Whether the layer keeps a group's shared prefix (full layers always; compressed by policy)."""
+        return self.budgets[layer] is None or self.prefix_in_compressed
+
     def kept_tokens(self, layer: int, n: int) -> int:
         k = self.budgets[layer]
         return n if (k is None or k >= n) else k
@@ -97,14 +106,15 @@ class PagedKVCache:
         if shares:
             if self.sharers.get(group, 0) == 0:                 # the group's prefix is created now
                 for l in range(self.n_layers):
-                    self.prefix_blocks[l][group] = [self._alloc(l) for _ in range(P)]
+                    if self.carries_prefix(l):
+                        self.prefix_blocks[l][group] = [self._alloc(l) for _ in range(P)]
                 new_prefix = True
             self.sharers[group] = self.sharers.get(group, 0) + 1
         self.group_of[seq] = group if shares else None
         plans = []
         for l in range(self.n_layers):
             kept = self.kept_tokens(l, n)
-            if shares:
+            if shares and self.carries_prefix(l):
                 table = list(self.prefix_blocks[l][group])
                 for b in table:
                     self._incref(l, b)
@@ -146,8 +156,23 @@ class PagedKVCache:
             self.sharers[group] -= 1
             if self.sharers[group] == 0:                        # last sharer: drop the group's references
                 for l in range(self.n_layers):
-                    for b in self.prefix_blocks[l].pop(group):
+                    for b in self.prefix_blocks[l].pop(group, []):
                         self._decref(l, b)
+
+    def slot_usage(self, layer: int) -> Tuple[int, int]:
+        """(slots holding a live token, slots in blocks taken from the pool) for one layer.
+
+        [PAG] "How paging works": paging wastes only the unfilled tail of each sequence's last
+        block.  A shared prefix block counts once, however many tables map it.
+        """
+        used = sum(self.prefix_len for _ in self.prefix_blocks[layer])
+        for (sid, l), n in self.length.items():
+            if l == layer:
+                # a sharing member's full-layer table maps the prefix blocks counted above
+                shared = self.group_of.get(sid) is not None and self.budgets[layer] is None
+                used += n - (self.prefix_len if shared else 0)
+        taken = self.alloc[layer].num_blocks - self.alloc[layer].num_free()
+        return used, taken * BLOCK_SIZE
 
     def num_free(self, layer: int) -> int:
         return self.alloc[layer].num_free()

@@ -26,9 +26,11 @@
 //     groups of four wavefronts (one of each on every SIMD) run one phase apart, separated by
 //     workgroup barriers, so each SIMD's matrix core works for one group while its vector unit
 //     works for the other.  Loads are issued two phases before their tile is first read.
-//   * Q stays in registers for the whole key loop.  Wavefronts whose rows all precede a key
-//     tile skip its work; only the diagonal tiles are masked, and O is rescaled only when a
-//     row maximum grows by more than 2^8 (wave-uniform branch).
+//   * Q stays in registers for the whole key loop.  Every wavefront runs every key tile its
+//     workgroup visits (the barriers of the ping-pong are shared); the causal mask applies to
+//     any tile that reaches past a wavefront's first row, so the tiles that lie wholly past
+//     its rows are computed and masked to P = 0.  O is rescaled only when a row maximum grows
+//     by more than 2^8 (wave-uniform branch).
 //   * Workgroups are remapped so that each XCD (8 per chip, each with its own L2) works on
 //     one KV head at a time, heaviest (last) query tiles first.
 #include "kvs_common.h"

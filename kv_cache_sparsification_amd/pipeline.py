@@ -79,6 +79,18 @@ def default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
 
 
+def check_chunk_lengths(q_lengths: Sequence[int], k_lengths: Sequence[int], alpha: int, scored: bool) -> None:
+    """Host check of a chunked step's lengths (see prefill_compress_layer_chunked)."""
+    if len(q_lengths) != len(k_lengths):
+        raise ValueError("q_lengths and k_lengths differ in length")
+    for s, (m, n) in enumerate(zip(q_lengths, k_lengths)):
+        if m < 0 or m > n:
+            raise ValueError(f"prompt {s}: chunk of {m} rows for a prompt of {n} tokens")
+        if scored and m < min(alpha, n):
+            raise ValueError(f"prompt {s}: the chunk holds {m} rows but the window score needs the last "
+                             f"{min(alpha, n)}")
+
+
 def prefill_compress_layer_chunked(q, k, v, cu_q, cu_k, q_lengths: Sequence[int], k_lengths: Sequence[int],
                                    alpha: int, k_budget: Optional[int], k_pool, v_pool, tables: List[List[int]],
                                    max_blocks: int, cached: Optional[Sequence[int]] = None,
@@ -89,7 +101,12 @@ def prefill_compress_layer_chunked(q, k, v, cu_q, cu_k, q_lengths: Sequence[int]
     Compressed layers select over all n_s tokens and compact into `tables` from slot 0; a full
     layer writes only rows cached[s] .. n_s-1 (the reused prefix keeps its shared blocks), from
     slot cached[s].  Returns o, lse (chunk rows), scores, keep_idx, keep_offsets, tables_dev.
+
+    Raises ValueError before any launch when a prompt's chunk is longer than the prompt, or, in a
+    compressed layer, holds fewer than its last min(alpha, n) rows: the window score reads the
+    LSE of the window rows from the chunk, and rows before it would silently be left out.
     """
+    check_chunk_lengths(q_lengths, k_lengths, alpha, k_budget is not None)
     dev = q.device
     max_q, max_k = max(q_lengths), max(k_lengths)
     o, lse = ops.kvs_prefill_attn_lse_chunk(q, k, v, cu_q, cu_k, max_q, max_k, scale=scale, stream=stream)

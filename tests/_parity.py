@@ -3,7 +3,9 @@
 Tolerances (bf16 inputs, fp32 accumulation on the GPU):
   attention / decode outputs  per (row, head): max_c |o - r| <= 1e-2 * max_c |r|
   LSE                         |delta| <= 1e-3 (absolute, natural log)
-  window score S              |delta S_i| <= 1e-3 * |S_i| + 1e-7 * G * alpha
+  window score S              per KV head, |delta S_i| <= 1e-3 * |S_i| for every token with
+                              S_i >= 1e-6 * max_i S_i; below that threshold (scores far under the
+                              fp32 exponential's useful range) |delta S_i| <= 1e-3 * threshold
   kept index sets             equal, except that a GPU-only index and an oracle-only index may swap
                               when both oracle scores lie within 1e-4 (relative) of the oracle's
                               boundary score (the (k_eff - alpha)-th largest candidate score)
@@ -55,13 +57,23 @@ def assert_lse_close(got, ref, tol: float = LSE_TOL, what: str = "LSE"):
         raise AssertionError(f"{what}: max |delta| {d.max():.3e} > {tol}")
 
 
-def assert_scores_close(got, ref, G: int, alpha: int, what: str = "S"):
-    got = np.asarray(got, dtype=np.float64)
-    bound = S_REL * np.abs(ref) + 1e-7 * G * alpha
+S_FLOOR = 1e-6
+
+
+def assert_scores_close(got, ref, what: str = "S") -> int:
+    """got/ref [Hkv][n] (or [n]): 1e-3 relative per token above 1e-6 of the head's largest score,
+    absolute 1e-3 * that threshold below it.  Returns how many tokens took the absolute branch."""
+    got = np.atleast_2d(np.asarray(got, dtype=np.float64))
+    ref = np.atleast_2d(np.asarray(ref, dtype=np.float64))
+    thr = S_FLOOR * np.abs(ref).max(axis=-1, keepdims=True)
+    small = np.abs(ref) < thr
+    bound = np.where(small, S_REL * thr, S_REL * np.abs(ref))
     d = np.abs(got - ref)
     if not (d <= bound).all():
-        i = np.unravel_index(np.argmax(d / bound), d.shape)
-        raise AssertionError(f"{what}: worst at {i}: got {got[i]:.6e} ref {ref[i]:.6e}")
+        i = np.unravel_index(np.argmax(d / np.maximum(bound, 1e-300)), d.shape)
+        raise AssertionError(f"{what}: worst at {i}: got {got[i]:.6e} ref {ref[i]:.6e} "
+                             f"({int(small.sum())} of {small.size} tokens under the threshold)")
+    return int(small.sum())
 
 
 def assert_keep_matches(keep_gpu: np.ndarray, keep_ref: np.ndarray, S_ref: np.ndarray, n: int, alpha: int,

@@ -228,3 +228,18 @@ def test_package_refuses_to_import_without_the_library(tmp_path):
                        env=dict(os.environ, PYTHONPATH=str(tmp_path)))
     assert r.returncode != 0
     assert "ImportError" in r.stderr and "is not built" in r.stderr
+
+
+def test_chunked_step_rejects_short_chunks_on_the_host():
+    """A compressed layer's chunk must hold its prompt's last min(alpha, n) rows, and no chunk may
+    be longer than its prompt: the pipeline raises before touching a device."""
+    from kv_cache_sparsification_amd import pipeline
+    pipeline.check_chunk_lengths([32, 100], [4000, 100], 32, True)
+    pipeline.check_chunk_lengths([5], [5], 32, True)                  # n < alpha: the whole prompt
+    pipeline.check_chunk_lengths([1], [4000], 32, False)              # a full layer needs no window
+    for q, k in (([31], [4000]), ([4], [5]), ([101], [100]), ([-1], [10])):
+        with pytest.raises(ValueError):
+            pipeline.check_chunk_lengths(q, k, 32, True)
+    with pytest.raises(ValueError):
+        pipeline.prefill_compress_layer_chunked(None, None, None, None, None, [16], [4000], 32, 400, None, None,
+                                                [[0]], 1)

@@ -68,7 +68,7 @@ def test_chunk_rows_and_window_score(hq, hkv, d):
         assert_lse_close(lg[:, cu_q[s]:cu_q[s + 1]], lse_ref, what=f"chunk LSE seq {s}")
         a = min(alpha, n[s])
         S_ref = oracle.window_score(qf[n[s] - a:], kf, lse_ref[:, m[s] - a:], alpha, window_only=True)
-        assert_scores_close(Sg[:, cu_k[s]:cu_k[s + 1]], S_ref, G, alpha, what=f"chunk S seq {s}")
+        assert_scores_close(Sg[:, cu_k[s]:cu_k[s + 1]], S_ref, what=f"chunk S seq {s}")
 
 
 def test_gather_paged_round_trip():
@@ -165,7 +165,7 @@ def test_prefix_reuse_end_to_end(k_budget):
         _, lse_full, _, _ = oracle.causal_attention(qf, kf, vf, rows=range(nB - alpha, nB))
         S_ref = oracle.window_score(qf[nB - alpha:], kf, lse_full, alpha, window_only=True)
         S_g = res["scores"].cpu().numpy().astype(np.float64)
-        assert_scores_close(S_g, S_ref, hq // hkv, alpha, what="B scores")
+        assert_scores_close(S_g, S_ref, what="B scores")
         keep = res["keep_idx"].cpu().numpy().reshape(hkv, k_budget)
         gk, gv = gather_pools(k_pool, v_pool, table_b, k_budget)
         for g in range(hkv):

@@ -1,11 +1,17 @@
 """GPU parity of the continuous-batch mix: 64 slots, prompts log-uniform in [512, 32768],
 8 groups of 8 sharing a 2048-token prefix through refcounted blocks, pyramid budgets, decode
-with append, sequences finishing after U[100, 500] tokens and being replaced.
+with append, sequences finishing after U[100, 500] tokens and being replaced, over 1000
+iterations (every slot turns over at least twice).
 
 Kernels run on layers 0 (full cache), 3 (k = 2048) and 31 (k = 128); every layer's block
-bookkeeping runs through the product's cache manager on the native allocator.  Four seeded
-sequences are checked against the oracle: prefill O / LSE on seeded rows, window scores and
-kept sets, block contents (shared prefix blocks included) and decode outputs.
+bookkeeping runs through the product's cache manager on the native allocator, with the shared
+prefix carried by every layer.  A group's prefix blocks are written once, from the rows of the
+member whose admission creates them; every later member reads its first 2048 keys and values
+back from those blocks (kvs_gather_paged, checked bit-exact against the generated rows) and
+computes only its own rows (chunked prefill and window score), and each compressed layer's
+compaction lands in copy-on-write replacements of the shared blocks.  Five seeded sequences
+are checked against the oracle: prefill O / LSE on seeded rows, window scores and kept sets,
+block contents (shared prefix blocks included) and decode outputs.
 """
 import sys
 
@@ -17,7 +23,6 @@ import oracle
 import workloads as wl
 from tests._parity import (bf16_to_f64, bf16_bits, i32, assert_rows_close, assert_lse_close, assert_scores_close,
                            assert_keep_matches, gather_pools)
-from tests.test_lifecycle import pool_sizes
 
 pytestmark = pytest.mark.gpu
 
@@ -25,7 +30,8 @@ kvs = pytest.importorskip("kv_cache_sparsification_amd")
 from kv_cache_sparsification_amd.cache_manager import PagedKVCache
 
 LAYERS = (0, 3, 31)
-ITERATIONS = 160
+ITERATIONS = 1000
+NAN_BF16 = 0x7FC0
 
 
 def _say(*a):
@@ -46,74 +52,50 @@ def _prompt(w, layer, sq):
                             prefix_len=w.prefix_len if shares else 0)
 
 
+def _pick_tracked(w, trace):
+    """A group's creating member and a member reusing its prefix (first wave), a prompt that shares
+    nothing, the first late admission that shares, and the first sequence to finish."""
+    first_wave = trace[0][0]
+    P = w.prefix_len
+    tracked = set()
+    for g in range(w.num_seqs // w.group_size):
+        members = [sq for sq in first_wave if sq.group == g and sq.n > P]
+        if len(members) >= 2 and members[0].n <= 16384 and any(P + w.alpha <= m.n <= 16384 for m in members[1:]):
+            tracked.add(members[0].seq_id)
+            tracked.add(next(m.seq_id for m in members[1:] if P + w.alpha <= m.n <= 16384))
+            break
+    tracked.add(next(sq.seq_id for sq in first_wave if sq.n <= P))
+    late = [sq for adm, _ in trace[1:] for sq in adm if P + w.alpha <= sq.n <= 16384]
+    if late:
+        tracked.add(late[0].seq_id)
+    tracked.add(next(sid for _, fin in trace for sid in fin))
+    return tracked
+
+
+@pytest.mark.timeout(900)
 def test_continuous_mix_with_shared_prefixes():
     w = wl.WORKLOADS[5]
-    sizes = pool_sizes(w)
-    cache = PagedKVCache(w.budgets, sizes, prefix_len=w.prefix_len)
+    P = w.prefix_len
+    sizes = wl.mix_pool_sizes(w)
+    cache = PagedKVCache(w.budgets, sizes, prefix_len=P, prefix_in_compressed=True)
     pools = {l: kvs.new_pools(sizes[l], w.hkv, w.d) for l in LAYERS}
+    for kp, vp in pools.values():
+        kp.view(torch.int16).fill_(NAN_BF16)
+        vp.view(torch.int16).fill_(NAN_BF16)
     trace = wl.mix_trace(w, ITERATIONS)
     all_seqs = [sq for adm, _ in trace for sq in adm]
-    r = np.random.default_rng(w.seed)
-    sharing = [sq.seq_id for sq in all_seqs if sq.n > w.prefix_len and sq.n <= 16384]
-    private = [sq.seq_id for sq in all_seqs if sq.n <= w.prefix_len]
-    late = [sq.seq_id for sq in all_seqs if sq.seq_id >= w.num_seqs]
-    tracked = {int(sharing[0]), int(sharing[len(sharing) // 2]), int(r.choice(private))}
-    if late:
-        tracked.add(int(late[0]))
-    tracked.add(next(sid for _, fin in trace for sid in fin))      # one that finishes within the run
+    tracked = _pick_tracked(w, trace)
     _say(f"mix: {len(all_seqs)} admissions over {ITERATIONS} iterations, tracked {sorted(tracked)}")
-    info = {sq.seq_id: sq for sq in all_seqs}
     decoded = {}
     oracle_cache = {}          # (seq, layer) -> [K bits list, V bits list] in cache order
     live = []
     finished_tracked = []
+    stats = dict(reused=0, gathered_rows=0, swaps=0)
     for it, (admitted, finished) in enumerate(trace):
         if admitted:
             plans = {sq.seq_id: cache.admit(sq.seq_id, sq.group, sq.n) for sq in admitted}
             for l in LAYERS:
-                k_pool, v_pool = pools[l]
-                parts = [_prompt(w, l, sq) for sq in admitted]
-                q = torch.cat([p[0] for p in parts]); k = torch.cat([p[1] for p in parts])
-                v = torch.cat([p[2] for p in parts])
-                lengths = [sq.n for sq in admitted]
-                cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
-                cu_d = i32(cu)
-                o, lse = kvs.kvs_prefill_attn_lse(q, k, v, cu_d, max(lengths))
-                kb = w.budgets[l]
-                # shared prefixes created by this admission: written once, from the first member's rows
-                for s, sq in enumerate(admitted):
-                    pl = plans[sq.seq_id][l]
-                    if pl.new_prefix:
-                        pre = cache.prefix_blocks[l][sq.group]
-                        kvs.kvs_compact_paged(k[cu[s]:cu[s] + w.prefix_len].contiguous(),
-                                              v[cu[s]:cu[s] + w.prefix_len].contiguous(), i32([0, w.prefix_len]),
-                                              None, None, w.prefix_len, k_pool, v_pool, i32([pre]))
-                max_blocks = max(len(plans[sq.seq_id][l].table) for sq in admitted)
-                tbl = np.full((len(admitted), max_blocks), -1, np.int32)
-                for s, sq in enumerate(admitted):
-                    t = plans[sq.seq_id][l].table
-                    tbl[s, :len(t)] = t
-                if kb is None:
-                    # full layer: each prompt's rows from its first unshared slot on
-                    offs = [plans[sq.seq_id][l].dst_offset for sq in admitted]
-                    segs = [(cu[s] + offs[s], cu[s + 1]) for s in range(len(admitted))]
-                    ks = torch.cat([k[a:b] for a, b in segs]); vs = torch.cat([v[a:b] for a, b in segs])
-                    cus = np.concatenate([[0], np.cumsum([b - a for a, b in segs])]).astype(np.int32)
-                    kvs.kvs_compact_paged(ks, vs, i32(cus), None, None, int(max(cus[1:] - cus[:-1])), k_pool,
-                                          v_pool, i32(tbl), dst_slot_offset=i32(offs))
-                    S = keep = None
-                else:
-                    S = kvs.kvs_window_score(q, k, lse, cu_d, max(lengths), w.alpha)
-                    kept = [plans[sq.seq_id][l].kept for sq in admitted]
-                    koff = np.concatenate([[0], np.cumsum(kept)]).astype(np.int32)
-                    keep = kvs.kvs_topk_select(S, cu_d, max(lengths), w.alpha, kb, i32(koff),
-                                               total_keep=int(koff[-1]))
-                    kvs.kvs_compact_paged(k, v, cu_d, keep, i32(koff), max(kept), k_pool, v_pool, i32(tbl))
-                torch.cuda.synchronize()
-                for s, sq in enumerate(admitted):
-                    if sq.seq_id in tracked:
-                        check_admission(w, l, sq, q, k, v, o, lse, S, keep, cu, s, admitted, plans, cache,
-                                        pools[l], oracle_cache)
+                admit_layer(w, l, admitted, plans, cache, pools[l], tracked, oracle_cache, stats)
             for sq in admitted:
                 live.append(sq.seq_id)
                 decoded[sq.seq_id] = 0
@@ -141,7 +123,7 @@ def test_continuous_mix_with_shared_prefixes():
                     ck, cv = oracle_cache[(sid, l)]
                     ck.append(bf16_bits(dk[i]))
                     cv.append(bf16_bits(dv[i]))
-                    if decoded[sid] in (0, 1, 17, 99) or sid in finished:
+                    if decoded[sid] in (0, 1, 17, 99, 255) or sid in finished:
                         kc = wl.bf16_bits_to_f64(np.stack(ck))
                         vc = wl.bf16_bits_to_f64(np.stack(cv))
                         o_ref, l_ref = oracle.decode_attention(bf16_to_f64(dq[i]), kc, vc)
@@ -162,6 +144,8 @@ def test_continuous_mix_with_shared_prefixes():
                 finished_tracked.append(sid)
             cache.finish(sid)
             live.remove(sid)
+        if it % 100 == 0:
+            _say(f"iteration {it}: {len(live)} live, {stats['reused']} prefix reuses so far")
     # the tracked sequences still live: their caches hold the kept prompt rows and every append
     for sid in sorted(tracked):
         if sid in live:
@@ -170,22 +154,104 @@ def test_continuous_mix_with_shared_prefixes():
                 gk, gv = gather_pools(pools[l][0], pools[l][1], cache.tables[(sid, l)], cache.length[(sid, l)])
                 np.testing.assert_array_equal(gk, np.stack(ck), err_msg=f"cache K seq {sid} layer {l}")
                 np.testing.assert_array_equal(gv, np.stack(cv), err_msg=f"cache V seq {sid} layer {l}")
+    admissions_per_slot = np.bincount([sq.slot for sq in all_seqs], minlength=w.num_seqs)
+    _say(f"done: {stats['reused']} prefix reuses ({stats['gathered_rows']} rows gathered), "
+         f"{stats['swaps']} copy-on-write swaps, admissions per slot {admissions_per_slot.min()}.."
+         f"{admissions_per_slot.max()}")
+    assert admissions_per_slot.min() >= 3, "every slot should turn over at least twice"
     assert finished_tracked, "a tracked sequence should have finished"
+    assert stats["reused"] > 0 and stats["swaps"] > 0
 
 
-def check_admission(w, l, sq, q, k, v, o, lse, S, keep, cu, s, admitted, plans, cache, pool, oracle_cache):
-    n, a0 = sq.n, int(cu[s])
+def admit_layer(w, l, admitted, plans, cache, pool, tracked, oracle_cache, stats):
+    """Prefill, score, select and compact one admission wave in layer l."""
+    P = w.prefix_len
+    k_pool, v_pool = pool
+    parts = [_prompt(w, l, sq) for sq in admitted]
+    k = torch.cat([p[1] for p in parts]); v = torch.cat([p[2] for p in parts])
+    lengths = [sq.n for sq in admitted]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    kb = w.budgets[l]
+    # prefixes created by this admission: written once, from the creating member's rows
+    for s, sq in enumerate(admitted):
+        if plans[sq.seq_id][l].new_prefix:
+            kvs.kvs_compact_paged(k[cu[s]:cu[s] + P].contiguous(), v[cu[s]:cu[s] + P].contiguous(), i32([0, P]),
+                                  None, None, P, k_pool, v_pool, i32([cache.prefix_blocks[l][sq.group]]))
+    # members of a live prefix read its rows back from the shared blocks and compute only their
+    # own rows (when those hold the whole window)
+    first = [P if (sq.n > P and cache.carries_prefix(l) and not plans[sq.seq_id][l].new_prefix
+                   and sq.n - P >= w.alpha) else 0 for sq in admitted]
+    reusers = [s for s in range(len(admitted)) if first[s]]
+    if reusers:
+        generated_k = [k[cu[s]:cu[s] + P].clone() for s in reusers]
+        generated_v = [v[cu[s]:cu[s] + P].clone() for s in reusers]
+        rows = torch.as_tensor([r for s in reusers for r in range(cu[s], cu[s] + P)], device="cuda")
+        k[rows] = float("nan")          # only the read-back can restore them
+        v[rows] = float("nan")
+        kvs.kvs_gather_paged(k_pool, v_pool, i32([cache.prefix_blocks[l][admitted[s].group] for s in reusers]),
+                             i32([P] * len(reusers)), i32([cu[s] for s in reusers]), P, k, v)
+        for s, gk, gv in zip(reusers, generated_k, generated_v):
+            assert torch.equal(k[cu[s]:cu[s] + P].view(torch.int16), gk.view(torch.int16)), \
+                f"prefix K read back for seq {admitted[s].seq_id} layer {l}"
+            assert torch.equal(v[cu[s]:cu[s] + P].view(torch.int16), gv.view(torch.int16)), \
+                f"prefix V read back for seq {admitted[s].seq_id} layer {l}"
+        stats["reused"] += len(reusers)
+        stats["gathered_rows"] += P * len(reusers)
+    q = torch.cat([p[0][first[s]:] for s, p in enumerate(parts)])
+    qlen = [n - f for n, f in zip(lengths, first)]
+    cu_q = np.concatenate([[0], np.cumsum(qlen)]).astype(np.int32)
+    cu_d = i32(cu)
+    if reusers:
+        o, lse = kvs.kvs_prefill_attn_lse_chunk(q, k, v, i32(cu_q), cu_d, max(qlen), max(lengths))
+    else:
+        o, lse = kvs.kvs_prefill_attn_lse(q, k, v, cu_d, max(lengths))
+    max_blocks = max(len(plans[sq.seq_id][l].table) for sq in admitted)
+    tbl = np.full((len(admitted), max_blocks), -1, np.int32)
+    for s, sq in enumerate(admitted):
+        t = plans[sq.seq_id][l].table
+        tbl[s, :len(t)] = t
+    if kb is None:
+        # full layer: each prompt's rows from its first unshared slot on
+        offs = [plans[sq.seq_id][l].dst_offset for sq in admitted]
+        segs = [(cu[s] + offs[s], cu[s + 1]) for s in range(len(admitted))]
+        ks = torch.cat([k[a:b] for a, b in segs]); vs = torch.cat([v[a:b] for a, b in segs])
+        cus = np.concatenate([[0], np.cumsum([b - a for a, b in segs])]).astype(np.int32)
+        kvs.kvs_compact_paged(ks, vs, i32(cus), None, None, int(max(cus[1:] - cus[:-1])), k_pool,
+                              v_pool, i32(tbl), dst_slot_offset=i32(offs))
+        S = keep = None
+    else:
+        if reusers:
+            S = kvs.kvs_window_score_chunk(q, k, lse, i32(cu_q), cu_d, max(lengths), w.alpha)
+        else:
+            S = kvs.kvs_window_score(q, k, lse, cu_d, max(lengths), w.alpha)
+        kept = [plans[sq.seq_id][l].kept for sq in admitted]
+        koff = np.concatenate([[0], np.cumsum(kept)]).astype(np.int32)
+        keep = kvs.kvs_topk_select(S, cu_d, max(lengths), w.alpha, kb, i32(koff), total_keep=int(koff[-1]))
+        kvs.kvs_compact_paged(k, v, cu_d, keep, i32(koff), max(kept), k_pool, v_pool, i32(tbl))
+        # each sharing member swaps the prefix entries its compaction writes
+        stats["swaps"] += sum(min(-(-plans[sq.seq_id][l].kept // 16), P // 16) for sq in admitted if sq.n > P)
+    torch.cuda.synchronize()
+    for s, sq in enumerate(admitted):
+        if sq.seq_id in tracked:
+            _say(f"check admission of seq {sq.seq_id} (n={sq.n}, group {sq.group}, rows from {first[s]}) "
+                 f"layer {l}")
+            check_admission(w, l, sq, q, k, v, o, lse, S, keep, cu, cu_q, first[s], s, admitted, plans, pool,
+                            oracle_cache)
+
+
+def check_admission(w, l, sq, q, k, v, o, lse, S, keep, cu, cu_q, first, s, admitted, plans, pool, oracle_cache):
+    n, a0, q0 = sq.n, int(cu[s]), int(cu_q[s])
     win = np.arange(n - min(w.alpha, n), n)
-    sample = np.random.default_rng(sq.seq_id + 31 * l).choice(n - len(win), size=min(24, n - len(win)),
-                                                                replace=False)
+    cand = np.arange(first, n - len(win))
+    sample = np.random.default_rng(sq.seq_id + 31 * l).choice(cand, size=min(24, len(cand)), replace=False)
     rows = np.unique(np.concatenate([sample, win]))
-    idx = a0 + torch.as_tensor(rows, device="cuda")
+    qidx = q0 + torch.as_tensor(rows - first, device="cuda")
     kf = bf16_to_f64(k[a0:a0 + n])
     vf = bf16_to_f64(v[a0:a0 + n])
-    qrows = bf16_to_f64(q[idx])
+    qrows = bf16_to_f64(q[qidx])
     O_ref, lse_ref, _, _ = oracle.causal_attention(qrows, kf, vf, rows=rows, q_holds_rows=True)
-    assert_rows_close(bf16_to_f64(o[idx]), O_ref, what=f"O seq {sq.seq_id} layer {l}")
-    assert_lse_close(lse[:, idx].cpu().numpy(), lse_ref, what=f"LSE seq {sq.seq_id} layer {l}")
+    assert_rows_close(bf16_to_f64(o[qidx]), O_ref, what=f"O seq {sq.seq_id} layer {l}")
+    assert_lse_close(lse[:, qidx].cpu().numpy(), lse_ref, what=f"LSE seq {sq.seq_id} layer {l}")
     kbits = bf16_bits(k[a0:a0 + n])
     vbits = bf16_bits(v[a0:a0 + n])
     kb = w.budgets[l]
@@ -196,7 +262,7 @@ def check_admission(w, l, sq, q, k, v, o, lse, S, keep, cu, s, admitted, plans, 
         wi = np.searchsorted(rows, win)
         S_ref = oracle.window_score(qrows[wi], kf, lse_ref[:, wi], w.alpha, window_only=True)
         Sg = S[:, a0:a0 + n].cpu().numpy().astype(np.float64)
-        assert_scores_close(Sg, S_ref, w.g, w.alpha, what=f"S seq {sq.seq_id} layer {l}")
+        assert_scores_close(Sg, S_ref, what=f"S seq {sq.seq_id} layer {l}")
         kept = [plans[x.seq_id][l].kept for x in admitted]
         koff = np.concatenate([[0], np.cumsum(kept)])
         kg = keep.cpu().numpy()[w.hkv * koff[s]: w.hkv * koff[s + 1]].reshape(w.hkv, kept[s])

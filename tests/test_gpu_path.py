@@ -63,7 +63,7 @@ def run_full_path(w: wl.Workload, layer: int, check_decode_steps, decode_steps: 
     S = kvs.kvs_window_score(q, k, lse, cu_d, n, alpha)
     S_ref = oracle.window_score(qf, kf, lse_ref, alpha)
     S_g = S.cpu().numpy().astype(np.float64)
-    assert_scores_close(S_g, S_ref, G, alpha)
+    assert_scores_close(S_g, S_ref)
     np.testing.assert_allclose(S_g.sum(1), G * min(alpha, n), rtol=1e-4)   # each window row sums to one
 
     # ---- step 3: top-k
@@ -182,7 +182,7 @@ def test_prefill_ragged_batch(d, hq, hkv):
         for s, n in enumerate(lengths):
             a, b = cu[s], cu[s + 1]
             S_ref = oracle.window_score(_f64(qb[a:b]), _f64(kb[a:b]), lse32[:, a:b], alpha)
-            assert_scores_close(S[:, a:b].astype(np.float64), S_ref, hq // hkv, alpha, what=f"S seq {s} a={alpha}")
+            assert_scores_close(S[:, a:b].astype(np.float64), S_ref, what=f"S seq {s} a={alpha}")
 
 
 def test_topk_exact_with_ties_and_budgets():

@@ -1,7 +1,7 @@
 """GPU parity at the full sizes of the multi-layer workloads, through the C ABI.
 
   * 32 layers x 20 concurrent prompts of U[1000, 4000] tokens (layers 0-2 full, 3-31 k=512,
-    alpha=32), then batched decode at concurrency 20;
+    alpha=32), then 500 batched decode steps at concurrency 20 on layers 0, 3 and 31;
   * 4 prompts x 30000 tokens (alpha=64, k=3000 on layers 3-31), then 500 decode steps.
 
 Inputs are drawn on the device (seeded); the oracle gets the slices it needs copied back.
@@ -125,7 +125,7 @@ class LayerRun:
             return
         wi = np.searchsorted(rows, win)
         S_ref = oracle.window_score(qrows[wi], kf, lse_ref[:, wi], w.alpha, window_only=True)
-        assert_scores_close(self.S[:, a0:a0 + n], S_ref, w.g, w.alpha, what=f"S layer {self.layer} seq {s}")
+        assert_scores_close(self.S[:, a0:a0 + n], S_ref, what=f"S layer {self.layer} seq {s}")
         for g in range(w.hkv):
             assert_keep_matches(self.keep[s][g], oracle.select_keep(S_ref[g], n, w.alpha, self.k_budget), S_ref[g],
                                 n, w.alpha, self.k_budget, what=f"keep layer {self.layer} seq {s} head {g}")
@@ -177,12 +177,13 @@ class LayerRun:
         return max(self.kept) + steps
 
 
+@pytest.mark.timeout(900)
 def test_32_layers_concurrency_20():
     w = wl.WORKLOADS[3]
     lengths = w.seq_lengths()
     seq_ids = list(range(w.num_seqs))
     _say(f"32 layers x {len(lengths)} prompts, lengths {min(lengths)}..{max(lengths)}")
-    dec_steps = 48
+    dec_steps = w.decode_steps
     for layer in range(w.n_layers):
         full_check = layer in (0, 3, 31)
         _say(f"layer {layer} (full check: {full_check})")
@@ -193,11 +194,13 @@ def test_32_layers_concurrency_20():
         if full_check:
             for s in range(len(lengths)):
                 run.check_oracle(s, n_rows=24, seed=100 * layer + s)
-            run.decode(dec_steps, check_steps={0, 1, 15, 16, 47}, seq_ids=seq_ids, check_seqs=range(len(lengths)))
+            run.decode(dec_steps, check_steps={0, 1, 15, 16, 249, 499}, seq_ids=seq_ids,
+                       check_seqs=range(len(lengths)))
         del run
         torch.cuda.empty_cache()
 
 
+@pytest.mark.timeout(600)
 def test_long_context_4x30000():
     w = wl.WORKLOADS[4]
     lengths = w.seq_lengths()

@@ -260,6 +260,16 @@ def mix_sequence(w: Workload, seq_id: int, slot: int) -> MixSequence:
     return MixSequence(seq_id, slot, slot // w.group_size, n, life)
 
 
+def mix_pool_sizes(w: Workload) -> list:
+    """Blocks per layer for the continuous-batch trace: full layers hold every slot at its longest
+    prompt plus decode and the group prefixes; compressed layers the budget plus decode per slot,
+    the prefixes and the transient copy-on-write blocks, with room to spare."""
+    full = w.num_seqs * (-(-(w.len_range[1] + w.lifetime_range[1]) // BLOCK_SIZE)) + 8 * (w.prefix_len // 16) + 64
+    return [full if k is None else
+            w.num_seqs * (-(-(k + w.lifetime_range[1]) // BLOCK_SIZE)) + 16 * (w.prefix_len // 16) + 64
+            for k in w.budgets]
+
+
 def mix_trace(w: Workload, iterations: int):
     """Per iteration: (admitted sequences, finished seq ids).
 

@@ -35,6 +35,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+ALL_SECTIONS = ("ceiling", "lse", "scale", "fp8", "prefix", "layers32", "evict", "prompt3", "prompt4", "prompt5",
+                "memory")
 
 
 def parse():
@@ -52,8 +54,8 @@ def parse():
                         "decode steps as another (the launch mode of a serving loop); loop: one host launch "
                         "per kernel")
     p.add_argument("--sections", default="all",
-                   help="comma list of the reports to add after the timed step: scale, fp8, prefix, layers32, "
-                        "evict (default all); the timed step and its roofline always run")
+                   help="comma list of the reports to add after the timed step: " + ", ".join(ALL_SECTIONS) +
+                        " (default all); the timed step and its roofline always run")
     return p.parse_args()
 
 
@@ -214,36 +216,24 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    # Per-kernel durations of the prompt-side kernels: in graph mode from an eager pass with an
-    # event after each launch (so they include the launch gaps the graph avoids).
-    eager = recs
-    if pre_graph is not None:
-        eager = []
-        for _ in range(max(args.steps, 3)):
-            rec = {}
-            e = ev()
-            e.record(stream)
-            rec["prefill_begin"] = [e]
-
-            def mark(key, rec=rec):
-                e = ev()
-                e.record(stream)
-                rec.setdefault(key, []).append(e)
-            prefill_compress(mark)
-            eager.append(rec)
-        torch.cuda.synchronize()
+    # Per-kernel durations of the prompt-side kernels: each kernel alone, captured as a HIP graph
+    # of back-to-back launches (the same inputs every launch), so no host launch gap is counted.
+    launches = {
+        "prefill_attn_lse": lambda: kvs.kvs_prefill_attn_lse(q, k, v, cu_d, n, o=o, lse=lse),
+        "window_score": lambda: kvs.kvs_window_score(q, k, lse, cu_d, n, alpha, scores=S),
+        "topk_select": lambda: kvs.kvs_topk_select(S, cu_d, n, alpha, kb, keep_off, keep_idx=keep),
+        "compact_paged": lambda: kvs.kvs_compact_paged(k, v, cu_d, keep, keep_off, k_eff, k_pool, v_pool, tbl),
+    }
+    kernel_us = {kname: kernel_graph_us(torch, fn, 10 if kname == "prefill_attn_lse" else 50)
+                 for kname, fn in launches.items()}
 
     # ---- per-kernel GPU durations (ms) from the timed steps' events
     def span(rec, a, b, i=0, j=0):
         return rec[a][i].elapsed_time(rec[b][j])
 
-    dur = {"prefill_attn_lse": [], "window_score": [], "topk_select": [], "compact_paged": [], "paged_decode": []}
+    dur = {kname: [us * 1e-3] for kname, us in kernel_us.items()}
+    dur["paged_decode"] = []
     pre_phase, dec_phase = [], []
-    for rec in eager:
-        dur["prefill_attn_lse"].append(span(rec, "prefill_begin", "prefill_end"))
-        dur["window_score"].append(span(rec, "prefill_end", "score_end"))
-        dur["topk_select"].append(span(rec, "score_end", "topk_end"))
-        dur["compact_paged"].append(span(rec, "topk_end", "compact_end"))
     for rec in recs:
         de = rec["decode_end"]
         if graph is not None:     # one event pair around the 500 captured steps
@@ -277,7 +267,11 @@ def main():
                             "frac": round(achieved / peak, 4),
                             "traffic": measured_traffic(kname, src),
                             "avg_launch_us": round(avg_ms[kname] * 1e3, 2),
-                            "algorithmic_per_launch": amount}
+                            "algorithmic_per_launch": amount,
+                            "timed_as": ("one decode call (decode kernel, plus the merge kernel when the "
+                                         "context is split) inside the 500-step graph of the timed steps"
+                                         if kname == "paged_decode" else
+                                         "graph of back-to-back launches of this kernel alone")}
         if bound == "mfma":
             rooflines[kname]["counters"] = measured_mfma(kname, src)
     dominant = max(per_step_ms, key=per_step_ms.get)
@@ -314,23 +308,49 @@ def main():
         "kernel_share_ms_per_step": {kk: round(vv, 4) for kk, vv in per_step_ms.items()},
     }
 
-    sections = {"scale", "fp8", "prefix", "layers32", "evict"} if args.sections == "all" else \
+    sections = set(ALL_SECTIONS) if args.sections == "all" else \
         set(x.strip() for x in args.sections.split(",") if x.strip())
+    unknown = sections - set(ALL_SECTIONS)
+    if unknown:
+        raise SystemExit(f"unknown sections: {sorted(unknown)}")
+    def progress(what):
+        print(f"[bench] {what}", file=sys.stderr, flush=True)
+
+    progress(f"timed step done: {ms_per_step:.3f} ms per step")
+    if "ceiling" in sections:
+        progress("ceiling")
+        line["hbm_ceiling"] = hbm_ceiling(kvs, torch)
+    if "lse" in sections:
+        progress("lse")
+        line["lse_output_cost"] = lse_output_cost(kvs, torch, q, k, v, cu_d, n, o, lse)
     if "scale" in sections:
+        progress("scale")
         line["decode_at_scale"] = decode_at_scale(kvs, torch, wl, 100)
     if "fp8" in sections:
+        progress("fp8")
         line["fp8_decode_at_scale"] = decode_at_scale(kvs, torch, wl, 100, fp8=True)
         line["fp8_layer"] = fp8_layer(kvs, torch, wl, w, k, v, cu_d, keep, keep_off, steps_dec)
     if "prefix" in sections:
+        progress("prefix")
         line["prefix_reuse"] = prefix_reuse(kvs, torch, wl, w, q, k, v)
     if "layers32" in sections:
+        progress("layers32")
         line["decode_32_layers"] = decode_32_layers(kvs, torch, wl, 10)
         line["fp8_decode_32_layers"] = decode_32_layers(kvs, torch, wl, 10, fp8=True)
     if "evict" in sections:
         # the prefill-side pass of the last step left the compressed cache in the pools
         kvs.kvs_compact_paged(k, v, cu_d, keep, keep_off, k_eff, k_pool, v_pool, tbl)
+        progress("evict")
         line["decode_evict"] = decode_evict(kvs, torch, wl, w, k_pool, v_pool, tbl, S, cu_d, keep, keep_off, 200)
+    for cid in (3, 4, 5):
+        if f"prompt{cid}" in sections:
+            progress("prompt side")
+            line[f"prompt_side_w{cid}"] = prompt_side(kvs, torch, wl, cid)
+    if "memory" in sections:
+        progress("memory")
+        line["paged_memory"] = paged_memory(wl)
     if not args.no_cpu_baseline:
+        progress("cpu baseline")
         line["cpu_baseline"] = cpu_baseline(w, qb, kbits, vb, dec, args.cpu_budget_s)
     print(json.dumps(line), flush=True)
 
@@ -379,6 +399,8 @@ def decode_at_scale(kvs, torch, wl, steps, fp8=False):
     gbs = nbytes / (us * 1e-6) / 1e9
     return {"workload": f"{B} sequences x {kept}-{kept + steps} cached tokens, {hq}q/{hkv}kv heads, d={d}, "
                         f"{steps} decode steps with append (HIP graph)" + (", 8-bit E4M3 cache" if fp8 else ""),
+            "resident_in": "Infinity Cache (MALL): the same cache of about %d MB is re-read every step, below "
+                           "the 256 MB MALL, so this rate is not an HBM rate" % round(nbytes / 1e6),
             "us_per_step": round(us, 3), "algorithmic_bytes_per_step": int(nbytes),
             "achieved_GBs": round(gbs, 1), "peak_GBs": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4),
             "tok_s": round(B / (us * 1e-6), 1)}
@@ -418,6 +440,228 @@ def _graph_time_us(torch, run, steps, reps=3):
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1e3 / (reps * steps)
+
+
+def kernel_graph_us(torch, launch, count, replays=5, warm_ms=40.0):
+    """us per launch of one kernel: `count` back-to-back launches captured as one HIP graph.
+    The graph is replayed for about warm_ms first (the chip's clock settles under the kernel's
+    own load), then `replays` replays are timed one by one; the median replay is returned."""
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        for _ in range(count):
+            launch()                           # warm outside capture
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(count):
+            launch()
+    t0 = time.perf_counter()
+    while True:
+        graph.replay()
+        torch.cuda.synchronize()
+        if (time.perf_counter() - t0) * 1e3 >= warm_ms:
+            break
+    times = []
+    for _ in range(replays):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3 / count)
+    return float(sorted(times)[len(times) // 2])
+
+
+def hbm_ceiling(kvs, torch, gib=4):
+    """The practical memory ceilings beside the published 8 TB/s: a hand-written streaming-read
+    kernel (16 bytes per lane, four loads in flight) over a buffer far larger than the 256 MB
+    Infinity Cache, best over a few grid sizes, and a plain device copy of the same size."""
+    dev = torch.device("cuda:0")
+    nbytes = gib << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    best = None
+    per_grid = {}
+    stream = torch.cuda.current_stream()
+    for grid in (2048, 4096, 8192, 16384, 32768):
+        sink = torch.empty(grid, dtype=torch.int32, device=dev)
+        kvs.kvs_probe_stream_read(buf, grid, sink=sink)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(3):
+            kvs.kvs_probe_stream_read(buf, grid, sink=sink)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        gbs = 3 * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        per_grid[str(grid)] = round(gbs, 1)
+        best = gbs if best is None else max(best, gbs)
+    half = nbytes // 2
+    src, dst = buf[:half], buf[half:]
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(3):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 3 * 2 * half / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    return {"read_GBs": round(best, 1), "read_frac_of_peak": round(best / HBM_PEAK_GBS, 4),
+            "read_GBs_by_grid": per_grid, "read_bytes": nbytes,
+            "copy_GBs_read_plus_write": round(copy_gbs, 1), "copy_bytes_each_way": half,
+            "kernel": "kvs_probe_stream_read (16-byte nontemporal loads, 4 in flight per lane, 256 threads)"}
+
+
+def lse_output_cost(kvs, torch, q, k, v, cu_d, n, o, lse, rounds=3):
+    """What returning the row statistics costs: the bench layer's prefill with the LSE written
+    (the modified kernel) against the same kernel writing only O (the unmodified attention),
+    alternated `rounds` times, each a graph of 10 back-to-back launches."""
+    with_lse, without = [], []
+    for _ in range(rounds):
+        with_lse.append(kernel_graph_us(torch, lambda: kvs.kvs_prefill_attn_lse(q, k, v, cu_d, n, o=o, lse=lse), 10))
+        without.append(kernel_graph_us(torch, lambda: kvs.kvs_prefill_attn_lse(q, k, v, cu_d, n, o=o,
+                                                                                skip_lse=True), 10))
+    a, b = min(with_lse), min(without)
+    return {"workload": "bench layer prefill, n=4000, 32q/8kv heads, d=128",
+            "us_with_lse": round(a, 2), "us_without": round(b, 2),
+            "extra_us": round(a - b, 2), "extra_frac": round((a - b) / b, 4),
+            "lse_bytes_written": int(lse.numel() * 4), "o_bytes_written": int(o.numel() * 2),
+            "samples_us": {"with_lse": [round(x, 2) for x in with_lse], "without": [round(x, 2) for x in without]}}
+
+
+def prompt_side(kvs, torch, wl, cid):
+    """Prefill+compress of a multi-prompt workload, per layer class, each kernel alone as a graph
+    of back-to-back launches.  Prefill attention and the window score do not depend on the
+    budget, so they are timed once; top-k and compaction are timed for every distinct budget
+    (keep-all compaction for the full layers).  The 32-layer figure sums the layers' kernels:
+    prompt tokens / (32 prefills + a score, top-k and compaction per compressed layer + a
+    keep-all compaction per full layer).  Workload 5 is its first admission wave (64 prompts,
+    each prefilled whole: prefix reuse would only lower the work)."""
+    import numpy as np
+    dev = torch.device("cuda:0")
+    w = wl.WORKLOADS[cid]
+    if cid == 5:
+        lengths = [wl.mix_sequence(w, i, i).n for i in range(w.num_seqs)]
+    else:
+        lengths = w.seq_lengths()
+    hq, hkv, d, alpha = w.hq, w.hkv, w.d, w.alpha
+    q, k, v, cu = wl.device_batch(w, 3, lengths, list(range(len(lengths))), device=dev)
+    cu_d = torch.from_numpy(cu).to(dev)
+    T, max_n = int(cu[-1]), max(lengths)
+    o = torch.empty_like(q)
+    lse = torch.empty(hq, T, dtype=torch.float32, device=dev)
+    S = torch.empty(hkv, T, dtype=torch.float32, device=dev)
+    big = T > 200000
+    t_pre = kernel_graph_us(torch, lambda: kvs.kvs_prefill_attn_lse(q, k, v, cu_d, max_n, o=o, lse=lse),
+                            2 if big else 4)
+    t_score = kernel_graph_us(torch, lambda: kvs.kvs_window_score(q, k, lse, cu_d, max_n, alpha, scores=S), 10)
+    flops = sum(2.0 * d * hq * n * (n + 1) for n in lengths)
+    score_bytes = sum(n * hkv * d * 2 + min(alpha, n) * hq * (2 * d + 4) + 4 * hkv * n for n in lengths)
+    per_budget = {}
+    layer_us = []
+    for kb in sorted(set(w.budgets), key=lambda x: -1 if x is None else x):
+        kept = [n if kb is None or kb >= n else kb for n in lengths]
+        nbs = [-(-c // 16) for c in kept]
+        nb_total = sum(nbs)
+        k_pool, v_pool = kvs.new_pools(nb_total, hkv, d, device=dev)
+        perm = np.random.default_rng(cid).permutation(nb_total).astype(np.int32)
+        tbl = np.full((len(lengths), max(nbs)), -1, np.int32)
+        at = 0
+        for i, nb in enumerate(nbs):
+            tbl[i, :nb] = perm[at:at + nb]
+            at += nb
+        tbl = torch.from_numpy(tbl).to(dev)
+        koff = torch.from_numpy(np.concatenate([[0], np.cumsum(kept)]).astype(np.int32)).to(dev)
+        comp_bytes = 8 * sum(kept) * hkv * d
+        if kb is None:
+            t_topk = 0.0
+            t_comp = kernel_graph_us(torch, lambda: kvs.kvs_compact_paged(k, v, cu_d, None, None, max_n, k_pool,
+                                                                          v_pool, tbl), 3 if big else 10)
+            rec = {"compact_us": round(t_comp, 2)}
+        else:
+            keep = torch.empty(hkv * sum(kept), dtype=torch.int32, device=dev)
+            t_topk = kernel_graph_us(torch, lambda: kvs.kvs_topk_select(S, cu_d, max_n, alpha, kb, koff,
+                                                                         keep_idx=keep), 10)
+            t_comp = kernel_graph_us(torch, lambda: kvs.kvs_compact_paged(k, v, cu_d, keep, koff, max(kept), k_pool,
+                                                                          v_pool, tbl), 10)
+            rec = {"topk_us": round(t_topk, 2), "compact_us": round(t_comp, 2),
+                   "topk_bytes": 4 * hkv * (T + sum(kept))}
+        rec.update({"kept_tokens_per_head": int(sum(kept)), "compact_bytes": int(comp_bytes),
+                    "compact_GBs": round(comp_bytes / (t_comp * 1e-6) / 1e9, 1),
+                    "compact_frac_of_peak": round(comp_bytes / (t_comp * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                    "layers": sum(1 for x in w.budgets if x == kb)})
+        per_budget["full" if kb is None else f"k={kb}"] = rec
+        layer = t_pre + (t_comp if kb is None else t_score + t_topk + t_comp)
+        layer_us += [layer] * rec["layers"]
+        del k_pool, v_pool
+    total_us = sum(layer_us)
+    del q, k, v, o
+    torch.cuda.empty_cache()
+    names = {3: "20 prompts U[1000,4000]", 4: "4 prompts x 30000", 5: "64 prompts log-uniform [512,32768] "
+             "(first admission wave)"}
+    budgets = "layers 0-2 full, " + ("3-31 k=%d" % w.budgets[3] if cid != 5 else "pyramid k 2048..128 on 3-31")
+    return {"workload": f"{names[cid]}, {w.n_layers} layers ({budgets}), alpha={alpha}, {hq}q/{hkv}kv heads, d={d}",
+            "prompt_tokens": T,
+            "prefill_us": round(t_pre, 2), "prefill_TFLOPs": round(flops / (t_pre * 1e-6) / 1e12, 1),
+            "prefill_frac_of_mfma_peak": round(flops / (t_pre * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "prefill_flops": flops,
+            "score_us": round(t_score, 2), "score_GBs": round(score_bytes / (t_score * 1e-6) / 1e9, 1),
+            "per_budget": per_budget,
+            "us_32_layers": round(total_us, 1),
+            "prompt_tok_s_32_layers": round(T / (total_us * 1e-6), 1),
+            "prompt_tok_s_per_layer": round(T / (total_us * 1e-6) * w.n_layers, 1)}
+
+
+def paged_memory(wl, iterations=1000):
+    """Slots taken from the pool that hold no token ([PAG] "How paging works": with blocks only
+    the tail of each table's last block is empty).  Workload 3: the 20 prompts' tables over
+    the 500 decode steps, every layer.  Workload 5: the product's cache manager driven over the
+    continuous-batch trace (shared prefixes counted once), sampled every 10 iterations; beside
+    it, what reserving each slot's longest possible sequence contiguously would leave empty."""
+    import numpy as np
+    from kv_cache_sparsification_amd.cache_manager import PagedKVCache
+    w3 = wl.WORKLOADS[3]
+    lens3 = w3.seq_lengths()
+    used = taken = 0
+    for kb in w3.budgets:
+        for n in lens3:
+            c = n if kb is None or kb >= n else kb
+            L = c + np.arange(w3.decode_steps + 1)
+            used += int(L.sum())
+            taken += int((16 * (-(-L // 16))).sum())
+    w5 = wl.WORKLOADS[5]
+    cache = PagedKVCache(w5.budgets, wl.mix_pool_sizes(w5), prefix_len=w5.prefix_len)
+    live = []
+    u5 = t5 = 0
+    reserved_used = 0
+    for it, (admitted, finished) in enumerate(wl.mix_trace(w5, iterations)):
+        for sq in admitted:
+            cache.admit(sq.seq_id, sq.group, sq.n)
+            live.append(sq.seq_id)
+        for sid in live:
+            for l in range(w5.n_layers):
+                cache.append(sid, l)
+        if it % 10 == 5:
+            for l in range(w5.n_layers):
+                a, b = cache.slot_usage(l)
+                u5 += a
+                t5 += b
+            reserved_used += sum(cache.length[(sid, l)] for sid in live for l in range(w5.n_layers))
+        for sid in finished:
+            cache.finish(sid)
+            live.remove(sid)
+    samples = len(range(5, iterations, 10))
+    reserve = samples * w5.num_seqs * w5.n_layers * (w5.len_range[1] + w5.lifetime_range[1])
+    return {"w3_tail_slot_frac": round(1 - used / taken, 5),
+            "w3_note": "20 prompts x 32 layers, every decode step 0..500",
+            "w5_tail_slot_frac": round(1 - u5 / t5, 5),
+            "w5_contiguous_reservation_waste_frac": round(1 - reserved_used / reserve, 4),
+            "w5_note": f"continuous-batch trace, {iterations} iterations sampled every 10, 32 layers; the "
+                       "reservation figure assumes each slot holds room for 32768 + 500 tokens in every layer"}
 
 
 def fp8_layer(kvs, torch, wl, w, k, v, cu_d, keep, keep_off, steps):
@@ -638,14 +882,28 @@ def cpu_baseline(w, qb, kbits, vb, dec, budget_s):
     the rate is scaled from the groups done to the full layer.  Decode: oracle decode steps
     over the compressed cache (all heads), as many of the 500 as fit the rest of the budget.
     """
+    from threadpoolctl import threadpool_limits
+    threads = host_cores()
+    with threadpool_limits(limits=threads):
+        return _cpu_baseline(w, qb, kbits, vb, dec, budget_s, threads)
+
+
+def host_cores() -> int:
+    """Cores this process may use: its affinity mask, capped by a cgroup CPU quota if one is set."""
+    cores = len(os.sched_getaffinity(0))
+    try:
+        quota, period = open("/sys/fs/cgroup/cpu.max").read().split()[:2]
+        if quota != "max":
+            cores = min(cores, max(1, math.ceil(int(quota) / int(period))))
+    except (OSError, ValueError):
+        pass
+    return cores
+
+
+def _cpu_baseline(w, qb, kbits, vb, dec, budget_s, threads):
     import numpy as np
     import oracle
     import workloads as wl
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
     n, alpha, kb, G, hkv = w.fixed_len, w.alpha, w.budgets[0], w.g, w.hkv
     k_eff = min(kb, n)
     f = wl.bf16_bits_to_f64
@@ -687,6 +945,7 @@ def cpu_baseline(w, qb, kbits, vb, dec, budget_s):
             "sample": f"prefill+compress of {groups} of {hkv} KV-head groups of the n={n} layer "
                       f"({t_pre:.2f} s, scaled to the layer); decode: {done} of {len(dec)} steps ({t_dec:.2f} s)",
             "decode_value": round(done / t_dec, 2),
+            "cores_note": "len(os.sched_getaffinity(0)), capped by the cgroup CPU quota; BLAS threads set to it",
             "cpu_model": _cpu_model()}
 
 

@@ -74,7 +74,9 @@ const char* kvs_version(void);
  * In:  q [total][hq][d], k, v [total][hkv][d] bf16; cu_seqlens [num_seqs+1] int32 (device).
  *      max_seqlen >= every n_s; total_tokens = cu_seqlens[num_seqs]; scale > 0 (1/sqrt(d)).
  * Out: o [total][hq][d] bf16 (round to nearest even); lse [hq][total_tokens] fp32 natural
- *      log; rowmax_opt, ell_opt [hq][total_tokens] fp32 (m_j and l_j; NULL to skip).
+ *      log; rowmax_opt, ell_opt [hq][total_tokens] fp32 (m_j and l_j; NULL to skip).  With
+ *      lse NULL as well the call is the unmodified attention (first Fig. 7): nothing but o
+ *      is written, which measures what returning the statistics costs.
  * Errors: KVS_E_INVAL on a bad shape or when max_seqlen * hkv * d * 2 exceeds 2^31 - 1 (one
  *         prompt's K or V rows are addressed with 32-bit byte offsets), KVS_E_HIP if the
  *         launch fails.
@@ -334,6 +336,18 @@ int kvs_paged_decode_scored_fp8(const void* q, void* k_pool, void* v_pool, float
  */
 int kvs_copy_blocks_fp8(void* k_pool, void* v_pool, float* k_scale, float* v_scale, int num_blocks, int hkv, int d,
                         const int32_t* src_dst_pairs, int n_pairs, void* stream);
+
+/*
+ * kvs_probe_stream_read - measurement helper: read `bytes` of device memory once, 16 bytes
+ *   per lane with four loads in flight, and fold the words per workgroup.  It gives the
+ *   read rate a plain streaming kernel reaches, the practical ceiling the memory-bound
+ *   steps (compaction, paged decode) are compared with beside the published HBM peak.
+ * In:  buf device, 16-byte aligned; bytes a positive multiple of 16; grid workgroups of 256
+ *      threads (1 .. 2^20).  sink: device array of grid words, written only where a
+ *      workgroup's folded word equals key (the caller picks a key that does not occur).
+ * Errors: KVS_E_INVAL on a NULL pointer, misalignment or a bad size; KVS_E_HIP on launch failure.
+ */
+int kvs_probe_stream_read(const void* buf, size_t bytes, int grid, uint32_t key, uint32_t* sink, void* stream);
 
 /*
  * Host block allocator.  [PAG] "How paging works": a request gets a new block only when

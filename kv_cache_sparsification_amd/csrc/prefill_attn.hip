@@ -379,7 +379,7 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void prefill_kernel(
       }
     if (half == 0) {
       const size_t li = (size_t)h * total_tokens + base + row;
-      lse[li] = (m_ref + log2f(l)) * kLn2;
+      if (lse) lse[li] = (m_ref + log2f(l)) * kLn2;
       if (rowmax) rowmax[li] = m_true * kLn2;
       if (ell) ell[li] = l * __builtin_amdgcn_exp2f(m_ref - m_true);   // sum of exp(s - rowmax)
     }
@@ -395,7 +395,7 @@ static int run_prefill(const char* name, const void* q, const void* k, const voi
                        const int32_t* cu_seqlens_k, int num_seqs, int total_tokens, int max_seqlen, int max_seqlen_k,
                        int hq, int hkv, int d, float scale, void* o, float* lse, float* rowmax_opt, float* ell_opt,
                        void* stream) {
-  if (!q || !k || !v || !cu_seqlens || !o || !lse) return fail(KVS_E_INVAL, "%s: NULL tensor", name);
+  if (!q || !k || !v || !cu_seqlens || !o) return fail(KVS_E_INVAL, "%s: NULL tensor", name);
   if (num_seqs < 0 || total_tokens < 0 || max_seqlen < 0 || max_seqlen_k < 0 || hq <= 0 || hkv <= 0 || hq % hkv ||
       hq / hkv > 16 || (d != 64 && d != 128) || !(scale > 0.f))
     return fail(KVS_E_INVAL, "%s: bad shape (hq=%d hkv=%d d=%d)", name, hq, hkv, d);

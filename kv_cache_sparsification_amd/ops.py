@@ -35,8 +35,9 @@ def _stream(stream) -> int:
 
 
 def kvs_prefill_attn_lse(q, k, v, cu_seqlens, max_seqlen: int, scale: Optional[float] = None, o=None, lse=None,
-                         rowmax=None, ell=None, stream=None):
-    """Causal attention + LSE.  q [T][Hq][d], k/v [T][Hkv][d] bf16; returns (o, lse [Hq][T])."""
+                         rowmax=None, ell=None, stream=None, skip_lse: bool = False):
+    """Causal attention + LSE.  q [T][Hq][d], k/v [T][Hkv][d] bf16; returns (o, lse [Hq][T]).
+    skip_lse: the plain attention, writing only o (returns (o, None))."""
     _dev(q, torch.bfloat16, "q"); _dev(k, torch.bfloat16, "k"); _dev(v, torch.bfloat16, "v")
     _dev(cu_seqlens, torch.int32, "cu_seqlens")
     T, hq, d = q.shape
@@ -44,13 +45,17 @@ def kvs_prefill_attn_lse(q, k, v, cu_seqlens, max_seqlen: int, scale: Optional[f
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     o = torch.empty_like(q) if o is None else _dev(o, torch.bfloat16, "o")
-    lse = torch.empty(hq, T, device=q.device, dtype=torch.float32) if lse is None else _dev(lse, torch.float32, "lse")
+    if skip_lse:
+        lse = None
+    else:
+        lse = torch.empty(hq, T, device=q.device, dtype=torch.float32) if lse is None else \
+            _dev(lse, torch.float32, "lse")
     for name, t in (("rowmax", rowmax), ("ell", ell)):
         if t is not None:
             _dev(t, torch.float32, name)
     check(lib.kvs_prefill_attn_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(),
                                    cu_seqlens.numel() - 1, T, int(max_seqlen), hq, hkv, d, float(scale),
-                                   o.data_ptr(), lse.data_ptr(), _ptr(rowmax), _ptr(ell), _stream(stream)))
+                                   o.data_ptr(), _ptr(lse), _ptr(rowmax), _ptr(ell), _stream(stream)))
     return o, lse
 
 
@@ -370,3 +375,15 @@ def kvs_paged_decode_scored_fp8(q, k_pool, v_pool, k_scale, v_scale, block_table
                                           _ptr(new_v), _ptr(dst_slots), slot_scores.data_ptr(), slot_scores.shape[2],
                                           o.data_ptr(), _ptr(lse), workspace.data_ptr(), ws_bytes, _stream(stream)))
     return o
+
+
+# ---- measurement helper
+def kvs_probe_stream_read(buf, grid: int, sink=None, key: int = 0x9E3779B9, stream=None):
+    """Read every byte of the contiguous device tensor buf once (the streaming-read ceiling probe)."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf: contiguous device tensor expected")
+    if sink is None:
+        sink = torch.empty(grid, dtype=torch.int32, device=buf.device)
+    check(lib.kvs_probe_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), int(grid), int(key),
+                                    sink.data_ptr(), _stream(stream)))
+    return sink

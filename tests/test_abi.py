@@ -58,6 +58,11 @@ def test_host_validation_rejects_before_launch():
     # empty work is a no-op that launches nothing
     assert L.kvs_prefill_attn_lse(fake, fake, fake, fake, 0, 0, 0, 8, 2, 128, 0.1, fake, fake, None, None, None) == 0
     assert L.kvs_copy_blocks(fake, fake, 4, 2, 128, fake, 0, None) == 0
+    # the read probe: sizes and alignment are checked on the host
+    assert L.kvs_probe_stream_read(fake, 100, 64, 0, fake, None) == -1          # not a multiple of 16
+    assert L.kvs_probe_stream_read(fake + 8, 1024, 64, 0, fake, None) == -1     # misaligned
+    assert L.kvs_probe_stream_read(fake, 1024, 0, 0, fake, None) == -1          # empty grid
+    assert L.kvs_probe_stream_read(None, 1024, 64, 0, fake, None) == -1
 
 
 def test_workspace_size_policy():

@@ -383,3 +383,19 @@ def test_decode_ignores_unwritten_slots(fp8, d, hq, hkv, lens):
             o_ref, l_ref = oracle.decode_attention(_f64(qb[b]), kc, vc)
             assert_rows_close(og[b], o_ref, what=f"decode b={b} append={append}")
             assert_lse_close(lg[b], l_ref, what=f"decode lse b={b} append={append}")
+
+
+def test_prefill_without_statistics_writes_only_o():
+    """With the LSE output left out (the unmodified attention, measured against the one that
+    returns its statistics) the call runs and O is bit-identical."""
+    w = wl.WORKLOADS[2]
+    n = 1000
+    _say(f"prefill without LSE: n={n}, 32/8 heads, d=128")
+    qb, kb, vb, cu = wl.prefill_batch(w, 0, [n])
+    q, k, v = to_dev_bf16(qb), to_dev_bf16(kb), to_dev_bf16(vb)
+    cu_d = i32(cu)
+    o1, lse = kvs.kvs_prefill_attn_lse(q, k, v, cu_d, n)
+    o2, none = kvs.kvs_prefill_attn_lse(q, k, v, cu_d, n, skip_lse=True)
+    torch.cuda.synchronize()
+    assert none is None
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))

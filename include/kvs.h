@@ -332,6 +332,27 @@ int kvs_paged_decode_scored_fp8(const void* q, void* k_pool, void* v_pool, float
                                 void* o, float* lse_opt, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kvs_paged_decode_noalloc - kvs_paged_decode for callers that cannot allocate device memory
+ *   (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * Same arguments, meaning, layouts and results as kvs_paged_decode, without the workspace:
+ * the split partials go to a scratch array of 16 MiB that the library holds on every device
+ * it runs on until the process ends (its address is looked up on the first call on a device).
+ * The call uses the scratch of the device current on the calling thread; the stream (NULL for
+ * the default one) must belong to that device.  Nothing needs to start at zero there: every
+ * call writes each partial it reads.  All calls on one device share that array, so calls that
+ * overlap on one device (concurrent streams or threads) race; calls in one stream do not.
+ * Nothing is allocated: no hipMalloc, no hipFree, no allocating library routine.
+ * Errors: as kvs_paged_decode; KVS_E_INVAL also when kvs_paged_decode_workspace_size for the
+ * shape exceeds 16 MiB (use kvs_paged_decode with a workspace), or when the stream belongs to
+ * another device; KVS_E_HIP if the scratch address cannot be obtained.
+ */
+int kvs_paged_decode_noalloc(const void* q, void* k_pool, void* v_pool, int num_blocks,
+                             const int32_t* block_tables, int max_blocks, const int32_t* ctx_lens,
+                             int batch, int max_ctx, int hq, int hkv, int d, float scale,
+                             const void* new_k_opt, const void* new_v_opt, void* o, float* lse_opt,
+                             void* stream);
+
+/*
  * kvs_copy_blocks_fp8 - kvs_copy_blocks for an 8-bit cache: code blocks and scale rows.
  */
 int kvs_copy_blocks_fp8(void* k_pool, void* v_pool, float* k_scale, float* v_scale, int num_blocks, int hkv, int d,

@@ -30,6 +30,8 @@ SIGNATURES = {
     "kvs_paged_decode": (_c_int, [_vp, _vp, _vp, _c_int, _vp, _c_int, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                   _c_float, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
     "kvs_copy_blocks": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _vp, _c_int, _vp]),
+    "kvs_paged_decode_noalloc": (_c_int, [_vp, _vp, _vp, _c_int, _vp, _c_int, _vp, _c_int, _c_int, _c_int, _c_int,
+                                          _c_int, _c_float, _vp, _vp, _vp, _vp, _vp]),
     "kvs_slot_init": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
     "kvs_decode_select_slot": (_c_int, [_vp, _vp, _c_int, _vp, _c_int, _c_int, _c_int, _vp, _c_int, _vp, _vp]),
     "kvs_paged_decode_scored_workspace_size": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),

@@ -26,6 +26,8 @@
 // would save that launch, but making the partials of other XCDs visible needs an agent-scope
 // release, i.e. an L2 write-back per workgroup, which costs more on this chip than the
 // launch: measured about 3x slower.)
+#include <mutex>
+
 #include "kvs_common.h"
 
 namespace kvs {
@@ -715,6 +717,65 @@ extern "C" int kvs_paged_decode_fp8(const void* q, void* k_pool, void* v_pool, f
   return run_decode("kvs_paged_decode_fp8", q, k_pool, v_pool, k_scale, v_scale, true, num_blocks, block_tables,
                     max_blocks, ctx_lens, batch, max_ctx, hq, hkv, d, scale, new_k, new_v, o, lse_opt, workspace,
                     workspace_bytes, stream);
+}
+
+// ---- Decode for callers that cannot allocate device memory (code under graph capture, tight
+// serving loops, harnesses that forbid allocation): the split partials go to a scratch array
+// the library holds on every device it runs on, for the life of the process.
+namespace {
+constexpr size_t kScratchBytes = size_t(16) << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` on each device, looked up once
+}  // namespace
+
+// Device address of the current device's scratch array.  In host code `scratch` only names a
+// host-side stand-in: its device address comes from the runtime, once per device, with that
+// device current.
+static int scratch_on_current_device(const char* name, void* stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(KVS_E_HIP, "%s: hipGetDevice: %s", name, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(KVS_E_INVAL, "%s: device %d is beyond the %d tracked", name, dev,
+                                                   kMaxDevices);
+  if (stream) {
+    int sdev = -1;
+    e = hipStreamGetDevice(as_stream(stream), &sdev);
+    if (e != hipSuccess) return fail(KVS_E_HIP, "%s: hipStreamGetDevice: %s", name, hipGetErrorString(e));
+    if (sdev != dev) return fail(KVS_E_INVAL, "%s: the stream belongs to device %d, the current device is %d", name,
+                                 sdev, dev);
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(KVS_E_HIP, "%s: hipGetSymbolAddress(scratch): %s", name, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return KVS_OK;
+}
+
+extern "C" int kvs_paged_decode_noalloc(const void* q, void* k_pool, void* v_pool, int num_blocks,
+                                        const int32_t* block_tables, int max_blocks, const int32_t* ctx_lens,
+                                        int batch, int max_ctx, int hq, int hkv, int d, float scale,
+                                        const void* new_k, const void* new_v, void* o, float* lse_opt,
+                                        void* stream) {
+  const char* name = "kvs_paged_decode_noalloc";
+  const size_t need = kvs_paged_decode_workspace_size(batch, hq, hkv, d, max_ctx);
+  if (need > kScratchBytes)
+    return fail(KVS_E_INVAL, "%s: this call needs %zu bytes of split partials, more than the %zu-byte scratch the "
+                "library holds per device (use kvs_paged_decode with a workspace)", name, need, kScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    const int rc = scratch_on_current_device(name, stream, &ws);
+    if (rc != KVS_OK) return rc;
+  }
+  return run_decode(name, q, k_pool, v_pool, nullptr, nullptr, false, num_blocks, block_tables, max_blocks, ctx_lens,
+                    batch, max_ctx, hq, hkv, d, scale, new_k, new_v, o, lse_opt, ws, need > 0 ? kScratchBytes : 0,
+                    stream);
 }
 
 // ---- Scored decode: partials (always, even for one split) then the logits.

@@ -139,6 +139,27 @@ def kvs_paged_decode(q, k_pool, v_pool, block_tables, ctx_lens, max_ctx: int, sc
     return o
 
 
+def kvs_paged_decode_noalloc(q, k_pool, v_pool, block_tables, ctx_lens, max_ctx: int, scale: Optional[float] = None,
+                             new_k=None, new_v=None, o=None, lse=None, stream=None):
+    """kvs_paged_decode with its split partials in the library's per-device scratch (no workspace)."""
+    _dev(q, torch.bfloat16, "q"); _dev(k_pool, torch.bfloat16, "k_pool"); _dev(v_pool, torch.bfloat16, "v_pool")
+    _dev(block_tables, torch.int32, "block_tables"); _dev(ctx_lens, torch.int32, "ctx_lens")
+    B, hq, d = q.shape
+    hkv = k_pool.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if new_k is not None:
+        _dev(new_k, torch.bfloat16, "new_k"); _dev(new_v, torch.bfloat16, "new_v")
+    o = torch.empty_like(q) if o is None else _dev(o, torch.bfloat16, "o")
+    if lse is not None:
+        _dev(lse, torch.float32, "lse")
+    check(lib.kvs_paged_decode_noalloc(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), k_pool.shape[0],
+                                       block_tables.data_ptr(), block_tables.shape[1], ctx_lens.data_ptr(), B,
+                                       int(max_ctx), hq, hkv, d, float(scale), _ptr(new_k), _ptr(new_v), o.data_ptr(),
+                                       _ptr(lse), _stream(stream)))
+    return o
+
+
 def kvs_slot_init(scores, cu_seqlens, keep_idx, keep_offsets, slot_stride: int, slot_scores=None, slot_pos=None,
                   stream=None):
     """Slot state after compaction: scores/positions [S][Hkv][slot_stride] (keep_idx None: keep all)."""

@@ -75,6 +75,18 @@ def measured_traffic(kernel_key: str, source: str):
     return rec.get("bytes_per_launch")
 
 
+def measured_scale_traffic(key: str):
+    """HBM bytes of an at-scale figure (32-layer decode step, multi-prompt prefill or compaction)
+    from the committed counter summary, or None if the kernel's source changed since."""
+    path = os.path.join(ROOT, "profiles", "traffic_scale.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(key)
+    if not rec or rec.get("source_sha256_16") != kernel_source_hash(rec["source"]):
+        return None
+    return rec
+
+
 def measured_mfma(kernel_key: str, source: str):
     """MFMA counters of a launch (rocprofv3: executed bf16 flops, MFMA-busy share of the SIMDs' active
     cycles) from the committed summary, or None if the kernel changed since."""
@@ -604,7 +616,18 @@ def prompt_side(kvs, torch, wl, cid):
     names = {3: "20 prompts U[1000,4000]", 4: "4 prompts x 30000", 5: "64 prompts log-uniform [512,32768] "
              "(first admission wave)"}
     budgets = "layers 0-2 full, " + ("3-31 k=%d" % w.budgets[3] if cid != 5 else "pyramid k 2048..128 on 3-31")
+    if cid == 3:
+        # counter figures of this workload's kernels (profiles/traffic_scale.json), while current
+        per_budget["full"]["traffic"] = _traffic_rate(
+            measured_scale_traffic("keep-all compaction, 20 prompts (47731 tokens)"), None,
+            per_budget["full"]["compact_us"])
+        per_budget["k=512"]["traffic"] = _traffic_rate(measured_scale_traffic("compaction k=512, 20 prompts"), None,
+                                                        per_budget["k=512"]["compact_us"])
+        prefill_traffic = _traffic_rate(measured_scale_traffic("prefill, 20 prompts (47731 tokens)"), None, t_pre)
+    else:
+        prefill_traffic = None
     return {"workload": f"{names[cid]}, {w.n_layers} layers ({budgets}), alpha={alpha}, {hq}q/{hkv}kv heads, d={d}",
+            "prefill_traffic": prefill_traffic,
             "prompt_tokens": T,
             "prefill_us": round(t_pre, 2), "prefill_TFLOPs": round(flops / (t_pre * 1e-6) / 1e12, 1),
             "prefill_frac_of_mfma_peak": round(flops / (t_pre * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
@@ -614,6 +637,16 @@ def prompt_side(kvs, torch, wl, cid):
             "us_32_layers": round(total_us, 1),
             "prompt_tok_s_32_layers": round(T / (total_us * 1e-6), 1),
             "prompt_tok_s_per_layer": round(T / (total_us * 1e-6) * w.n_layers, 1)}
+
+
+def _traffic_rate(rec, key, us):
+    """Counter-measured HBM bytes of a launch (or step) and the rate they give at `us`."""
+    if rec is None:
+        return None
+    nbytes = rec[key] if key else rec["read_bytes"] + rec["write_bytes"]
+    return {"bytes": int(nbytes), "GBs": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "source": "profiles/traffic_scale.json (rocprofv3 FETCH_SIZE and WRITE_SIZE, copy-calibrated)"}
 
 
 def paged_memory(wl, iterations=1000):
@@ -776,6 +809,8 @@ def decode_32_layers(kvs, torch, wl, steps, fp8=False):
             "launches_per_step": sum(2 if kvs.kvs_paged_decode_workspace_size(B, hq, hkv, d, l[3]) else 1
                                      for l in layers),
             "cached_tokens_per_head": cached,
+            "traffic": _traffic_rate(measured_scale_traffic("decode_32_layers" + ("_fp8" if fp8 else "")),
+                                     "bytes_per_step", graph_us),
             # K/V bytes read per step (about 1.8 GB: more than the 256 MB Infinity Cache holds,
             # so this is an HBM rate); 8-bit rows carry one fp32 scale each for K and V
             "kv_bytes_per_step": kv_bytes,

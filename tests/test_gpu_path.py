@@ -399,3 +399,55 @@ def test_prefill_without_statistics_writes_only_o():
     torch.cuda.synchronize()
     assert none is None
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_empty_prompts_in_a_ragged_batch():
+    """Prompts of length 0 between real ones (repeated cu_seqlens entries): they produce no
+    rows, scores, kept indices or blocks, and the prompts around them match the oracle."""
+    lengths = [0, 7, 0, 300, 0, 40, 0]
+    hq, hkv, d, alpha, kb = 8, 2, 128, 16, 32
+    _say(f"empty prompts in a ragged batch: lengths={lengths}")
+    r = np.random.default_rng(23)
+    T = sum(lengths)
+    qb = wl.f32_to_bf16_bits(r.standard_normal((T, hq, d), dtype=np.float32))
+    kk = wl.f32_to_bf16_bits(r.standard_normal((T, hkv, d), dtype=np.float32))
+    vb = wl.f32_to_bf16_bits(r.standard_normal((T, hkv, d), dtype=np.float32))
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    q, k, v = to_dev_bf16(qb), to_dev_bf16(kk), to_dev_bf16(vb)
+    o, lse = kvs.kvs_prefill_attn_lse(q, k, v, i32(cu), max(lengths))
+    S = kvs.kvs_window_score(q, k, lse, i32(cu), max(lengths), alpha)
+    kept = [min(kb, n) for n in lengths]
+    koff = np.concatenate([[0], np.cumsum(kept)]).astype(np.int32)
+    keep = kvs.kvs_topk_select(S, i32(cu), max(lengths), alpha, kb, i32(koff), total_keep=int(koff[-1]))
+    nbs = [-(-c // 16) for c in kept]
+    k_pool, v_pool = kvs.new_pools(sum(nbs) + 1, hkv, d)
+    k_pool.view(torch.int16).fill_(0x7FC0)
+    v_pool.view(torch.int16).fill_(0x7FC0)
+    tbl = np.full((len(lengths), max(nbs)), -1, np.int32)
+    at = 0
+    for s, nb in enumerate(nbs):
+        tbl[s, :nb] = np.arange(at, at + nb)
+        at += nb
+    kvs.kvs_compact_paged(k, v, i32(cu), keep, i32(koff), max(kept), k_pool, v_pool, i32(tbl))
+    torch.cuda.synchronize()
+    og, lg, Sg, keepg = bf16_to_f64(o), lse.cpu().numpy(), S.cpu().numpy().astype(np.float64), keep.cpu().numpy()
+    assert keepg.size == hkv * koff[-1]
+    kbits, vbits = bf16_bits(k), bf16_bits(v)
+    for s, n in enumerate(lengths):
+        if n == 0:
+            continue
+        a, b = cu[s], cu[s + 1]
+        O_ref, lse_ref, _, _ = oracle.causal_attention(_f64(qb[a:b]), _f64(kk[a:b]), _f64(vb[a:b]))
+        assert_rows_close(og[a:b], O_ref, what=f"O seq {s}")
+        assert_lse_close(lg[:, a:b], lse_ref, what=f"LSE seq {s}")
+        S_ref = oracle.window_score(_f64(qb[a:b]), _f64(kk[a:b]), lse_ref, alpha)
+        assert_scores_close(Sg[:, a:b], S_ref, what=f"S seq {s}")
+        seg = keepg[hkv * koff[s]: hkv * koff[s + 1]].reshape(hkv, kept[s])
+        for g in range(hkv):
+            np.testing.assert_array_equal(seg[g], oracle.select_keep(Sg[g, a:b], n, alpha, kb))
+        gk, gv = gather_pools(k_pool, v_pool, tbl[s, :nbs[s]], kept[s])
+        for g in range(hkv):
+            np.testing.assert_array_equal(gk[:, g], kbits[a + seg[g], g])
+            np.testing.assert_array_equal(gv[:, g], vbits[a + seg[g], g])
+    # the spare block was never written
+    assert torch.all(k_pool[-1].view(torch.int16) == 0x7FC0)

@@ -354,10 +354,10 @@ def main():
         kvs.kvs_compact_paged(k, v, cu_d, keep, keep_off, k_eff, k_pool, v_pool, tbl)
         progress("evict")
         line["decode_evict"] = decode_evict(kvs, torch, wl, w, k_pool, v_pool, tbl, S, cu_d, keep, keep_off, 200)
-    for cid in (3, 4, 5):
+    for cid, key in ((3, "prompt_side_20_prompts"), (4, "prompt_side_4x30000"), (5, "prompt_side_64_prompt_mix")):
         if f"prompt{cid}" in sections:
-            progress("prompt side")
-            line[f"prompt_side_w{cid}"] = prompt_side(kvs, torch, wl, cid)
+            progress(key)
+            line[key] = prompt_side(kvs, torch, wl, cid)
     if "memory" in sections:
         progress("memory")
         line["paged_memory"] = paged_memory(wl)
@@ -551,8 +551,8 @@ def prompt_side(kvs, torch, wl, cid):
     budget, so they are timed once; top-k and compaction are timed for every distinct budget
     (keep-all compaction for the full layers).  The 32-layer figure sums the layers' kernels:
     prompt tokens / (32 prefills + a score, top-k and compaction per compressed layer + a
-    keep-all compaction per full layer).  Workload 5 is its first admission wave (64 prompts,
-    each prefilled whole: prefix reuse would only lower the work)."""
+    keep-all compaction per full layer).  The continuous-batch mix is measured on its first
+    admission wave (64 prompts, each prefilled whole: prefix reuse would only lower the work)."""
     import numpy as np
     dev = torch.device("cuda:0")
     w = wl.WORKLOADS[cid]
@@ -651,8 +651,9 @@ def _traffic_rate(rec, key, us):
 
 def paged_memory(wl, iterations=1000):
     """Slots taken from the pool that hold no token ([PAG] "How paging works": with blocks only
-    the tail of each table's last block is empty).  Workload 3: the 20 prompts' tables over
-    the 500 decode steps, every layer.  Workload 5: the product's cache manager driven over the
+    the tail of each table's last block is empty).  The 32-layer, 20-prompt workload: its
+    tables over the 500 decode steps, every layer.  The continuous-batch mix: the product's
+    cache manager driven over the
     continuous-batch trace (shared prefixes counted once), sampled every 10 iterations; beside
     it, what reserving each slot's longest possible sequence contiguously would leave empty."""
     import numpy as np
@@ -689,11 +690,11 @@ def paged_memory(wl, iterations=1000):
             live.remove(sid)
     samples = len(range(5, iterations, 10))
     reserve = samples * w5.num_seqs * w5.n_layers * (w5.len_range[1] + w5.lifetime_range[1])
-    return {"w3_tail_slot_frac": round(1 - used / taken, 5),
-            "w3_note": "20 prompts x 32 layers, every decode step 0..500",
-            "w5_tail_slot_frac": round(1 - u5 / t5, 5),
-            "w5_contiguous_reservation_waste_frac": round(1 - reserved_used / reserve, 4),
-            "w5_note": f"continuous-batch trace, {iterations} iterations sampled every 10, 32 layers; the "
+    return {"tail_slot_frac_20_prompts": round(1 - used / taken, 5),
+            "note_20_prompts": "20 prompts x 32 layers, every decode step 0..500",
+            "tail_slot_frac_continuous_mix": round(1 - u5 / t5, 5),
+            "contiguous_reservation_waste_frac_continuous_mix": round(1 - reserved_used / reserve, 4),
+            "note_continuous_mix": f"continuous-batch trace, {iterations} iterations sampled every 10, 32 layers; the "
                        "reservation figure assumes each slot holds room for 32768 + 500 tokens in every layer"}
 
 

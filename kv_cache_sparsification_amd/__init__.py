@@ -15,7 +15,8 @@ from .ops import (kvs_prefill_attn_lse, kvs_window_score, kvs_topk_select, kvs_c
                   kvs_gather_paged, kvs_paged_decode_scored_fp8, kvs_probe_stream_read,
                   kvs_paged_decode_noalloc)
 from .allocator import BlockAllocator
-from .pipeline import layer_policy, keep_counts, prefill_compress_layer, prefill_compress_layer_chunked
+from .pipeline import (layer_policy, keep_counts, prefill_compress_layer, prefill_compress_layer_chunked,
+                       prefix_rows_reused, prefill_compress_admission)
 from .prefix_cache import BlockHashIndex, chained_block_keys
 
 __all__ = [
@@ -27,5 +28,6 @@ __all__ = [
     "kvs_prefill_attn_lse_chunk", "kvs_window_score_chunk", "kvs_gather_paged", "kvs_paged_decode_scored_fp8",
     "kvs_probe_stream_read", "kvs_paged_decode_noalloc",
     "BlockAllocator", "layer_policy", "keep_counts", "prefill_compress_layer",
-    "prefill_compress_layer_chunked", "BlockHashIndex", "chained_block_keys",
+    "prefill_compress_layer_chunked", "prefix_rows_reused", "prefill_compress_admission", "BlockHashIndex",
+    "chained_block_keys",
 ]

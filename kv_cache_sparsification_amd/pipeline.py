@@ -142,3 +142,109 @@ def prefill_compress_layer_chunked(q, k, v, cu_q, cu_k, q_lengths: Sequence[int]
         ops.kvs_compact_paged(k, v, cu_k, keep_idx, keep_off_dev, max(kept), k_pool, v_pool, tbl_dev, stream=stream)
     return dict(o=o, lse=lse, scores=scores, keep_idx=keep_idx, keep_offsets=keep_off_dev, kept=kept,
                 tables_dev=tbl_dev)
+
+
+def prefix_rows_reused(cache, layer: int, plan, n: int, alpha: int) -> int:
+    """Prompt rows a new member reads back from its group's prefix blocks in `layer` instead of
+    computing them.
+
+    [PAG] "Sharing blocks between sequences": sequences of one prefix map the same blocks.  A
+    member reuses the whole prefix when the layer carries the group's prefix, the prefix was
+    written before this member's admission (a member whose admission created it computes it),
+    and the member's own rows still hold its last min(alpha, n) tokens, whose LSE the window
+    score reads.  Otherwise 0: the member computes all its rows.
+    """
+    P = cache.prefix_len
+    if P and n > P and cache.carries_prefix(layer) and not plan.new_prefix and n - P >= min(alpha, n):
+        return P
+    return 0
+
+
+def prefill_compress_admission(cache, layer: int, seqs: Sequence, plans, q, k, v, alpha: int, k_pool, v_pool,
+                               scale: Optional[float] = None, stream=None):
+    """One layer of an admission wave under continuous batching with shared prefixes.
+
+    seqs: the admitted prompts in batch order as (seq_id, group, n); plans: {seq_id: the list
+    cache.admit() returned}.  q holds the rows each prompt computes (rows r0..n-1 with
+    r0 = prefix_rows_reused(...)), k and v all n rows of every prompt; the rows of a reused
+    prefix are overwritten here by the read-back from the group's blocks.  In order, on the
+    caller's stream and with no device readback:
+      1. a prefix created by this admission is written once into its group's blocks, from the
+         rows of the member whose admission created it;
+      2. members of a prefix written earlier read its rows back from the shared blocks;
+      3. causal attention with LSE for the computed rows ([KVS] Key techniques 2);
+      4. full layer: each prompt's rows from its first unshared slot are compacted (the prefix
+         stays shared); compressed layer: window score, top-k over all n tokens and compaction
+         into the prompt's own blocks, which are copy-on-write replacements of shared entries
+         ([KVS] Key techniques 1, 2; [PAG] How paging works).
+    Returns o, lse (computed rows), scores, keep_idx, keep_offsets, kept, first (rows reused per
+    prompt), cu_q, cu_k (host lists) and tables_dev.
+    """
+    dev = k.device
+    P = cache.prefix_len
+    lengths = [int(sq[2]) for sq in seqs]
+    lp = [plans[sq[0]][layer] for sq in seqs]
+    first = [prefix_rows_reused(cache, layer, p, n, alpha) for p, n in zip(lp, lengths)]
+    cu_k = [0]
+    for n in lengths:
+        cu_k.append(cu_k[-1] + n)
+    cu_q = [0]
+    for n, f in zip(lengths, first):
+        cu_q.append(cu_q[-1] + n - f)
+    if k.shape[0] != cu_k[-1] or v.shape[0] != cu_k[-1] or q.shape[0] != cu_q[-1]:
+        raise ValueError("q must hold each prompt's computed rows and k, v all its rows")
+
+    def i32(x):
+        return torch.tensor(x, dtype=torch.int32).to(dev)
+
+    for s, sq in enumerate(seqs):
+        if lp[s].new_prefix:
+            a = cu_k[s]
+            ops.kvs_compact_paged(k[a:a + P].contiguous(), v[a:a + P].contiguous(), i32([0, P]), None, None, P,
+                                  k_pool, v_pool, i32([cache.prefix_blocks[layer][sq[1]]]), stream=stream)
+    reusers = [s for s in range(len(seqs)) if first[s]]
+    if reusers:
+        ops.kvs_gather_paged(k_pool, v_pool, i32([cache.prefix_blocks[layer][seqs[s][1]] for s in reusers]),
+                             i32([P] * len(reusers)), i32([cu_k[s] for s in reusers]), P, k, v, stream=stream)
+    cu_k_dev = i32(cu_k)
+    max_n = max(lengths)
+    if reusers:
+        o, lse = ops.kvs_prefill_attn_lse_chunk(q, k, v, i32(cu_q), cu_k_dev, max(cu_q[s + 1] - cu_q[s]
+                                                                                    for s in range(len(seqs))),
+                                                max_n, scale=scale, stream=stream)
+    else:
+        o, lse = ops.kvs_prefill_attn_lse(q, k, v, cu_k_dev, max_n, scale=scale, stream=stream)
+    max_blocks = max(len(p.table) for p in lp)
+    tbl = torch.full((len(seqs), max_blocks), -1, dtype=torch.int32)
+    for s, p in enumerate(lp):
+        tbl[s, :len(p.table)] = torch.tensor(p.table, dtype=torch.int32)
+    tbl_dev = tbl.to(dev)
+    budget = cache.budgets[layer]
+    scores = keep_idx = keep_off_dev = None
+    kept = [p.kept for p in lp]
+    if budget is None:
+        offs = [p.dst_offset for p in lp]
+        segs = [(cu_k[s] + offs[s], cu_k[s + 1]) for s in range(len(seqs))]
+        ks = torch.cat([k[a:b] for a, b in segs])
+        vs = torch.cat([v[a:b] for a, b in segs])
+        cus = [0]
+        for a, b in segs:
+            cus.append(cus[-1] + b - a)
+        ops.kvs_compact_paged(ks, vs, i32(cus), None, None, max(b - a for a, b in segs), k_pool, v_pool, tbl_dev,
+                              dst_slot_offset=i32(offs), stream=stream)
+    else:
+        if reusers:
+            scores = ops.kvs_window_score_chunk(q, k, lse, i32(cu_q), cu_k_dev, max_n, alpha, scale=scale,
+                                                stream=stream)
+        else:
+            scores = ops.kvs_window_score(q, k, lse, cu_k_dev, max_n, alpha, scale=scale, stream=stream)
+        keep_off = [0]
+        for c in kept:
+            keep_off.append(keep_off[-1] + c)
+        keep_off_dev = i32(keep_off)
+        keep_idx = ops.kvs_topk_select(scores, cu_k_dev, max_n, alpha, budget, keep_off_dev, total_keep=keep_off[-1],
+                                       stream=stream)
+        ops.kvs_compact_paged(k, v, cu_k_dev, keep_idx, keep_off_dev, max(kept), k_pool, v_pool, tbl_dev,
+                              stream=stream)
+    return dict(o=o, lse=lse, scores=scores, keep_idx=keep_idx, keep_offsets=keep_off_dev, kept=kept, first=first,
+                cu_q=cu_q, cu_k=cu_k, tables_dev=tbl_dev)

@@ -5,7 +5,8 @@ iterations (every slot turns over at least twice).
 
 Kernels run on layers 0 (full cache), 3 (k = 2048) and 31 (k = 128); every layer's block
 bookkeeping runs through the product's cache manager on the native allocator, with the shared
-prefix carried by every layer.  A group's prefix blocks are written once, from the rows of the
+prefix carried by every layer, and every admission wave through the product's admission step
+(kvs.prefill_compress_admission).  A group's prefix blocks are written once, from the rows of the
 member whose admission creates them; every later member reads its first 2048 keys and values
 back from those blocks (kvs_gather_paged, checked bit-exact against the generated rows) and
 computes only its own rows (chunked prefill and window score), and each compressed layer's
@@ -164,79 +165,45 @@ def test_continuous_mix_with_shared_prefixes():
 
 
 def admit_layer(w, l, admitted, plans, cache, pool, tracked, oracle_cache, stats):
-    """Prefill, score, select and compact one admission wave in layer l."""
+    """One admission wave in layer l through the product's admission step (prefix written once,
+    read back by later members, chunked prefill of their own rows, score, top-k, compaction)."""
     P = w.prefix_len
     k_pool, v_pool = pool
     parts = [_prompt(w, l, sq) for sq in admitted]
     k = torch.cat([p[1] for p in parts]); v = torch.cat([p[2] for p in parts])
     lengths = [sq.n for sq in admitted]
     cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
-    kb = w.budgets[l]
-    # prefixes created by this admission: written once, from the creating member's rows
-    for s, sq in enumerate(admitted):
-        if plans[sq.seq_id][l].new_prefix:
-            kvs.kvs_compact_paged(k[cu[s]:cu[s] + P].contiguous(), v[cu[s]:cu[s] + P].contiguous(), i32([0, P]),
-                                  None, None, P, k_pool, v_pool, i32([cache.prefix_blocks[l][sq.group]]))
-    # members of a live prefix read its rows back from the shared blocks and compute only their
-    # own rows (when those hold the whole window)
-    first = [P if (sq.n > P and cache.carries_prefix(l) and not plans[sq.seq_id][l].new_prefix
-                   and sq.n - P >= w.alpha) else 0 for sq in admitted]
+    first = [kvs.prefix_rows_reused(cache, l, plans[sq.seq_id][l], sq.n, w.alpha) for sq in admitted]
     reusers = [s for s in range(len(admitted)) if first[s]]
+    # the reused prefix rows must come back from the shared blocks: keep the generated ones to
+    # compare with, and poison them in the buffer the step reads
+    generated = [(k[cu[s]:cu[s] + P].clone(), v[cu[s]:cu[s] + P].clone()) for s in reusers]
     if reusers:
-        generated_k = [k[cu[s]:cu[s] + P].clone() for s in reusers]
-        generated_v = [v[cu[s]:cu[s] + P].clone() for s in reusers]
         rows = torch.as_tensor([r for s in reusers for r in range(cu[s], cu[s] + P)], device="cuda")
-        k[rows] = float("nan")          # only the read-back can restore them
+        k[rows] = float("nan")
         v[rows] = float("nan")
-        kvs.kvs_gather_paged(k_pool, v_pool, i32([cache.prefix_blocks[l][admitted[s].group] for s in reusers]),
-                             i32([P] * len(reusers)), i32([cu[s] for s in reusers]), P, k, v)
-        for s, gk, gv in zip(reusers, generated_k, generated_v):
-            assert torch.equal(k[cu[s]:cu[s] + P].view(torch.int16), gk.view(torch.int16)), \
-                f"prefix K read back for seq {admitted[s].seq_id} layer {l}"
-            assert torch.equal(v[cu[s]:cu[s] + P].view(torch.int16), gv.view(torch.int16)), \
-                f"prefix V read back for seq {admitted[s].seq_id} layer {l}"
-        stats["reused"] += len(reusers)
-        stats["gathered_rows"] += P * len(reusers)
     q = torch.cat([p[0][first[s]:] for s, p in enumerate(parts)])
-    qlen = [n - f for n, f in zip(lengths, first)]
-    cu_q = np.concatenate([[0], np.cumsum(qlen)]).astype(np.int32)
-    cu_d = i32(cu)
-    if reusers:
-        o, lse = kvs.kvs_prefill_attn_lse_chunk(q, k, v, i32(cu_q), cu_d, max(qlen), max(lengths))
-    else:
-        o, lse = kvs.kvs_prefill_attn_lse(q, k, v, cu_d, max(lengths))
-    max_blocks = max(len(plans[sq.seq_id][l].table) for sq in admitted)
-    tbl = np.full((len(admitted), max_blocks), -1, np.int32)
-    for s, sq in enumerate(admitted):
-        t = plans[sq.seq_id][l].table
-        tbl[s, :len(t)] = t
-    if kb is None:
-        # full layer: each prompt's rows from its first unshared slot on
-        offs = [plans[sq.seq_id][l].dst_offset for sq in admitted]
-        segs = [(cu[s] + offs[s], cu[s + 1]) for s in range(len(admitted))]
-        ks = torch.cat([k[a:b] for a, b in segs]); vs = torch.cat([v[a:b] for a, b in segs])
-        cus = np.concatenate([[0], np.cumsum([b - a for a, b in segs])]).astype(np.int32)
-        kvs.kvs_compact_paged(ks, vs, i32(cus), None, None, int(max(cus[1:] - cus[:-1])), k_pool,
-                              v_pool, i32(tbl), dst_slot_offset=i32(offs))
-        S = keep = None
-    else:
-        if reusers:
-            S = kvs.kvs_window_score_chunk(q, k, lse, i32(cu_q), cu_d, max(lengths), w.alpha)
-        else:
-            S = kvs.kvs_window_score(q, k, lse, cu_d, max(lengths), w.alpha)
-        kept = [plans[sq.seq_id][l].kept for sq in admitted]
-        koff = np.concatenate([[0], np.cumsum(kept)]).astype(np.int32)
-        keep = kvs.kvs_topk_select(S, cu_d, max(lengths), w.alpha, kb, i32(koff), total_keep=int(koff[-1]))
-        kvs.kvs_compact_paged(k, v, cu_d, keep, i32(koff), max(kept), k_pool, v_pool, i32(tbl))
+    res = kvs.prefill_compress_admission(cache, l, [(sq.seq_id, sq.group, sq.n) for sq in admitted], plans, q, k, v,
+                                         w.alpha, k_pool, v_pool)
+    assert res["first"] == first
+    torch.cuda.synchronize()
+    for s, (gk, gv) in zip(reusers, generated):
+        assert torch.equal(k[cu[s]:cu[s] + P].view(torch.int16), gk.view(torch.int16)), \
+            f"prefix K read back for seq {admitted[s].seq_id} layer {l}"
+        assert torch.equal(v[cu[s]:cu[s] + P].view(torch.int16), gv.view(torch.int16)), \
+            f"prefix V read back for seq {admitted[s].seq_id} layer {l}"
+    stats["reused"] += len(reusers)
+    stats["gathered_rows"] += P * len(reusers)
+    if w.budgets[l] is not None:
         # each sharing member swaps the prefix entries its compaction writes
         stats["swaps"] += sum(min(-(-plans[sq.seq_id][l].kept // 16), P // 16) for sq in admitted if sq.n > P)
-    torch.cuda.synchronize()
+    cu_q = np.asarray(res["cu_q"], dtype=np.int32)
     for s, sq in enumerate(admitted):
         if sq.seq_id in tracked:
             _say(f"check admission of seq {sq.seq_id} (n={sq.n}, group {sq.group}, rows from {first[s]}) "
                  f"layer {l}")
-            check_admission(w, l, sq, q, k, v, o, lse, S, keep, cu, cu_q, first[s], s, admitted, plans, pool,
-                            oracle_cache)
+            check_admission(w, l, sq, q, k, v, res["o"], res["lse"], res["scores"], res["keep_idx"], cu, cu_q,
+                            first[s], s, admitted, plans, pool, oracle_cache)
 
 
 def check_admission(w, l, sq, q, k, v, o, lse, S, keep, cu, cu_q, first, s, admitted, plans, pool, oracle_cache):

@@ -124,3 +124,21 @@ def test_slot_usage(carried):
         tails = sum(-prod.length[(sid, l)] % 16 for sid in live)
         assert slots - used == tails
         assert slots == 16 * (prod.alloc[l].num_blocks - prod.num_free(l))
+
+
+def test_prefix_rows_reused_rule():
+    """Who reads the shared prefix back instead of computing it: later members of a live prefix in
+    the layers that carry it, when their own rows still hold the whole window."""
+    budgets, P, alpha = [None, 32], 48, 16
+    for carried in (True, False):
+        cache = PagedKVCache(budgets, [64, 64], prefix_len=P, prefix_in_compressed=carried)
+        creator = cache.admit(0, 0, 100)
+        member = cache.admit(1, 0, 100)
+        short = cache.admit(2, 0, P + alpha - 1)           # its own rows would miss part of the window
+        private = cache.admit(3, 1, 40)                    # no longer than the prefix: shares nothing
+        for l in (0, 1):
+            assert kvs.prefix_rows_reused(cache, l, creator[l], 100, alpha) == 0
+            assert kvs.prefix_rows_reused(cache, l, short[l], P + alpha - 1, alpha) == 0
+            assert kvs.prefix_rows_reused(cache, l, private[l], 40, alpha) == 0
+        assert kvs.prefix_rows_reused(cache, 0, member[0], 100, alpha) == P
+        assert kvs.prefix_rows_reused(cache, 1, member[1], 100, alpha) == (P if carried else 0)

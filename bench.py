@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+REALTIME_HZ = 100e6          # the GPU's real-time counter (kvs_probe_timestamp) on MI355X
 ALL_SECTIONS = ("ceiling", "lse", "scale", "fp8", "prefix", "layers32", "evict", "prompt3", "prompt4", "prompt5",
                 "memory")
 
@@ -177,6 +178,10 @@ def main():
         mark("compact_end")
 
     graph = pre_graph = None
+    # GPU clock stamps (100 MHz real-time counter) as the first and last launches of each
+    # captured phase: [prompt begin, prompt end, decode begin, decode end], copied per timed step
+    stamps = torch.zeros(4, dtype=torch.int64, device=dev)
+    stamp_hist = torch.zeros(max(args.steps, 1), 4, dtype=torch.int64, device=dev)
     if args.decode_mode == "graph":
         # Both phases captured as HIP graphs, the way a serving loop launches a fixed sequence:
         # the four prompt-side kernels as one graph, the 500 decode steps as another.
@@ -192,13 +197,17 @@ def main():
         stream.wait_stream(side)
         torch.cuda.synchronize()
         with torch.cuda.graph(pre_graph):
+            kvs.kvs_probe_timestamp(stamps[0:1])
             prefill_compress(lambda key: None)
+            kvs.kvs_probe_timestamp(stamps[1:2])
         with torch.cuda.graph(graph):
+            kvs.kvs_probe_timestamp(stamps[2:3])
             decode_all(lambda key: None)
+            kvs.kvs_probe_timestamp(stamps[3:4])
         torch.cuda.synchronize()
 
-    def one_step(rec):
-        """rec: dict of event lists, or None for warm-up."""
+    def one_step(rec, i=None):
+        """rec: dict of event lists, or None for warm-up; i: the timed step's index."""
         def mark(key):
             if rec is not None:
                 e = ev()
@@ -213,6 +222,8 @@ def main():
         if graph is not None:
             graph.replay()
             mark("decode_end")
+            if i is not None:
+                stamp_hist[i].copy_(stamps)
         else:
             decode_all(mark)
 
@@ -221,9 +232,9 @@ def main():
     torch.cuda.synchronize()
     recs = []
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for i in range(args.steps):
         rec = {}
-        one_step(rec)
+        one_step(rec, i)
         recs.append(rec)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -288,8 +299,16 @@ def main():
             rooflines[kname]["counters"] = measured_mfma(kname, src)
     dominant = max(per_step_ms, key=per_step_ms.get)
 
-    prefill_ms = float(np.mean(pre_phase))
-    decode_ms = float(np.mean(dec_phase))
+    prefill_ms_events = float(np.mean(pre_phase))
+    decode_ms_events = float(np.mean(dec_phase))
+    if graph is not None:
+        # GPU time of each captured phase from its clock stamps: the graph's start latency (the
+        # gap between the previous graph's last kernel and this one's first) is not in it
+        h = stamp_hist.cpu().numpy().astype(np.float64) * (1e3 / REALTIME_HZ)       # ms
+        prefill_ms = float(np.mean(h[:, 1] - h[:, 0]))
+        decode_ms = float(np.mean(h[:, 3] - h[:, 2]))
+    else:
+        prefill_ms, decode_ms = prefill_ms_events, decode_ms_events
     value = n / (prefill_ms * 1e-3)
     decode_tok_s = steps_dec / (decode_ms * 1e-3)
 
@@ -309,10 +328,17 @@ def main():
         "config": {"workload": "llama3-8b-layer n=4000 prompt, 32q/8kv heads, d=128, alpha=32, k=400, "
                                "16-token blocks, then 500 paged decode steps",
                    "global_batch": 1, "seq_len": n, "parallelism": "none (1 GPU)"},
-        "value_definition": "prompt tokens / GPU time of prefill attention + window score + top-k + compaction",
+        "value_definition": ("prompt tokens / GPU time of prefill attention + window score + top-k + compaction"
+                             + (", from a clock stamp launched first in the captured prompt-side graph to one "
+                                "launched last (the graph's start latency is outside it: graph_start_gap_us)"
+                                if graph is not None else ", between events around the eager launches")),
         "decode": {"metric": "paged-decode tok/s", "value": round(decode_tok_s, 1), "unit": "tok/s",
                    "ms_for_500_steps": round(decode_ms, 4)},
         "phase_ms": {"prefill_compress": round(prefill_ms, 4), "decode_500": round(decode_ms, 4)},
+        "phase_ms_events": {"prefill_compress": round(prefill_ms_events, 4), "decode_500": round(decode_ms_events, 4),
+                            "note": "events recorded on the stream around each graph replay: graph start "
+                                    "latency included"},
+        "graph_start_gap_us": round((prefill_ms_events - prefill_ms) * 1e3, 2) if graph is not None else None,
         "launch_mode": args.decode_mode,
         "roofline": {kk: rooflines[dominant][kk] for kk in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
         "roofline_kernel": dominant,

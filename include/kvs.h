@@ -371,6 +371,16 @@ int kvs_copy_blocks_fp8(void* k_pool, void* v_pool, float* k_scale, float* v_sca
 int kvs_probe_stream_read(const void* buf, size_t bytes, int grid, uint32_t key, uint32_t* sink, void* stream);
 
 /*
+ * kvs_probe_timestamp - measurement helper: one lane stores the GPU's real-time counter (a
+ *   fixed 100 MHz clock on MI355X, independent of the shader clock) when the kernel runs.
+ *   Two stamps placed as the first and last launches of a captured graph give the GPU time
+ *   of the work between them from the moment the graph starts running.
+ * In/out: out device pointer to one uint64, 8-byte aligned (written, counter ticks).
+ * Errors: KVS_E_INVAL on a NULL or misaligned pointer; KVS_E_HIP on launch failure.
+ */
+int kvs_probe_timestamp(uint64_t* out, void* stream);
+
+/*
  * Host block allocator.  [PAG] "How paging works": a request gets a new block only when
  * its last block is full, from any free block (the worked example pops from the front of
  * the free list).  [PAG] "Sharing blocks between sequences": a reference count per block;

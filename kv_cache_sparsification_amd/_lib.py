@@ -52,6 +52,7 @@ SIGNATURES = {
     "kvs_gather_paged": (_c_int, [_vp, _vp, _c_int, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _c_int, _vp, _vp,
                                   _vp]),
     "kvs_probe_stream_read": (_c_int, [_vp, _c_size, _c_int, ctypes.c_uint32, _vp, _vp]),
+    "kvs_probe_timestamp": (_c_int, [_vp, _vp]),
     "kvs_alloc_create": (_c_int, [_c_int, _i32p, _c_int, ctypes.POINTER(_vp)]),
     "kvs_alloc_destroy": (None, [_vp]),
     "kvs_alloc_block": (_c_int, [_vp, _i32p]),

@@ -1,4 +1,6 @@
-// Streaming-read probe: the rate at which one plain kernel reads device memory on this chip.
+// Measurement probes.
+//
+// Streaming read: the rate at which one plain kernel reads device memory on this chip.
 //
 // The memory-bound steps of the path (compaction, paged decode) are reported against the
 // published HBM peak; this kernel gives the practical ceiling beside it: 16 bytes per lane
@@ -31,6 +33,14 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4* __re
   if (folded == key) sink[blockIdx.x] = folded;
 }
 
+// Clock stamp: one lane stores the GPU's fixed-frequency real-time counter (100 MHz on this
+// chip).  Placed as the first and last nodes of a captured graph, two stamps time the work
+// between them from when the graph starts running, without the latency of starting it.
+__global__ __launch_bounds__(kWave) void timestamp_kernel(uint64_t* __restrict__ out) {
+  const uint64_t t = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) out[0] = t;
+}
+
 }  // namespace
 }  // namespace kvs
 
@@ -45,4 +55,11 @@ extern "C" int kvs_probe_stream_read(const void* buf, size_t bytes, int grid, ui
   stream_read_kernel<<<grid, kThreads, 0, as_stream(stream)>>>(static_cast<const u32x4*>(buf), bytes / 16, key,
                                                                sink);
   return launch_status("kvs_probe_stream_read");
+}
+
+extern "C" int kvs_probe_timestamp(uint64_t* out, void* stream) {
+  if (!out || (reinterpret_cast<uintptr_t>(out) & 7))
+    return fail(KVS_E_INVAL, "kvs_probe_timestamp: out must be a non-NULL, 8-byte aligned device pointer");
+  timestamp_kernel<<<1, kWave, 0, as_stream(stream)>>>(out);
+  return launch_status("kvs_probe_timestamp");
 }

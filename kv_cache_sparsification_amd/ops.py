@@ -408,3 +408,12 @@ def kvs_probe_stream_read(buf, grid: int, sink=None, key: int = 0x9E3779B9, stre
     check(lib.kvs_probe_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), int(grid), int(key),
                                     sink.data_ptr(), _stream(stream)))
     return sink
+
+
+def kvs_probe_timestamp(out, stream=None):
+    """Store the GPU's 100 MHz real-time counter into out (a device int64 tensor, element 0)
+    when the launch runs."""
+    if not out.is_cuda or out.dtype != torch.int64 or out.numel() < 1:
+        raise ValueError("out: device int64 tensor expected")
+    check(lib.kvs_probe_timestamp(out.data_ptr(), _stream(stream)))
+    return out

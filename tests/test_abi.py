@@ -63,6 +63,9 @@ def test_host_validation_rejects_before_launch():
     assert L.kvs_probe_stream_read(fake + 8, 1024, 64, 0, fake, None) == -1     # misaligned
     assert L.kvs_probe_stream_read(fake, 1024, 0, 0, fake, None) == -1          # empty grid
     assert L.kvs_probe_stream_read(None, 1024, 64, 0, fake, None) == -1
+    # the clock stamp: its output pointer is checked on the host
+    assert L.kvs_probe_timestamp(None, None) == -1
+    assert L.kvs_probe_timestamp(fake + 4, None) == -1                          # not 8-byte aligned
 
 
 def test_workspace_size_policy():

@@ -126,3 +126,35 @@ def test_decode_graph_replays_match_eager_and_oracle():
         for li, L in enumerate(layers):
             assert torch.equal(L["out"].view(torch.int16), eager[li].view(torch.int16)), f"replay {rep} layer {li}"
         del scratch
+
+
+def test_clock_stamps_time_the_work_between_them():
+    """Two clock stamps as the first and last launches of a captured graph (the bench's phase
+    timer): they run in order, the counter ticks at 100 MHz (the span agrees with events around
+    the replay, which add only the graph's start latency), and the span covers the work."""
+    _say("clock stamps around 16 streaming reads of 256 MiB in a graph")
+    buf = torch.zeros(256 << 20, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(2048, dtype=torch.int32, device="cuda")
+    stamps = torch.zeros(2, dtype=torch.int64, device="cuda")
+    kvs.kvs_probe_stream_read(buf, 2048, sink=sink)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        kvs.kvs_probe_timestamp(stamps[0:1])
+        for _ in range(16):
+            kvs.kvs_probe_stream_read(buf, 2048, sink=sink)
+        kvs.kvs_probe_timestamp(stamps[1:2])
+    st = torch.cuda.current_stream()
+    for rep in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        g.replay()
+        e1.record(st)
+        torch.cuda.synchronize()
+        t0, t1 = (int(x) for x in stamps.cpu())
+        span_ms = (t1 - t0) / 100e6 * 1e3
+        ev_ms = e0.elapsed_time(e1)
+        _say(f"replay {rep}: stamps {span_ms:.4f} ms, events {ev_ms:.4f} ms")
+        assert t1 > t0 > 0
+        assert 0.9 * ev_ms <= span_ms <= 1.01 * ev_ms + 0.005
+    assert int(sink.abs().sum()) == 0       # the zero buffer folds to 0, never the probe's key

@@ -962,29 +962,44 @@ def decode_evict(kvs, torch, wl, w, k_pool, v_pool, tbl, S, cu_d, keep, keep_off
     """Decode with scoring and eviction on the bench layer: the compressed cache is full
     (k_eff = k_l), so every step picks each head's lowest-score replaceable slot and runs the
     scored decode (attention, then the probabilities added to the slot scores); `steps` steps
-    replayed as one HIP graph."""
+    replayed as one HIP graph.  Two launch plans: the slot choice as its own launch before each
+    step (three launches per step), and the choice for the next step made by the step's
+    merge-and-score kernel (kvs_paged_decode_scored_select, two launches per step)."""
     dev = torch.device("cuda:0")
     n, hq, hkv, d, alpha, cap = w.fixed_len, w.hq, w.hkv, w.d, w.alpha, w.budgets[0]
     stride = tbl.shape[1] * 16
-    sl_sc, sl_pos = kvs.kvs_slot_init(S, cu_d, keep, keep_off, stride)
+    sl_sc0, sl_pos0 = kvs.kvs_slot_init(S, cu_d, keep, keep_off, stride)
     n_fill = torch.tensor([cap], dtype=torch.int32, device=dev)
-    pos = torch.tensor([[n + s] for s in range(steps)], dtype=torch.int32, device=dev)
+    pos = torch.tensor([[n + s] for s in range(steps + 1)], dtype=torch.int32, device=dev)
     qs, nks, nvs = zip(*[wl.device_decode_step(w, 0, 1000 + s, [0], device=dev) for s in range(steps)])
-    dst = torch.empty(1, hkv, dtype=torch.int32, device=dev)
     ws = torch.empty(kvs.kvs_paged_decode_scored_workspace_size(1, hq, hkv, d, cap), dtype=torch.uint8, device=dev)
     od = torch.empty(steps, 1, hq, d, dtype=torch.bfloat16, device=dev)
+    sl_sc, sl_pos = sl_sc0.clone(), sl_pos0.clone()
+    dst = torch.empty(1, hkv, dtype=torch.int32, device=dev)
+    dsts = torch.empty(steps + 1, 1, hkv, dtype=torch.int32, device=dev)
 
-    def run():
+    def run3():
         for s in range(steps):
             kvs.kvs_decode_select_slot(sl_sc, sl_pos, n_fill, pos[s], cap, alpha, dst_slot=dst)
             kvs.kvs_paged_decode_scored(qs[s], k_pool, v_pool, tbl, n_fill, cap, sl_sc, new_k=nks[s], new_v=nvs[s],
                                         dst_slots=dst, o=od[s], workspace=ws)
 
-    us = _graph_time_us(torch, run, steps)
+    def run2():
+        kvs.kvs_decode_select_slot(sl_sc, sl_pos, n_fill, pos[0], cap, alpha, dst_slot=dsts[0])
+        for s in range(steps):
+            kvs.kvs_paged_decode_scored_select(qs[s], k_pool, v_pool, tbl, n_fill, cap, sl_sc, sl_pos, cap, alpha,
+                                               pos[s + 1], next_dst_slots=dsts[s + 1], new_k=nks[s], new_v=nvs[s],
+                                               dst_slots=dsts[s], o=od[s], workspace=ws)
+
+    us3 = _graph_time_us(torch, run3, steps)
+    sl_sc.copy_(sl_sc0)
+    sl_pos.copy_(sl_pos0)
+    us2 = _graph_time_us(torch, run2, steps)
     return {"workload": f"bench layer, cache full at k={cap} (alpha={alpha}): every step evicts per KV head, "
                         f"{steps} steps (HIP graph)",
-            "us_per_step": round(us, 3), "tok_s": round(1.0 / (us * 1e-6), 1),
-            "launches_per_step": 3}
+            "us_per_step": round(us2, 3), "tok_s": round(1.0 / (us2 * 1e-6), 1), "launches_per_step": 2,
+            "separate_selection": {"us_per_step": round(us3, 3), "tok_s": round(1.0 / (us3 * 1e-6), 1),
+                                   "launches_per_step": 3}}
 
 
 def cpu_baseline(w, qb, kbits, vb, dec, budget_s):

@@ -275,6 +275,28 @@ int kvs_paged_decode_scored(const void* q, void* k_pool, void* v_pool, int num_b
                             size_t workspace_bytes, void* stream);
 
 /*
+ * kvs_paged_decode_scored_select - kvs_paged_decode_scored followed by what
+ *   kvs_decode_select_slot would do for the next step, in the same launches: the workgroup
+ *   that adds a (sequence, KV head)'s probabilities to its slot scores then picks the slot of
+ *   the next token, with n_filled = ctx_lens[b] (the live slots after this step) and position
+ *   next_pos[b], under cap and alpha, and marks it (score 0, position next_pos[b]).  One
+ *   decode step with eviction is then two launches instead of three; the first step's slot
+ *   comes from kvs_decode_select_slot.  [KVS] Key techniques 1 (step preparation: the lowest
+ *   score is replaced) and 2, last paragraph.
+ * In: as kvs_paged_decode_scored, plus slot_pos [B][Hkv][slot_stride] int32 (read and
+ *   written), cap, alpha, next_pos [B] int32.  Out: next_dst_slots [B][Hkv] int32.
+ * Errors: as kvs_paged_decode_scored; KVS_E_INVAL also for a NULL slot_pos, next_pos or
+ *   next_dst_slots, or unless 0 <= alpha < cap <= slot_stride and max_ctx <= cap.
+ */
+int kvs_paged_decode_scored_select(const void* q, void* k_pool, void* v_pool, int num_blocks,
+                                   const int32_t* block_tables, int max_blocks, const int32_t* ctx_lens, int batch,
+                                   int max_ctx, int hq, int hkv, int d, float scale, const void* new_k,
+                                   const void* new_v, const int32_t* dst_slots, float* slot_scores, int32_t* slot_pos,
+                                   int slot_stride, int cap, int alpha, const int32_t* next_pos,
+                                   int32_t* next_dst_slots, void* o, float* lse_opt, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/*
  * kvs_copy_blocks - device side of copy-on-write: whole-block copies in both pools.
  *   [PAG] "Sharing blocks between sequences": a sequence that must write a block still
  *   used by others copies it first.
@@ -330,6 +352,14 @@ int kvs_paged_decode_scored_fp8(const void* q, void* k_pool, void* v_pool, float
                                 int batch, int max_ctx, int hq, int hkv, int d, float scale, const void* new_k,
                                 const void* new_v, const int32_t* dst_slots, float* slot_scores, int slot_stride,
                                 void* o, float* lse_opt, void* workspace, size_t workspace_bytes, void* stream);
+/* kvs_paged_decode_scored_select on the 8-bit cache (as kvs_paged_decode_scored_fp8). */
+int kvs_paged_decode_scored_select_fp8(const void* q, void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                                       int num_blocks, const int32_t* block_tables, int max_blocks,
+                                       const int32_t* ctx_lens, int batch, int max_ctx, int hq, int hkv, int d,
+                                       float scale, const void* new_k, const void* new_v, const int32_t* dst_slots,
+                                       float* slot_scores, int32_t* slot_pos, int slot_stride, int cap, int alpha,
+                                       const int32_t* next_pos, int32_t* next_dst_slots, void* o, float* lse_opt,
+                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * kvs_paged_decode_noalloc - kvs_paged_decode for callers that cannot allocate device memory

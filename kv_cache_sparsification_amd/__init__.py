@@ -13,7 +13,7 @@ from .ops import (kvs_prefill_attn_lse, kvs_window_score, kvs_topk_select, kvs_c
                   kvs_paged_decode_scored_workspace_size, new_pools_fp8, kvs_compact_paged_fp8,
                   kvs_paged_decode_fp8, kvs_copy_blocks_fp8, kvs_prefill_attn_lse_chunk, kvs_window_score_chunk,
                   kvs_gather_paged, kvs_paged_decode_scored_fp8, kvs_probe_stream_read,
-                  kvs_probe_timestamp,
+                  kvs_probe_timestamp, kvs_paged_decode_scored_select, kvs_paged_decode_scored_select_fp8,
                   kvs_paged_decode_noalloc)
 from .allocator import BlockAllocator
 from .pipeline import (layer_policy, keep_counts, prefill_compress_layer, prefill_compress_layer_chunked,
@@ -28,6 +28,7 @@ __all__ = [
     "new_pools_fp8", "kvs_compact_paged_fp8", "kvs_paged_decode_fp8", "kvs_copy_blocks_fp8",
     "kvs_prefill_attn_lse_chunk", "kvs_window_score_chunk", "kvs_gather_paged", "kvs_paged_decode_scored_fp8",
     "kvs_probe_stream_read", "kvs_probe_timestamp", "kvs_paged_decode_noalloc",
+    "kvs_paged_decode_scored_select", "kvs_paged_decode_scored_select_fp8",
     "BlockAllocator", "layer_policy", "keep_counts", "prefill_compress_layer",
     "prefill_compress_layer_chunked", "prefix_rows_reused", "prefill_compress_admission", "BlockHashIndex",
     "chained_block_keys",

@@ -44,6 +44,12 @@ SIGNATURES = {
     "kvs_paged_decode_scored_fp8": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _c_int, _vp, _c_int, _c_int,
                                              _c_int, _c_int, _c_int, _c_float, _vp, _vp, _vp, _vp, _c_int, _vp, _vp,
                                              _vp, _c_size, _vp]),
+    "kvs_paged_decode_scored_select": (_c_int, [_vp, _vp, _vp, _c_int, _vp, _c_int, _vp, _c_int, _c_int, _c_int,
+                                                _c_int, _c_int, _c_float, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int,
+                                                _c_int, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "kvs_paged_decode_scored_select_fp8": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _c_int, _vp, _c_int,
+                                                    _c_int, _c_int, _c_int, _c_int, _c_float, _vp, _vp, _vp, _vp, _vp,
+                                                    _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
     "kvs_copy_blocks_fp8": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _c_int, _vp]),
     "kvs_prefill_attn_lse_chunk": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                             _c_int, _c_float, _vp, _vp, _vp, _vp, _vp]),

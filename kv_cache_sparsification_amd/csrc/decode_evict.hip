@@ -13,9 +13,9 @@
 //   slot_pos     the token's prompt-local position, -1 for an empty slot.
 // While a cache has room the new token is appended; once it holds `cap` tokens each KV head
 // replaces its lowest-score token among those older than the alpha most recent positions,
-// ties going to the older position.  Scores are non-negative, so (score bits, position) as
-// one 64-bit key orders like (score, position).
+// ties going to the older position (slot_select.h).
 #include "kvs_common.h"
+#include "slot_select.h"
 
 namespace kvs {
 namespace {
@@ -48,68 +48,14 @@ __global__ __launch_bounds__(kThreads) void slot_init_kernel(const float* __rest
   }
 }
 
-__global__ __launch_bounds__(kThreads) void select_slot_kernel(float* __restrict__ slot_scores,
-                                                               int32_t* __restrict__ slot_pos, int slot_stride,
-                                                               const int32_t* __restrict__ n_filled, int hkv, int cap,
-                                                               const int32_t* __restrict__ new_pos, int alpha,
-                                                               int32_t* __restrict__ dst_slot) {
-  __shared__ unsigned long long best;
-  __shared__ int best_slot;
-  const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  float* sc = slot_scores + ((size_t)b * hkv + g) * slot_stride;
-  int32_t* ps = slot_pos + ((size_t)b * hkv + g) * slot_stride;
-  const int n = n_filled[b];
-  const int np = new_pos[b];
-  int dst = n;                                    // room left: append
-  if (n >= cap) {                                 // block-uniform
-    if (tid == 0) {
-      best = ~0ull;
-      best_slot = -1;
-    }
-    __syncthreads();
-    // Slots are read kPer per thread at a time, all loads of a round in flight together; with
-    // cap <= kThreads * kPer (one round) the second pass reuses the registers.
-    constexpr int kPer = 8;
-    auto key_of = [&](int p, float v) {
-      return (p >= 0 && p < np - alpha) ? (((unsigned long long)__float_as_uint(v) << 32) | (unsigned)p) : ~0ull;
-    };
-    unsigned long long keys[kPer];
-    unsigned long long mine = ~0ull;
-    for (int c0 = 0; c0 < cap; c0 += kThreads * kPer) {
-      int p[kPer];
-      float v[kPer];
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        const int t = c0 + j * kThreads + tid;
-        p[j] = t < cap ? ps[t] : -1;
-        v[j] = t < cap ? sc[t] : 0.f;
-      }
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        keys[j] = key_of(p[j], v[j]);
-        mine = keys[j] < mine ? keys[j] : mine;
-      }
-    }
-    atomicMin(&best, mine);
-    __syncthreads();
-    if (cap <= kThreads * kPer) {                 // the registers hold the only round
-#pragma unroll
-      for (int j = 0; j < kPer; ++j)
-        if (keys[j] != ~0ull && keys[j] == best) best_slot = j * kThreads + tid;
-    } else {
-      for (int t = tid; t < cap; t += kThreads)   // positions are distinct: one slot matches
-        if (key_of(ps[t], sc[t]) == best && best != ~0ull) best_slot = t;
-    }
-    __syncthreads();
-    dst = best_slot;                              // -1 only if no slot may go (cap <= alpha: refused on the host)
-  }
-  if (tid == 0) {
-    dst_slot[(size_t)b * hkv + g] = dst;
-    if (dst >= 0) {
-      sc[dst] = 0.f;
-      ps[dst] = np;
-    }
-  }
+__global__ __launch_bounds__(kSelectThreads) void select_slot_kernel(float* __restrict__ slot_scores,
+                                                                     int32_t* __restrict__ slot_pos, int slot_stride,
+                                                                     const int32_t* __restrict__ n_filled, int hkv,
+                                                                     int cap, const int32_t* __restrict__ new_pos,
+                                                                     int alpha, int32_t* __restrict__ dst_slot) {
+  const int g = blockIdx.x, b = blockIdx.y;
+  select_slot_block(slot_scores + ((size_t)b * hkv + g) * slot_stride, slot_pos + ((size_t)b * hkv + g) * slot_stride,
+                    n_filled[b], cap, new_pos[b], alpha, dst_slot + (size_t)b * hkv + g);
 }
 
 }  // namespace
@@ -139,7 +85,7 @@ extern "C" int kvs_decode_select_slot(float* slot_scores, int32_t* slot_pos, int
     return fail(KVS_E_INVAL, "kvs_decode_select_slot: need 0 <= alpha < cap <= slot_stride (alpha=%d cap=%d stride=%d)",
                 alpha, cap, slot_stride);
   if (batch == 0) return KVS_OK;
-  hipLaunchKernelGGL(select_slot_kernel, dim3(hkv, batch), dim3(kThreads), 0, as_stream(stream), slot_scores,
+  hipLaunchKernelGGL(select_slot_kernel, dim3(hkv, batch), dim3(kSelectThreads), 0, as_stream(stream), slot_scores,
                      slot_pos, slot_stride, n_filled, hkv, cap, new_pos, alpha, dst_slot);
   return launch_status("kvs_decode_select_slot");
 }

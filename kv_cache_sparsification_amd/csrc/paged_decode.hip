@@ -29,6 +29,7 @@
 #include <mutex>
 
 #include "kvs_common.h"
+#include "slot_select.h"
 
 namespace kvs {
 namespace {
@@ -559,10 +560,15 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict
 // of the G query heads (output, LSE), then adds every live slot's probability summed over
 // those heads, exp2(logit - LSE2), to its score: the decode row's contribution to S.
 template <int D>
-__global__ __launch_bounds__(256) void decode_merge_score_kernel(
+// With next_dst set, the same workgroup then chooses the slot of the next step's token from the
+// scores it has just updated (select_slot_block, with the live count L as n_filled), which
+// saves the next step a launch.
+__global__ __launch_bounds__(kSelectThreads) void decode_merge_score_kernel(
     const float* __restrict__ ws, const float* __restrict__ logits, int logit_stride,
     const int32_t* __restrict__ ctx_lens, int hq, int hkv, int max_blocks, int splits, int bps,
-    uint16_t* __restrict__ o, float* __restrict__ lse_out, float* __restrict__ slot_scores, int slot_stride) {
+    uint16_t* __restrict__ o, float* __restrict__ lse_out, float* __restrict__ slot_scores, int slot_stride,
+    int32_t* __restrict__ slot_pos, int cap, int alpha, const int32_t* __restrict__ next_pos,
+    int32_t* __restrict__ next_dst) {
   __shared__ float lse2[16];
   const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int G = hq / hkv;
@@ -583,10 +589,15 @@ __global__ __launch_bounds__(256) void decode_merge_score_kernel(
   __syncthreads();
   const float* lg = logits + ((size_t)b * hq + g * G) * logit_stride;
   float* sc = slot_scores + ((size_t)b * hkv + g) * slot_stride;
-  for (int t = tid; t < L; t += 256) {
+  for (int t = tid; t < L; t += kSelectThreads) {
     float sum = 0.f;
     for (int c = 0; c < G; ++c) sum += __builtin_amdgcn_exp2f(lg[(size_t)c * logit_stride + t] - lse2[c]);
     sc[t] += sum;
+  }
+  if (next_dst) {   // grid-uniform
+    __syncthreads();   // every updated score visible to the whole workgroup
+    select_slot_block(sc, slot_pos + ((size_t)b * hkv + g) * slot_stride, L, cap, next_pos[b], alpha,
+                      next_dst + (size_t)b * hkv + g);
   }
 }
 
@@ -794,9 +805,15 @@ static int run_scored(const char* name, const void* q, void* k_pool, void* v_poo
                       bool f8, int num_blocks, const int32_t* block_tables, int max_blocks, const int32_t* ctx_lens,
                       int batch, int max_ctx, int hq, int hkv, int d, float scale, const void* new_k,
                       const void* new_v, const int32_t* dst_slots, float* slot_scores, int slot_stride, void* o,
-                      float* lse_opt, void* workspace, size_t workspace_bytes, void* stream) {
+                      float* lse_opt, void* workspace, size_t workspace_bytes, void* stream,
+                      int32_t* slot_pos = nullptr, int cap = 0, int alpha = 0, const int32_t* next_pos = nullptr,
+                      int32_t* next_dst = nullptr) {
   if (!q || !k_pool || !v_pool || !block_tables || !ctx_lens || !o || !slot_scores || (f8 && (!k_scale || !v_scale)))
     return fail(KVS_E_INVAL, "%s: NULL tensor", name);
+  if (next_dst && (!slot_pos || !next_pos)) return fail(KVS_E_INVAL, "%s: NULL tensor", name);
+  if (next_dst && (alpha < 0 || alpha >= cap || cap > slot_stride || max_ctx > cap))
+    return fail(KVS_E_INVAL, "%s: need 0 <= alpha < cap <= slot_stride and max_ctx <= cap (alpha=%d cap=%d stride=%d)",
+                name, alpha, cap, slot_stride);
   if ((new_k == nullptr) != (new_v == nullptr)) return fail(KVS_E_INVAL, "%s: new_k and new_v go together", name);
   if (dst_slots && !new_k) return fail(KVS_E_INVAL, "%s: dst_slots without a new token", name);
   if (batch < 0 || max_ctx < 1 || hq <= 0 || hkv <= 0 || hq % hkv || hq / hkv > 16 || (d != 64 && d != 128) ||
@@ -840,11 +857,13 @@ static int run_scored(const char* name, const void* q, void* k_pool, void* v_poo
   int rc = launch_status(name);
   if (rc != KVS_OK) return rc;
   if (d == 128)
-    hipLaunchKernelGGL(decode_merge_score_kernel<128>, dim3(hkv, batch), dim3(256), 0, st, ws, logits, max_ctx,
-                       ctx_lens, hq, hkv, max_blocks, p.splits, p.bps, oo, lse_opt, slot_scores, slot_stride);
+    hipLaunchKernelGGL(decode_merge_score_kernel<128>, dim3(hkv, batch), dim3(kSelectThreads), 0, st, ws, logits,
+                       max_ctx, ctx_lens, hq, hkv, max_blocks, p.splits, p.bps, oo, lse_opt, slot_scores, slot_stride,
+                       slot_pos, cap, alpha, next_pos, next_dst);
   else
-    hipLaunchKernelGGL(decode_merge_score_kernel<64>, dim3(hkv, batch), dim3(256), 0, st, ws, logits, max_ctx,
-                       ctx_lens, hq, hkv, max_blocks, p.splits, p.bps, oo, lse_opt, slot_scores, slot_stride);
+    hipLaunchKernelGGL(decode_merge_score_kernel<64>, dim3(hkv, batch), dim3(kSelectThreads), 0, st, ws, logits,
+                       max_ctx, ctx_lens, hq, hkv, max_blocks, p.splits, p.bps, oo, lse_opt, slot_scores, slot_stride,
+                       slot_pos, cap, alpha, next_pos, next_dst);
   return launch_status(name);
 }
 
@@ -868,4 +887,34 @@ extern "C" int kvs_paged_decode_scored_fp8(const void* q, void* k_pool, void* v_
   return run_scored("kvs_paged_decode_scored_fp8", q, k_pool, v_pool, k_scale, v_scale, true, num_blocks,
                     block_tables, max_blocks, ctx_lens, batch, max_ctx, hq, hkv, d, scale, new_k, new_v, dst_slots,
                     slot_scores, slot_stride, o, lse_opt, workspace, workspace_bytes, stream);
+}
+
+extern "C" int kvs_paged_decode_scored_select(const void* q, void* k_pool, void* v_pool, int num_blocks,
+                                              const int32_t* block_tables, int max_blocks, const int32_t* ctx_lens,
+                                              int batch, int max_ctx, int hq, int hkv, int d, float scale,
+                                              const void* new_k, const void* new_v, const int32_t* dst_slots,
+                                              float* slot_scores, int32_t* slot_pos, int slot_stride, int cap,
+                                              int alpha, const int32_t* next_pos, int32_t* next_dst_slots, void* o,
+                                              float* lse_opt, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!next_dst_slots) return fail(KVS_E_INVAL, "kvs_paged_decode_scored_select: NULL tensor");
+  return run_scored("kvs_paged_decode_scored_select", q, k_pool, v_pool, nullptr, nullptr, false, num_blocks,
+                    block_tables, max_blocks, ctx_lens, batch, max_ctx, hq, hkv, d, scale, new_k, new_v, dst_slots,
+                    slot_scores, slot_stride, o, lse_opt, workspace, workspace_bytes, stream, slot_pos, cap, alpha,
+                    next_pos, next_dst_slots);
+}
+
+extern "C" int kvs_paged_decode_scored_select_fp8(const void* q, void* k_pool, void* v_pool, float* k_scale,
+                                                  float* v_scale, int num_blocks, const int32_t* block_tables,
+                                                  int max_blocks, const int32_t* ctx_lens, int batch, int max_ctx,
+                                                  int hq, int hkv, int d, float scale, const void* new_k,
+                                                  const void* new_v, const int32_t* dst_slots, float* slot_scores,
+                                                  int32_t* slot_pos, int slot_stride, int cap, int alpha,
+                                                  const int32_t* next_pos, int32_t* next_dst_slots, void* o,
+                                                  float* lse_opt, void* workspace, size_t workspace_bytes,
+                                                  void* stream) {
+  if (!next_dst_slots) return fail(KVS_E_INVAL, "kvs_paged_decode_scored_select_fp8: NULL tensor");
+  return run_scored("kvs_paged_decode_scored_select_fp8", q, k_pool, v_pool, k_scale, v_scale, true, num_blocks,
+                    block_tables, max_blocks, ctx_lens, batch, max_ctx, hq, hkv, d, scale, new_k, new_v, dst_slots,
+                    slot_scores, slot_stride, o, lse_opt, workspace, workspace_bytes, stream, slot_pos, cap, alpha,
+                    next_pos, next_dst_slots);
 }

@@ -398,6 +398,86 @@ def kvs_paged_decode_scored_fp8(q, k_pool, v_pool, k_scale, v_scale, block_table
     return o
 
 
+def _select_args(slot_scores, slot_pos, next_pos, next_dst_slots):
+    _dev(slot_pos, torch.int32, "slot_pos"); _dev(next_pos, torch.int32, "next_pos")
+    if slot_pos.shape != slot_scores.shape:
+        raise ValueError("slot_pos must have slot_scores' shape [B][Hkv][stride]")
+    B, hkv, _ = slot_scores.shape
+    if next_dst_slots is None:
+        next_dst_slots = torch.empty(B, hkv, device=slot_scores.device, dtype=torch.int32)
+    return _dev(next_dst_slots, torch.int32, "next_dst_slots")
+
+
+def kvs_paged_decode_scored_select(q, k_pool, v_pool, block_tables, ctx_lens, max_ctx: int, slot_scores, slot_pos,
+                                   cap: int, alpha: int, next_pos, next_dst_slots=None, new_k=None, new_v=None,
+                                   dst_slots=None, scale: Optional[float] = None, o=None, lse=None, workspace=None,
+                                   stream=None):
+    """kvs_paged_decode_scored, then the next step's slot choice in the same launches.
+    Returns (o, next_dst_slots)."""
+    _dev(q, torch.bfloat16, "q"); _dev(k_pool, torch.bfloat16, "k_pool"); _dev(v_pool, torch.bfloat16, "v_pool")
+    _dev(block_tables, torch.int32, "block_tables"); _dev(ctx_lens, torch.int32, "ctx_lens")
+    _dev(slot_scores, torch.float32, "slot_scores")
+    nxt = _select_args(slot_scores, slot_pos, next_pos, next_dst_slots)
+    B, hq, d = q.shape
+    hkv = k_pool.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if new_k is not None:
+        _dev(new_k, torch.bfloat16, "new_k"); _dev(new_v, torch.bfloat16, "new_v")
+    if dst_slots is not None:
+        _dev(dst_slots, torch.int32, "dst_slots")
+    o = torch.empty_like(q) if o is None else _dev(o, torch.bfloat16, "o")
+    if lse is not None:
+        _dev(lse, torch.float32, "lse")
+    need = kvs_paged_decode_scored_workspace_size(B, hq, hkv, d, int(max_ctx))
+    if workspace is None:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    check(lib.kvs_paged_decode_scored_select(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), k_pool.shape[0],
+                                             block_tables.data_ptr(), block_tables.shape[1], ctx_lens.data_ptr(), B,
+                                             int(max_ctx), hq, hkv, d, float(scale), _ptr(new_k), _ptr(new_v),
+                                             _ptr(dst_slots), slot_scores.data_ptr(), slot_pos.data_ptr(),
+                                             slot_scores.shape[2], int(cap), int(alpha), next_pos.data_ptr(),
+                                             nxt.data_ptr(), o.data_ptr(), _ptr(lse), workspace.data_ptr(), ws_bytes,
+                                             _stream(stream)))
+    return o, nxt
+
+
+def kvs_paged_decode_scored_select_fp8(q, k_pool, v_pool, k_scale, v_scale, block_tables, ctx_lens, max_ctx: int,
+                                       slot_scores, slot_pos, cap: int, alpha: int, next_pos, next_dst_slots=None,
+                                       new_k=None, new_v=None, dst_slots=None, scale: Optional[float] = None, o=None,
+                                       lse=None, workspace=None, stream=None):
+    """kvs_paged_decode_scored_select over an 8-bit cache.  Returns (o, next_dst_slots)."""
+    _dev(q, torch.bfloat16, "q")
+    nb, hkv, _ = _check_fp8_pools(k_pool, v_pool, k_scale, v_scale)
+    _dev(block_tables, torch.int32, "block_tables"); _dev(ctx_lens, torch.int32, "ctx_lens")
+    _dev(slot_scores, torch.float32, "slot_scores")
+    nxt = _select_args(slot_scores, slot_pos, next_pos, next_dst_slots)
+    B, hq, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if new_k is not None:
+        _dev(new_k, torch.bfloat16, "new_k"); _dev(new_v, torch.bfloat16, "new_v")
+    if dst_slots is not None:
+        _dev(dst_slots, torch.int32, "dst_slots")
+    o = torch.empty_like(q) if o is None else _dev(o, torch.bfloat16, "o")
+    if lse is not None:
+        _dev(lse, torch.float32, "lse")
+    need = kvs_paged_decode_scored_workspace_size(B, hq, hkv, d, int(max_ctx))
+    if workspace is None:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    check(lib.kvs_paged_decode_scored_select_fp8(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                                 k_scale.data_ptr(), v_scale.data_ptr(), nb, block_tables.data_ptr(),
+                                                 block_tables.shape[1], ctx_lens.data_ptr(), B, int(max_ctx), hq, hkv,
+                                                 d, float(scale), _ptr(new_k), _ptr(new_v), _ptr(dst_slots),
+                                                 slot_scores.data_ptr(), slot_pos.data_ptr(), slot_scores.shape[2],
+                                                 int(cap), int(alpha), next_pos.data_ptr(), nxt.data_ptr(),
+                                                 o.data_ptr(), _ptr(lse), workspace.data_ptr(), ws_bytes,
+                                                 _stream(stream)))
+    return o, nxt
+
+
 # ---- measurement helper
 def kvs_probe_stream_read(buf, grid: int, sink=None, key: int = 0x9E3779B9, stream=None):
     """Read every byte of the contiguous device tensor buf once (the streaming-read ceiling probe)."""

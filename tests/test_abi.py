@@ -63,6 +63,15 @@ def test_host_validation_rejects_before_launch():
     assert L.kvs_probe_stream_read(fake + 8, 1024, 64, 0, fake, None) == -1     # misaligned
     assert L.kvs_probe_stream_read(fake, 1024, 0, 0, fake, None) == -1          # empty grid
     assert L.kvs_probe_stream_read(None, 1024, 64, 0, fake, None) == -1
+    # the scored decode that also chooses the next step's slot: its extra arguments
+    args = lambda nxt, slot_pos, cap, alpha, max_ctx: (fake, fake, fake, 64, fake, 8, fake, 1, max_ctx, 32, 8, 128, 0.1,
+                                                       fake, fake, fake, fake, slot_pos, 128, cap, alpha, fake, nxt,
+                                                       fake, None, fake, 1 << 20, None)
+    assert L.kvs_paged_decode_scored_select(*args(None, fake, 128, 32, 128)) == -1     # no next_dst_slots
+    assert L.kvs_paged_decode_scored_select(*args(fake, None, 128, 32, 128)) == -1     # no slot_pos
+    assert L.kvs_paged_decode_scored_select(*args(fake, fake, 128, 128, 128)) == -1    # alpha >= cap
+    assert L.kvs_paged_decode_scored_select(*args(fake, fake, 100, 32, 128)) == -1     # max_ctx > cap
+    assert L.kvs_paged_decode_scored_select(*args(fake, fake, 256, 32, 128)) == -1     # cap > slot_stride
     # the clock stamp: its output pointer is checked on the host
     assert L.kvs_probe_timestamp(None, None) == -1
     assert L.kvs_probe_timestamp(fake + 4, None) == -1                          # not 8-byte aligned

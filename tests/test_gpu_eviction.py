@@ -246,3 +246,67 @@ def test_eviction_llama8b_layer_fp8():
     for g in range(w.hkv):
         np.testing.assert_array_equal(gk[:, g], c.k[g], err_msg=f"K head {g}")
         np.testing.assert_array_equal(gv[:, g], c.v[g], err_msg=f"V head {g}")
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_select_in_the_scored_decode_matches_separate_launches(fp8):
+    """kvs_paged_decode_scored_select (the next step's slot chosen by the merge-and-score kernel)
+    gives, step for step, the slots, outputs, slot state and pools of kvs_decode_select_slot
+    followed by kvs_paged_decode_scored (checked against the oracle above), bit for bit:
+    three prompts (30, 48, 100 tokens), budget 48, alpha 8, 40 steps through the appends and
+    the evictions."""
+    from workloads import Workload
+    w = Workload(cid=92, name="fused selection", hq=8, hkv=2, d=128, alpha=8, n_layers=1, budgets=[48],
+                 decode_steps=40, sink_positions=(0,), num_seqs=3)
+    lengths = [30, 48, 100]
+    cap, alpha, steps = 48, 8, 40
+    B = len(lengths)
+    _say(f"scored decode with the next selection fused, fp8={fp8}, {steps} steps")
+    q, k, v, cu = wl.device_batch(w, 0, lengths, list(range(B)))
+    cu_d = i32(cu)
+    nb_seq = -(-cap // 16)
+    nblocks = B * nb_seq + 4
+    alloc = kvs.BlockAllocator(nblocks, list(np.random.default_rng(5).permutation(nblocks)))
+    k16, v16 = kvs.new_pools(nblocks, w.hkv, w.d)
+    res = kvs.prefill_compress_layer(q, k, v, cu_d, lengths, alpha, cap, alloc, k16, v16, nb_seq)
+    if fp8:
+        pools = list(kvs.new_pools_fp8(nblocks, w.hkv, w.d))
+        kvs.kvs_compact_paged_fp8(k, v, cu_d, res["keep_idx"], res["keep_offsets"], cap, *pools, res["tables_dev"])
+    else:
+        pools = [k16, v16]
+    stride = nb_seq * 16
+    sc_a, pos_a = kvs.kvs_slot_init(res["scores"], cu_d, res["keep_idx"], res["keep_offsets"], stride)
+    torch.cuda.synchronize()
+    pools_b = [t.clone() for t in pools]
+    sc_b, pos_b = sc_a.clone(), pos_a.clone()
+    tables = [list(t) for t in res["tables"]]
+    tbl = np.full((B, nb_seq), -1, np.int32)
+    n_fill = list(res["kept"])
+    ws = torch.empty(kvs.kvs_paged_decode_scored_workspace_size(B, w.hq, w.hkv, w.d, cap), dtype=torch.uint8,
+                     device="cuda")
+    scored = kvs.kvs_paged_decode_scored_fp8 if fp8 else kvs.kvs_paged_decode_scored
+    fused = kvs.kvs_paged_decode_scored_select_fp8 if fp8 else kvs.kvs_paged_decode_scored_select
+    dst_b = kvs.kvs_decode_select_slot(sc_b, pos_b, i32(n_fill), i32([n for n in lengths]), cap, alpha)
+    for step in range(steps):
+        for s in range(B):
+            if n_fill[s] < cap and n_fill[s] % 16 == 0 and n_fill[s] // 16 >= len(tables[s]):
+                tables[s].append(alloc.alloc())
+            tbl[s, :len(tables[s])] = tables[s]
+        new_pos = [n + step for n in lengths]
+        dst_a = kvs.kvs_decode_select_slot(sc_a, pos_a, i32(n_fill), i32(new_pos), cap, alpha)
+        n_fill = [min(x + 1, cap) for x in n_fill]
+        dq, dk, dv = wl.device_decode_step(w, 0, step, list(range(B)))
+        o_a = scored(dq, *pools, i32(tbl), i32(n_fill), cap, sc_a, new_k=dk, new_v=dv, dst_slots=dst_a,
+                     workspace=ws)
+        np.testing.assert_array_equal(dst_b.cpu().numpy(), dst_a.cpu().numpy(), err_msg=f"slots, step {step}")
+        o_b, dst_next = fused(dq, *pools_b, i32(tbl), i32(n_fill), cap, sc_b, pos_b, cap, alpha,
+                              i32([p + 1 for p in new_pos]), new_k=dk, new_v=dv, dst_slots=dst_b, workspace=ws)
+        np.testing.assert_array_equal(bf16_bits(o_b), bf16_bits(o_a), err_msg=f"o, step {step}")
+        dst_b = dst_next.clone()
+    # the fused path has already chosen (and marked) the slot of step `steps`
+    dst_a = kvs.kvs_decode_select_slot(sc_a, pos_a, i32(n_fill), i32([n + steps for n in lengths]), cap, alpha)
+    np.testing.assert_array_equal(dst_b.cpu().numpy(), dst_a.cpu().numpy())
+    np.testing.assert_array_equal(sc_b.cpu().numpy().view(np.uint32), sc_a.cpu().numpy().view(np.uint32))
+    np.testing.assert_array_equal(pos_b.cpu().numpy(), pos_a.cpu().numpy())
+    for ta, tb in zip(pools, pools_b):
+        np.testing.assert_array_equal(tb.view(torch.uint8).cpu().numpy(), ta.view(torch.uint8).cpu().numpy())

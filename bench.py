@@ -777,7 +777,8 @@ def paged_memory(wl, iterations=1000):
 
 def fp8_layer(kvs, torch, wl, w, k, v, cu_d, keep, keep_off, steps):
     """The bench layer with an 8-bit cache: the quantizing compaction of the kept rows (timed
-    per launch with events) and `steps` decode steps with append (one HIP graph)."""
+    like the other prompt-side kernels, as a graph of back-to-back launches) and `steps` decode
+    steps with append (one HIP graph)."""
     dev = torch.device("cuda:0")
     n, hq, hkv, d, kb = w.fixed_len, w.hq, w.hkv, w.d, w.budgets[0]
     k_eff = min(kb, n)
@@ -785,17 +786,8 @@ def fp8_layer(kvs, torch, wl, w, k, v, cu_d, keep, keep_off, steps):
     nblk = -(-max_ctx // 16)
     pools = kvs.new_pools_fp8(nblk, hkv, d, device=dev)
     tbl = torch.arange(nblk, dtype=torch.int32, device=dev).flip(0).reshape(1, nblk).contiguous()
-    stream = torch.cuda.current_stream()
-    for _ in range(3):
-        kvs.kvs_compact_paged_fp8(k, v, cu_d, keep, keep_off, k_eff, *pools, tbl)
-    reps = 20
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
-    evs[0].record(stream)
-    for i in range(reps):
-        kvs.kvs_compact_paged_fp8(k, v, cu_d, keep, keep_off, k_eff, *pools, tbl)
-        evs[i + 1].record(stream)
-    torch.cuda.synchronize()
-    comp_us = sum(evs[i].elapsed_time(evs[i + 1]) for i in range(reps)) * 1e3 / reps
+    comp_us = kernel_graph_us(torch, lambda: kvs.kvs_compact_paged_fp8(k, v, cu_d, keep, keep_off, k_eff, *pools, tbl),
+                              50)
     comp_bytes = 4 * k_eff * hkv * d + 2 * k_eff * hkv * (d + 4) + 4 * hkv * k_eff
     ctx = torch.arange(k_eff + 1, k_eff + steps + 1, dtype=torch.int32, device=dev).reshape(steps, 1)
     qs, nks, nvs = zip(*[wl.device_decode_step(w, 0, 2000 + s, [0], device=dev) for s in range(steps)])
@@ -901,8 +893,9 @@ def decode_32_layers(kvs, torch, wl, steps, fp8=False):
 def prefix_reuse(kvs, torch, wl, w, q, k, v, reps=10):
     """The bench layer when the first 2048 prompt tokens are found in the cache (block-hash
     match): their K/V come back from the blocks (gather) and only rows 2048-3999 are prefilled
-    against all 4000 keys, then window score, top-k and compaction as usual.  Per-launch HIP
-    event times against the whole-prompt step."""
+    against all 4000 keys, then window score, top-k and compaction as usual, captured as one
+    graph and timed with clock stamps between the launches (as the timed step's prompt phase)."""
+    import numpy as np
     dev = torch.device("cuda:0")
     n, hq, hkv, d, alpha, kb = w.fixed_len, w.hq, w.hkv, w.d, w.alpha, w.budgets[0]
     P = 2048
@@ -923,31 +916,46 @@ def prefix_reuse(kvs, torch, wl, w, q, k, v, reps=10):
     ctbl = torch.arange(nblk_p, nblk_p + (-(-k_eff // 16)), dtype=torch.int32, device=dev).reshape(1, -1)
     counts = torch.tensor([P], dtype=torch.int32, device=dev)
     start = torch.tensor([0], dtype=torch.int32, device=dev)
-    stream = torch.cuda.current_stream()
     marks = ["gather", "prefill_chunk", "window", "topk", "compact"]
+    o_c = torch.empty_like(q_rows)
+    lse_c = torch.empty(hq, n - P, dtype=torch.float32, device=dev)
+    S_c = torch.empty(hkv, n, dtype=torch.float32, device=dev)
+    keep_c = torch.empty(hkv * k_eff, dtype=torch.int32, device=dev)
+    stamps = torch.zeros(len(marks) + 1, dtype=torch.int64, device=dev)
 
-    def step(ev):
-        ev[0].record(stream)
+    def step():
+        kvs.kvs_probe_timestamp(stamps[0:1])
         kvs.kvs_gather_paged(k_pool, v_pool, tbl_p, counts, start, P, k_all, v_all)
-        ev[1].record(stream)
-        o, lse = kvs.kvs_prefill_attn_lse_chunk(q_rows, k_all, v_all, cu_q, cu_full, n - P, n)
-        ev[2].record(stream)
-        S = kvs.kvs_window_score_chunk(q_rows, k_all, lse, cu_q, cu_full, n, alpha)
-        ev[3].record(stream)
-        keep = kvs.kvs_topk_select(S, cu_full, n, alpha, kb, keep_off, total_keep=k_eff)
-        ev[4].record(stream)
-        kvs.kvs_compact_paged(k_all, v_all, cu_full, keep, keep_off, k_eff, k_pool, v_pool, ctbl)
-        ev[5].record(stream)
+        kvs.kvs_probe_timestamp(stamps[1:2])
+        kvs.kvs_prefill_attn_lse_chunk(q_rows, k_all, v_all, cu_q, cu_full, n - P, n, o=o_c, lse=lse_c)
+        kvs.kvs_probe_timestamp(stamps[2:3])
+        kvs.kvs_window_score_chunk(q_rows, k_all, lse_c, cu_q, cu_full, n, alpha, scores=S_c)
+        kvs.kvs_probe_timestamp(stamps[3:4])
+        kvs.kvs_topk_select(S_c, cu_full, n, alpha, kb, keep_off, keep_idx=keep_c)
+        kvs.kvs_probe_timestamp(stamps[4:5])
+        kvs.kvs_compact_paged(k_all, v_all, cu_full, keep_c, keep_off, k_eff, k_pool, v_pool, ctbl)
+        kvs.kvs_probe_timestamp(stamps[5:6])
 
-    warm = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
-    step(warm)
-    runs = []
-    for _ in range(reps):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
-        step(ev)
-        runs.append(ev)
+    # one captured graph, a clock stamp before each launch and after the last: each stage's span
+    # is its kernel plus one in-graph launch boundary; the graph's start latency is outside
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step()
+    stream.wait_stream(side)
     torch.cuda.synchronize()
-    per = {m: sum(r[i].elapsed_time(r[i + 1]) for r in runs) * 1e3 / reps for i, m in enumerate(marks)}
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    spans = []
+    for r in range(reps + 1):
+        graph.replay()
+        torch.cuda.synchronize()
+        if r:
+            t = stamps.cpu().numpy().astype(np.float64) * (1e6 / REALTIME_HZ)      # us
+            spans.append(np.diff(t))
+    per = {m: float(np.mean([x[i] for x in spans])) for i, m in enumerate(marks)}
     total = sum(per.values())
     flops = 2.0 * d * hq * sum(2 * (i + 1) for i in range(P, n))
     return {"workload": f"bench layer n={n} with the first {P} tokens reused from the cache: gather, prefill of "

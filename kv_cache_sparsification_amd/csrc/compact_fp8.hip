@@ -25,11 +25,21 @@ namespace {
 
 constexpr int kWavesPerWG = 4;
 
-// Maximum over the n lanes (n a power of two <= 16) that share lane / n.
+// Maximum over the N lanes (N = 8 or 16) that share lane / N, with DPP lane moves inside the
+// 16-lane rows instead of LDS permutes: the quad swaps (lane ^ 1, lane ^ 2) give each quad's
+// maximum, the half-row mirror (lane i <- 7 - i) each 8 lanes', the row mirror (i <- 15 - i)
+// each row's.  The operands are non-negative and every source lane is inside the row.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xf, 0xf, false));
+}
 template <int N>
 __device__ __forceinline__ float group_max(float v) {
-#pragma unroll
-  for (int m = 1; m < N; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+  static_assert(N == 8 || N == 16, "row groups of 8 or 16 lanes");
+  v = fmaxf(v, dpp_move<0xB1>(v));               // quad_perm [1, 0, 3, 2]
+  v = fmaxf(v, dpp_move<0x4E>(v));               // quad_perm [2, 3, 0, 1]
+  v = fmaxf(v, dpp_move<0x141>(v));              // row_half_mirror
+  if constexpr (N == 16) v = fmaxf(v, dpp_move<0x140>(v));   // row_mirror
   return v;
 }
 

@@ -96,7 +96,6 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
       }
     }
   }
-  auto at = [&](int i) { return in_lds ? cand[i] : bits[i]; };
 
   uint32_t prefix = 0, mask = 0;
   int remaining = kk;
@@ -107,9 +106,29 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
     const int shift = pass == 0 ? 21 : pass == 1 ? 10 : 0;
     const int nbins = pass == 2 ? 1024 : 2048;
     int* hs = hist[pass & 1];
-    for (int i = tid; i < n_cand; i += kThreads) {
-      const uint32_t u = at(i);
-      if ((u & mask) == prefix) atomicAdd(&hs[(u >> shift) & (nbins - 1)], 1);
+    // A thread's candidates tid, tid + kThreads, ... are read in batches of kBatch before their
+    // atomics, so a batch costs one read round trip; LDS and global memory get loops of their
+    // own (one loop over a pointer to either would compile to generic loads, each waited for).
+    constexpr int kBatch = 4;
+    auto count = [&](const uint32_t (&u)[kBatch], int i0) {
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+        if (i0 + j * kThreads < n_cand && (u[j] & mask) == prefix) atomicAdd(&hs[(u[j] >> shift) & (nbins - 1)], 1);
+    };
+    if (in_lds) {
+      for (int i0 = tid; i0 < n_cand; i0 += kBatch * kThreads) {
+        uint32_t u[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) u[j] = i0 + j * kThreads < n_cand ? cand[i0 + j * kThreads] : 0u;
+        count(u, i0);
+      }
+    } else {
+      for (int i0 = tid; i0 < n_cand; i0 += kBatch * kThreads) {
+        uint32_t u[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) u[j] = i0 + j * kThreads < n_cand ? bits[i0 + j * kThreads] : 0u;
+        count(u, i0);
+      }
     }
     if (pass < 2) {   // the next pass's histogram; its last reader finished two barriers ago
       for (int b = tid; b < 2048; b += kThreads) hist[(pass + 1) & 1][b] = 0;
@@ -182,7 +201,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   const int c0 = min(tid * per, n_cand), c1 = min(c0 + per, n_cand);
   int gt = 0, eq = 0;
   for (int i = c0; i < c1; ++i) {
-    const uint32_t u = at(i);
+    const uint32_t u = bits[i];
     gt += u > T;
     eq += u == T;
   }
@@ -192,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   int pos = block_incl_scan(sel, tot[0]) - sel;             // tot[0] was last read in pass 2
   int e = eq_before;
   for (int i = c0; i < c1; ++i) {
-    const uint32_t u = at(i);
+    const uint32_t u = bits[i];
     if (u > T || (u == T && e++ < ties)) out[pos++] = i;
   }
 }

@@ -12,10 +12,13 @@
 // One workgroup per (prompt, KV head).  Scores are non-negative fp32, so their bit patterns
 // order like unsigned integers: three radix passes (11, 11 and 10 bits) over the candidates
 // find the threshold value T (the (k-a)-th largest) and how many copies of T are still
-// needed.  The candidates are read from memory once, into LDS, when they fit; the passes
-// then run on LDS.  A final pass over contiguous per-thread chunks keeps every score above T
-// plus the first `ties` copies of T (lowest index first), placing them with two block scans,
-// and writes the window after them.  No sort, no device-wide traffic.
+// needed.  Scores crowd into a few leading bins (most of a head's scores share their
+// exponent), so every bin is kept in four copies on adjacent banks, lane l adding to copy
+// l % 4: a quarter of the same-address atomics per bin, summed back when the bins are read.
+// The candidates are read from memory once, into LDS, when they fit; the passes then run on
+// LDS.  A final pass over contiguous per-thread chunks keeps every score above T plus the
+// first `ties` copies of T (lowest index first), placing them with two block scans, and
+// writes the window after them.  No sort, no device-wide traffic.
 #include "kvs_common.h"
 
 namespace kvs {
@@ -24,6 +27,7 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kLdsCap = 16384;   // candidates held in LDS (64 KB); longer prompts read L2 each pass
+constexpr int kCopies = 4;       // copies of every histogram bin: lane l counts into copy l % 4
 
 // Inclusive scan across the 64 lanes with DPP moves (no LDS): prefix sums within rows of 16
 // lanes by shifts of 1, 2, 4 and 8, then row 0's total into rows 1 and 3 (row_bcast:15) and
@@ -56,7 +60,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
                                                         const int32_t* __restrict__ keep_offsets,
                                                         int32_t* __restrict__ keep_idx) {
   extern __shared__ __attribute__((aligned(16))) uint32_t cand[];   // up to kLdsCap candidate bit patterns (+4 spare)
-  __shared__ int hist[2][2048];    // alternate passes: one is cleared while the other is read
+  // alternate passes: one histogram is cleared while the other is read
+  __shared__ __attribute__((aligned(16))) int hist[2][2048 * kCopies];
   __shared__ int tot[2][kWaves];
   __shared__ int sel_bin, sel_rem;
 
@@ -99,7 +104,15 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
 
   uint32_t prefix = 0, mask = 0;
   int remaining = kk;
-  for (int b = tid; b < 2048; b += kThreads) hist[0][b] = 0;
+  const int copy = tid % kCopies;
+  auto clear = [&](int* h) {
+    for (int b = tid; b < 2048; b += kThreads) *reinterpret_cast<u32x4*>(&h[b * kCopies]) = u32x4{0u, 0u, 0u, 0u};
+  };
+  auto bin_count = [&](const int* h, int b) {   // a bin's four copies, one 16-byte read
+    const u32x4 c = *reinterpret_cast<const u32x4*>(&h[b * kCopies]);
+    return (int)(c[0] + c[1] + c[2] + c[3]);
+  };
+  clear(hist[0]);
   __syncthreads();   // also publishes the candidates in LDS
 #pragma unroll
   for (int pass = 0; pass < 3; ++pass) {
@@ -113,7 +126,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
     auto count = [&](const uint32_t (&u)[kBatch], int i0) {
 #pragma unroll
       for (int j = 0; j < kBatch; ++j)
-        if (i0 + j * kThreads < n_cand && (u[j] & mask) == prefix) atomicAdd(&hs[(u[j] >> shift) & (nbins - 1)], 1);
+        if (i0 + j * kThreads < n_cand && (u[j] & mask) == prefix)
+          atomicAdd(&hs[((u[j] >> shift) & (nbins - 1)) * kCopies + copy], 1);
     };
     if (in_lds) {
       for (int i0 = tid; i0 < n_cand; i0 += kBatch * kThreads) {
@@ -131,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
       }
     }
     if (pass < 2) {   // the next pass's histogram; its last reader finished two barriers ago
-      for (int b = tid; b < 2048; b += kThreads) hist[(pass + 1) & 1][b] = 0;
+      clear(hist[(pass + 1) & 1]);
     }
     __syncthreads();
     // Thread t owns bins hi = nbins-1-t*per down to hi-per+1; a scan in thread order counts the
@@ -140,12 +154,12 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
     const int per = nbins / kThreads;
     const int hi = nbins - 1 - tid * per;
     int local = 0;
-    for (int j = 0; j < per; ++j) local += hs[hi - j];
+    for (int j = 0; j < per; ++j) local += bin_count(hs, hi - j);
     const int incl = block_incl_scan(local, tot[pass & 1]);
     if (incl >= remaining && incl - local < remaining) {
       int cum = incl - local;
       for (int j = 0; j < per; ++j) {
-        const int c = hs[hi - j];
+        const int c = bin_count(hs, hi - j);
         if (cum + c >= remaining) {
           sel_bin = hi - j;
           sel_rem = remaining - cum;

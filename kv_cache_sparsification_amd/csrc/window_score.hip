@@ -12,25 +12,28 @@
 //   * causality and the window bound mean only window rows are visited (about n * alpha
 //     pairs instead of n * n).
 //
-// MI355X form.  A workgroup (4 wavefronts) owns 128 consecutive keys of one KV head (mapped to
-// the XCD that ran that head's prefill, whose L2 holds the keys); each
-// wavefront owns 32 keys, which are the N dimension of a bf16 32x32x16 MFMA, while the
-// G * a window rows of the group's query heads are the M dimension, staged through LDS in
-// chunks of 128 rows (one chunk for 4 query heads x a 32-token window) together with
-// LSE * log2(e) and each row's causal limit.  Every lane
-// ends up holding 16 (row, key) products for one key, so the window sum is 16 adds in
-// registers per M tile plus a single cross-lane add at the end: the pages' "row sum in
-// registers".  The key fragment is read from HBM once and kept in registers; nothing but
-// the window rows is ever touched.
+// MI355X form.  A workgroup (8 wavefronts) owns 128 consecutive keys of one KV head (mapped to
+// the XCD that ran that head's prefill, whose L2 holds the keys).  Wavefronts w and w + 4 own
+// the same 32 keys, which are the N dimension of a bf16 32x32x16 MFMA; the G * a window rows
+// of the group's query heads are the M dimension, staged through LDS in chunks of 128 rows
+// (one chunk for 4 query heads x a 32-token window) together with LSE * log2(e) and each
+// row's causal limit, and wavefront w takes M tiles 2(w/4) and 2(w/4) + 1 of every chunk.
+// Two wavefronts per SIMD: one's exponentials run beside the other's products.  Every lane
+// ends up holding 16 (row, key) products for one key per M tile, so the window sum is a
+// register sum plus one cross-lane add and one add of the two wavefronts' halves through
+// LDS: the pages' "row sum in registers".  The key fragment is read once per wavefront and
+// kept in registers; the window rows, their LSE and their limits are fetched in one round
+// trip per chunk; nothing but the window rows is ever touched.
 #include "kvs_common.h"
 
 namespace kvs {
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
+constexpr int kKeyWaves = 4;    // wavefronts across the keys; the other factor 2 splits the rows
 constexpr int kKeysPerWave = 32;
-constexpr int kKeysPerWG = kWaves * kKeysPerWave;
-constexpr int kRowChunk = 128;  // window rows staged in LDS at a time (4 M tiles)
+constexpr int kKeysPerWG = kKeyWaves * kKeysPerWave;
+constexpr int kRowChunk = 128;  // window rows staged in LDS at a time (4 M tiles, 2 per wavefront)
 constexpr int kXcds = 8;
 
 template <int D>
@@ -42,6 +45,7 @@ __global__ __launch_bounds__(kWaves * kWave) void window_score_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t qs[kRowChunk * kStride];
   __shared__ float lse2[kRowChunk];
   __shared__ int jlim[kRowChunk];
+  __shared__ float half_sums[kKeysPerWG];
 
   // Q rows and LSE of prompt s: [base, base + m); its keys and scores: [kbase, kbase + n).  The
   // Q rows are the prompt's last m positions (a chunk that ends the prompt, or all of it).
@@ -59,14 +63,15 @@ __global__ __launch_bounds__(kWaves * kWave) void window_score_kernel(
   const int kbase = cu_seqlens_k ? cu_seqlens_k[s] : base;
   const int n = cu_seqlens_k ? cu_seqlens_k[s + 1] - kbase : m;
   const int kb_wg = kt * kKeysPerWG;
-  if (kb_wg >= n) return;
+  if (kb_wg >= n) return;   // workgroup-uniform, before any barrier
   const int G = hq / hkv;
   const int a = alpha < n ? alpha : n;
   const int rows = G * a;                               // window rows of this KV head's group
 
   const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
   const int half = lane / 32, col = lane % 32;
-  const int key = kb_wg + w * kKeysPerWave + col;       // this lane's key (N index)
+  const int kw = w % kKeyWaves, rh = w / kKeyWaves;     // key slice and row half of this wavefront
+  const int key = kb_wg + kw * kKeysPerWave + col;      // this lane's key (N index)
 
   // B operand: K^T[d][key] for every 16-wide d step, kept in registers.
   bf16x8 kf[D / 16];
@@ -80,8 +85,8 @@ __global__ __launch_bounds__(kWaves * kWave) void window_score_kernel(
   float acc_sum = 0.f;
   for (int r0 = 0; r0 < rows; r0 += kRowChunk) {
     // Stage kRowChunk window rows: row r = (local head r / a, window position r % a).  All of
-    // a thread's loads are issued before any LDS store, so the staging costs one memory round
-    // trip, not one per load.
+    // a thread's loads (its Q pieces, and the LSE of row tid) are issued before any LDS
+    // store, so the staging costs one memory round trip, not one per load.
     constexpr int kStage = kRowChunk * (D / 8) / (kWaves * kWave);
     u32x4 staged[kStage];
 #pragma unroll
@@ -95,25 +100,29 @@ __global__ __launch_bounds__(kWaves * kWave) void window_score_kernel(
         staged[i] = *reinterpret_cast<const u32x4*>(q + ((size_t)(base + j) * hq + h) * D + cc * 8);
       }
     }
+    float row_lse = 0.f;
+    int row_lim = -1;                                   // padding row: masks every key
+    if (tid < kRowChunk) {
+      const int rr = r0 + tid;
+      if (rr < rows && m - a + rr % a >= 0) {
+        const int h = g * G + rr / a, j = m - a + rr % a;
+        row_lse = lse[(size_t)h * total_tokens + base + j];
+        row_lim = n - a + rr % a;                       // the row's prompt position: keys up to it count
+      }
+    }
 #pragma unroll
     for (int i = 0; i < kStage; ++i) {
       const int e = tid + i * kWaves * kWave;
       *reinterpret_cast<u32x4*>(&qs[(e / (D / 8)) * kStride + (e % (D / 8)) * 8]) = staged[i];
     }
     if (tid < kRowChunk) {
-      const int rr = r0 + tid;
-      if (rr < rows && m - a + rr % a >= 0) {
-        const int h = g * G + rr / a, j = m - a + rr % a;
-        lse2[tid] = lse[(size_t)h * total_tokens + base + j] * kLog2e;
-        jlim[tid] = n - a + rr % a;                     // the row's prompt position: keys up to it count
-      } else {
-        lse2[tid] = 0.f;
-        jlim[tid] = -1;                                 // padding row: masks every key
-      }
+      lse2[tid] = row_lse * kLog2e;
+      jlim[tid] = row_lim;
     }
     __syncthreads();
 #pragma unroll
-    for (int mt = 0; mt < kRowChunk / 32; ++mt) {
+    for (int mi = 0; mi < 2; ++mi) {
+      const int mt = 2 * rh + mi;
       f32x16 acc = {};
 #pragma unroll
       for (int st = 0; st < D / 16; ++st) {
@@ -128,10 +137,13 @@ __global__ __launch_bounds__(kWaves * kWave) void window_score_kernel(
         acc_sum += key <= jlim[r] ? p : 0.f;
       }
     }
-    __syncthreads();
+    __syncthreads();   // the next chunk's staging overwrites qs, lse2 and jlim
   }
   acc_sum += wave_xor(acc_sum, 32);
-  if (half == 0 && key < n) S[(size_t)g * total_k + kbase + key] = acc_sum;
+  if (rh == 1 && half == 0) half_sums[kw * kKeysPerWave + col] = acc_sum;
+  __syncthreads();
+  if (rh == 0 && half == 0 && key < n)
+    S[(size_t)g * total_k + kbase + key] = acc_sum + half_sums[kw * kKeysPerWave + col];
 }
 
 }  // namespace

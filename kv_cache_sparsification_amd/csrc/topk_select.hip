@@ -10,15 +10,16 @@
 // equal scores going to the lower index; indices are emitted in ascending order.
 //
 // One workgroup per (prompt, KV head).  Scores are non-negative fp32, so their bit patterns
-// order like unsigned integers: three radix passes (11, 11 and 10 bits) over the candidates
-// find the threshold value T (the (k-a)-th largest) and how many copies of T are still
-// needed.  Scores crowd into a few leading bins (most of a head's scores share their
-// exponent), so every bin is kept in four copies on adjacent banks, lane l adding to copy
-// l % 4: a quarter of the same-address atomics per bin, summed back when the bins are read.
-// The candidates are read from memory once, into LDS, when they fit; the passes then run on
-// LDS.  A final pass over contiguous per-thread chunks keeps every score above T plus the
-// first `ties` copies of T (lowest index first), placing them with two block scans, and
-// writes the window after them.  No sort, no device-wide traffic.
+// order like unsigned integers: up to three radix passes (11, 11 and 10 bits) over the
+// candidates find the threshold value T (the (k-a)-th largest) and how many copies of T are
+// still needed; the search ends early once the threshold bin is taken whole.  Scores crowd
+// into a few leading bins (most of a head's scores share their exponent), so every bin is kept
+// in four copies on adjacent banks, lane l adding to copy l % 4: a quarter of the
+// same-address atomics per bin, summed back when the bins are read.  The candidates are read
+// from memory once, into LDS, when they fit; the passes then run on LDS.  A final pass over
+// contiguous per-thread chunks keeps every score above T plus the first `ties` copies of T
+// (lowest index first), placing them with two block scans, and writes the window after them.
+// No sort, no device-wide traffic.
 #include "kvs_common.h"
 
 namespace kvs {
@@ -63,7 +64,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   // alternate passes: one histogram is cleared while the other is read
   __shared__ __attribute__((aligned(16))) int hist[2][2048 * kCopies];
   __shared__ int tot[2][kWaves];
-  __shared__ int sel_bin, sel_rem;
+  __shared__ int sel_bin, sel_rem, sel_all;
 
   const int g = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
   const int base = cu_seqlens[s];
@@ -163,6 +164,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
         if (cum + c >= remaining) {
           sel_bin = hi - j;
           sel_rem = remaining - cum;
+          sel_all = c == remaining - cum;   // the whole bin is taken: a later pass has nothing to split
           break;
         }
         cum += c;
@@ -173,9 +175,14 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
     mask |= (uint32_t)(nbins - 1) << shift;
     remaining = sel_rem;
     // sel_* are rewritten one pass later, after that pass's two barriers
+    if (sel_all) break;   // workgroup-uniform
   }
+  // The candidates are compared on the bits the passes resolved (`mask`): when a pass finds
+  // that every candidate of its threshold bin is taken (with scores spread over 22 bits, the
+  // second pass's bin usually holds a single candidate), the remaining passes are skipped and
+  // the whole bin counts as T.  The kept set is the same as with all three passes.
   const uint32_t T = prefix;
-  const int ties = remaining;   // copies of T to take, lowest index first
+  const int ties = remaining;   // candidates equal to T (under mask) to take, lowest index first
 
   // Contiguous chunk per thread, in index order.  With the candidates in LDS, a chunk is a
   // multiple of four (16-byte aligned) and read once into registers with 16-byte reads: one
@@ -192,20 +199,20 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const bool in = i + j < c1;
-        gt += in && x[j] > T;
-        eq += in && x[j] == T;
+        gt += in && (x[j] & mask) > T;
+        eq += in && (x[j] & mask) == T;
       }
     }
-    const int eq_before = block_incl_scan(eq, tot[1]) - eq;   // tot[1] was last read in pass 1
+    const int eq_before = block_incl_scan(eq, tot[1]) - eq;   // tot's last reads preceded the selection barrier
     const int take_eq = min(max(ties - eq_before, 0), eq);
     const int sel = gt + take_eq;
-    int pos = block_incl_scan(sel, tot[0]) - sel;             // tot[0] was last read in pass 2
+    int pos = block_incl_scan(sel, tot[0]) - sel;
     int e = eq_before;
     for (int i = c0; i < c1; i += 4) {
       const u32x4 x = group(i);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t u = x[j];
+        const uint32_t u = x[j] & mask;
         if (i + j < c1 && (u > T || (u == T && e++ < ties))) out[pos++] = i + j;
       }
     }
@@ -215,17 +222,17 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   const int c0 = min(tid * per, n_cand), c1 = min(c0 + per, n_cand);
   int gt = 0, eq = 0;
   for (int i = c0; i < c1; ++i) {
-    const uint32_t u = bits[i];
+    const uint32_t u = bits[i] & mask;
     gt += u > T;
     eq += u == T;
   }
-  const int eq_before = block_incl_scan(eq, tot[1]) - eq;   // tot[1] was last read in pass 1
+  const int eq_before = block_incl_scan(eq, tot[1]) - eq;   // tot's last reads preceded the selection barrier
   const int take_eq = min(max(ties - eq_before, 0), eq);
   const int sel = gt + take_eq;
-  int pos = block_incl_scan(sel, tot[0]) - sel;             // tot[0] was last read in pass 2
+  int pos = block_incl_scan(sel, tot[0]) - sel;
   int e = eq_before;
   for (int i = c0; i < c1; ++i) {
-    const uint32_t u = bits[i];
+    const uint32_t u = bits[i] & mask;
     if (u > T || (u == T && e++ < ties)) out[pos++] = i;
   }
 }

@@ -208,6 +208,32 @@ def test_topk_exact_with_ties_and_budgets():
                 np.testing.assert_array_equal(seg[g], ref, err_msg=f"seq {s} head {g} alpha {alpha} k {kb}")
 
 
+def test_topk_threshold_bin_taken_whole():
+    """The kept candidates are exactly the members of one radix bin (the top 11 bits, or the top
+    22) above everything else: the search stops at that pass and must keep the same set."""
+    r = np.random.default_rng(31)
+    for n, alpha, kb in ((300, 8, 40), (4000, 32, 400), (20000, 16, 700)):
+        kk = kb - alpha
+        S = np.zeros((3, n), np.float32)
+        pick = [r.choice(n - alpha, size=kk, replace=False) for _ in range(3)]
+        S[:] = (r.random((3, n)) * 0.5).astype(np.float32)               # below the chosen ones
+        S[0, pick[0]] = (1.0 + r.random(kk) * 0.24).astype(np.float32)     # one 11-bit bin: stops after one pass
+        # head 1: the kept ones share their top 22 bits (low 10 bits differ); unkept scores of 1.5
+        # share only their top 11, so the search stops after the second pass
+        low = r.choice(1024, size=kk, replace=kk > 1024).astype(np.uint32)
+        S[1, pick[1]] = (np.uint32(0x3FC00800) | low).view(np.float32)
+        rest = np.setdiff1d(np.arange(n - alpha), pick[1])
+        S[1, r.choice(rest, size=min(50, rest.size), replace=False)] = 1.5
+        S[2, pick[2]] = 1.0                                                # one value, every copy kept
+        _say(f"topk whole threshold bin n={n} alpha={alpha} k={kb}")
+        keep = kvs.kvs_topk_select(torch.from_numpy(S).cuda(), i32([0, n]), n, alpha, kb, i32([0, kb]),
+                                   total_keep=kb).cpu().numpy().reshape(3, kb)
+        for g in range(3):
+            ref = oracle.select_keep(S[g].astype(np.float64), n, alpha, kb)
+            np.testing.assert_array_equal(keep[g], ref, err_msg=f"head {g} n {n}")
+            np.testing.assert_array_equal(keep[g][:kk], np.sort(pick[g]))
+
+
 def test_compaction_offsets_keep_all_and_partial_blocks():
     _say("compaction with misaligned destination offsets, keep-all and partial blocks")
     r = np.random.default_rng(4)

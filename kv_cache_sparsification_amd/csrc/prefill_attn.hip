@@ -31,6 +31,8 @@
 //     any tile that reaches past a wavefront's first row, so the tiles that lie wholly past
 //     its rows are computed and masked to P = 0.  O is rescaled only when a row maximum grows
 //     by more than 2^8 (wave-uniform branch).
+//   * Query tiles are aligned to the end of each prompt, so a prompt's partial tile is its
+//     first (the one with the fewest key tiles) and its longest rows are all real.
 //   * Workgroups are remapped so that each XCD (8 per chip, each with its own L2) works on
 //     one KV head at a time, heaviest (last) query tiles first.
 #include "kvs_common.h"
@@ -85,14 +87,15 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void prefill_kernel(
   auto kbuf = [&](int b) { return b == 0 ? ks0 : b == 1 ? ks1 : ks2; };   // b: a constant at every call
   auto vbuf = [&](int b) { return b == 0 ? vs0 : b == 1 ? vs1 : vs2; };
 
-  // ---- XCD-aware work mapping: item order (g, s, query tile descending, head in group).
+  // ---- XCD-aware work mapping: item order (g, s, query tile counted from the prompt's end,
+  // head in group).
   const int per_xcd = gridDim.x / kXcds;
   const int item = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
   if (item >= total_items) return;
   const int G = hq / hkv;
   int rest = item;
   const int hl = rest % G; rest /= G;
-  const int qt = nqt - 1 - rest % nqt; rest /= nqt;
+  const int te = rest % nqt; rest /= nqt;   // te = 0: the prompt's last kBQ rows
   const int s = rest % num_seqs;
   const int g = rest / num_seqs;
   const int h = g * G + hl;
@@ -103,8 +106,8 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void prefill_kernel(
   const int kbase_tok = cu_seqlens_k ? cu_seqlens_k[s] : base;
   const int n = cu_seqlens_k ? cu_seqlens_k[s + 1] - kbase_tok : m;
   const int qoff = n - m;
-  const int r0 = qt * kBQ;
-  if (r0 >= m) return;
+  const int r0 = m - (te + 1) * kBQ;   // negative for a prompt's first, partial tile
+  if (r0 + kBQ <= 0) return;
 
   const int tid = threadIdx.x, lane = tid % kWave;
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform: branches on it stay scalar
@@ -120,7 +123,7 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void prefill_kernel(
 #pragma unroll
   for (int st = 0; st < ST1; ++st) {
     u32x4 x = {0u, 0u, 0u, 0u};
-    if (row < m) x = *reinterpret_cast<const u32x4*>(q + ((size_t)(base + row) * hq + h) * D + st * 16 + half * 8);
+    if (row >= 0) x = *reinterpret_cast<const u32x4*>(q + ((size_t)(base + row) * hq + h) * D + st * 16 + half * 8);
     qf[st] = __builtin_bit_cast(bf16x8, x);
   }
 
@@ -302,7 +305,7 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void prefill_kernel(
   auto vector_phase = [&](int t) {                 // X(t)
     const int kb = t * kBK;
     if (kb + kBK - 1 > qoff + R) {   // wave-uniform: mask keys past the row
-      const int lim = qoff + row - kb - 8 * half;
+      const int lim = qoff + max(row, 0) - kb - 8 * half;   // rows before the prompt (never stored) act as row 0
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -364,7 +367,7 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void prefill_kernel(
 
   // ---- epilogue: O = acc / l, LSE = ln 2 * (m_ref + log2 l)
   const float l = half_sum(l_lane);   // sum of exp2(x - m_ref)
-  if (row < m) {
+  if (row >= 0) {   // rows before the prompt belong to no query (every row is < m)
     const float inv = 1.f / l;
     uint16_t* orow = o + ((size_t)(base + row) * hq + h) * D;
 #pragma unroll

@@ -559,39 +559,136 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict
   }
 }
 
+// The merge of two (query head, channel) outputs at once, all loads of a chunk of 16 splits for
+// both issued before either is folded (one memory round trip per chunk for the pair).
+template <int D>
+__device__ __forceinline__ void merge_partials_pair(const float* __restrict__ part0, const float* __restrict__ part1,
+                                                    bool has1, int splits, int used, int dd0, int dd1, float (&M)[2],
+                                                    float (&l)[2], float (&acc)[2]) {
+  constexpr int C = 16;
+  for (int k = 0; k < 2; ++k) {
+    M[k] = -INFINITY;
+    l[k] = 0.f;
+    acc[k] = 0.f;
+  }
+  for (int sp0 = 0; sp0 < splits; sp0 += C) {
+    float mv[2][C], lv[2][C], ov[2][C];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const float* part = k == 0 ? part0 : part1;
+      const int dd = k == 0 ? dd0 : dd1;
+#pragma unroll
+      for (int i = 0; i < C; ++i) {
+        const float* ps = part + (size_t)(sp0 + i < splits ? sp0 + i : 0) * (D + 2);
+        const bool ld = k == 0 || has1;
+        mv[k][i] = ld ? ps[0] : -INFINITY;
+        lv[k][i] = ld ? ps[1] : 0.f;
+        ov[k][i] = ld ? ps[2 + dd] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+#pragma unroll
+      for (int i = 0; i < C; ++i) {
+        const bool in = sp0 + i < used;
+        mv[k][i] = in ? mv[k][i] : -INFINITY;
+        lv[k][i] = in ? lv[k][i] : 0.f;
+        ov[k][i] = in ? ov[k][i] : 0.f;
+      }
+      float cm = M[k];
+#pragma unroll
+      for (int i = 0; i < C; ++i) cm = fmaxf(cm, mv[k][i]);
+      const float corr = __builtin_amdgcn_exp2f(M[k] - cm);   // first chunk: exp2(-inf) = 0
+      l[k] *= corr;
+      acc[k] *= corr;
+#pragma unroll
+      for (int i = 0; i < C; ++i) {
+        const float wgt = __builtin_amdgcn_exp2f(mv[k][i] - cm);
+        l[k] += lv[k][i] * wgt;
+        acc[k] += ov[k][i] * wgt;
+      }
+      M[k] = cm;
+    }
+  }
+}
+
 // Scored decode, second kernel: one workgroup per (KV head, sequence).  Merges the partials
 // of the G query heads (output, LSE), then adds every live slot's probability summed over
 // those heads, exp2(logit - LSE2), to its score: the decode row's contribution to S.
-template <int D>
 // With next_dst set, the same workgroup then chooses the slot of the next step's token from the
-// scores it has just updated (select_slot_block, with the live count L as n_filled), which
-// saves the next step a launch.
+// scores it has just updated (with the live count L as n_filled), which saves the next step a
+// launch.  When a thread's slots (t = tid + 256 j, j < 2) and their G <= 8 logits fit in
+// registers, they are fetched at the start, in the same round trip as the partials and the
+// context length, and the choice is made from the registers; otherwise the slots are read after
+// the merge.  Either way every slot is updated and chosen by the same arithmetic.
+template <int D>
 __global__ __launch_bounds__(kSelectThreads) void decode_merge_score_kernel(
     const float* __restrict__ ws, const float* __restrict__ logits, int logit_stride,
     const int32_t* __restrict__ ctx_lens, int hq, int hkv, int max_blocks, int splits, int bps,
     uint16_t* __restrict__ o, float* __restrict__ lse_out, float* __restrict__ slot_scores, int slot_stride,
     int32_t* __restrict__ slot_pos, int cap, int alpha, const int32_t* __restrict__ next_pos,
     int32_t* __restrict__ next_dst) {
+  constexpr int kRS = 2, kRG = 8;   // register path: slots per thread, query heads per group
   __shared__ float lse2[16];
   const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int G = hq / hkv;
+  const float* lg = logits + ((size_t)b * hq + g * G) * logit_stride;
+  float* sc = slot_scores + ((size_t)b * hkv + g) * slot_stride;
+  int32_t* ps = next_dst ? slot_pos + ((size_t)b * hkv + g) * slot_stride : nullptr;
+  // grid-uniform, from host-known bounds (logit_stride is the launch's max_ctx >= L)
+  const bool regs = G <= kRG && logit_stride <= kRS * kSelectThreads && (!next_dst || cap <= kRS * kSelectThreads);
+  float lgv[kRS][kRG], scv[kRS];
+  int psv[kRS];
+  if (regs) {   // in bounds of the slot and logit rows whatever L is; slots >= L are ignored
+#pragma unroll
+    for (int j = 0; j < kRS; ++j) {
+      const int t = tid + kSelectThreads * j;
+#pragma unroll
+      for (int c = 0; c < kRG; ++c) lgv[j][c] = (c < G && t < logit_stride) ? lg[(size_t)c * logit_stride + t] : 0.f;
+      scv[j] = t < logit_stride ? sc[t] : 0.f;
+      psv[j] = (ps && t < cap) ? ps[t] : -1;
+    }
+  }
   const int L = ctx_lens[b];
   const int nblk = min((L + kBlock - 1) / kBlock, max_blocks);
   const int used = min((nblk + bps - 1) / bps, splits);
-  for (int e = tid; e < G * D; e += 256) {
-    const int c = e / D, dd = e % D;
-    const int h = g * G + c;
-    float M, l, acc;
-    merge_partials<D>(ws + ((size_t)b * hq + h) * splits * (D + 2), splits, used, dd, M, l, acc);
-    o[((size_t)b * hq + h) * D + dd] = (uint16_t)f32_to_bf16_bits(acc / l);
-    if (dd == 0) {
-      lse2[c] = M + log2f(l);
-      if (lse_out) lse_out[(size_t)b * hq + h] = (M + log2f(l)) * kLn2;
+  for (int e = tid; e < G * D; e += 2 * kSelectThreads) {
+    const int e1 = e + kSelectThreads;
+    const bool has1 = e1 < G * D;
+    const int c0 = e / D, dd0 = e % D, c1 = has1 ? e1 / D : c0, dd1 = has1 ? e1 % D : dd0;
+    const int h0 = g * G + c0, h1 = g * G + c1;
+    float M[2], l[2], acc[2];
+    merge_partials_pair<D>(ws + ((size_t)b * hq + h0) * splits * (D + 2), ws + ((size_t)b * hq + h1) * splits * (D + 2),
+                           has1, splits, used, dd0, dd1, M, l, acc);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      if (k == 1 && !has1) break;
+      const int h = k == 0 ? h0 : h1, dd = k == 0 ? dd0 : dd1, c = k == 0 ? c0 : c1;
+      o[((size_t)b * hq + h) * D + dd] = (uint16_t)f32_to_bf16_bits(acc[k] / l[k]);
+      if (dd == 0) {
+        lse2[c] = M[k] + log2f(l[k]);
+        if (lse_out) lse_out[(size_t)b * hq + h] = (M[k] + log2f(l[k])) * kLn2;
+      }
     }
   }
   __syncthreads();
-  const float* lg = logits + ((size_t)b * hq + g * G) * logit_stride;
-  float* sc = slot_scores + ((size_t)b * hkv + g) * slot_stride;
+  if (regs) {
+#pragma unroll
+    for (int j = 0; j < kRS; ++j) {
+      const int t = tid + kSelectThreads * j;
+      if (t < L) {
+        float sum = 0.f;
+#pragma unroll
+        for (int c = 0; c < kRG; ++c)
+          if (c < G) sum += __builtin_amdgcn_exp2f(lgv[j][c] - lse2[c]);
+        scv[j] += sum;
+        sc[t] = scv[j];
+      }
+    }
+    if (next_dst)   // grid-uniform; the slots below cap are below L when the cache is full
+      select_slot_regs<kRS>(psv, scv, sc, ps, L, cap, next_pos[b], alpha, next_dst + (size_t)b * hkv + g);
+    return;
+  }
   for (int t = tid; t < L; t += kSelectThreads) {
     float sum = 0.f;
     for (int c = 0; c < G; ++c) sum += __builtin_amdgcn_exp2f(lg[(size_t)c * logit_stride + t] - lse2[c]);
@@ -599,8 +696,7 @@ __global__ __launch_bounds__(kSelectThreads) void decode_merge_score_kernel(
   }
   if (next_dst) {   // grid-uniform
     __syncthreads();   // every updated score visible to the whole workgroup
-    select_slot_block(sc, slot_pos + ((size_t)b * hkv + g) * slot_stride, L, cap, next_pos[b], alpha,
-                      next_dst + (size_t)b * hkv + g);
+    select_slot_block(sc, ps, L, cap, next_pos[b], alpha, next_dst + (size_t)b * hkv + g);
   }
 }
 

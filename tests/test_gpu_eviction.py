@@ -121,6 +121,15 @@ def test_eviction_wide_groups(hq, hkv, d):
     assert c.n == c.cap
 
 
+def test_eviction_budget_beyond_register_slots():
+    """A budget of 600 slots: more than the merge-and-score kernel keeps in registers (512 per
+    workgroup), so the slots are read after the merge and the choice made from memory."""
+    w = dataclasses.replace(wl.WORKLOADS[1], hq=8, hkv=2, d=64, alpha=16, budgets=(600,), fixed_len=700,
+                            decode_steps=12)
+    c = _run(w, steps=12, check_every=4)
+    assert c.n == c.cap
+
+
 def test_eviction_batch_appends_then_evicts():
     """Three prompts (30, 48, 100 tokens), budget 48, alpha 8: the short one appends (taking a
     block when a slot opens one) until it is full, the others evict from the first step."""
@@ -248,18 +257,18 @@ def test_eviction_llama8b_layer_fp8():
         np.testing.assert_array_equal(gv[:, g], c.v[g], err_msg=f"V head {g}")
 
 
+@pytest.mark.parametrize("lengths,cap,alpha,steps", [([30, 48, 100], 48, 8, 40), ([500, 640, 900], 640, 16, 12)])
 @pytest.mark.parametrize("fp8", [False, True])
-def test_select_in_the_scored_decode_matches_separate_launches(fp8):
+def test_select_in_the_scored_decode_matches_separate_launches(fp8, lengths, cap, alpha, steps):
     """kvs_paged_decode_scored_select (the next step's slot chosen by the merge-and-score kernel)
     gives, step for step, the slots, outputs, slot state and pools of kvs_decode_select_slot
     followed by kvs_paged_decode_scored (checked against the oracle above), bit for bit:
     three prompts (30, 48, 100 tokens), budget 48, alpha 8, 40 steps through the appends and
-    the evictions."""
+    the evictions; and a budget of 640, beyond the 512 slots the merge-and-score kernel keeps
+    in registers."""
     from workloads import Workload
-    w = Workload(cid=92, name="fused selection", hq=8, hkv=2, d=128, alpha=8, n_layers=1, budgets=[48],
-                 decode_steps=40, sink_positions=(0,), num_seqs=3)
-    lengths = [30, 48, 100]
-    cap, alpha, steps = 48, 8, 40
+    w = Workload(cid=92, name="fused selection", hq=8, hkv=2, d=128, alpha=alpha, n_layers=1, budgets=[cap],
+                 decode_steps=steps, sink_positions=(0,), num_seqs=3)
     B = len(lengths)
     _say(f"scored decode with the next selection fused, fp8={fp8}, {steps} steps")
     q, k, v, cu = wl.device_batch(w, 0, lengths, list(range(B)))

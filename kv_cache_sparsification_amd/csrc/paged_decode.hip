@@ -93,12 +93,24 @@ inline Plan choose_plan(int batch, int hq, int hkv, int d, int max_ctx, bool f8)
   if (bps < p.waves) bps = p.waves;
   const int total = units * nblk;
   if (total >= kManyBlocks) {
-    // Read volume far beyond one wave generation: four wavefronts of two blocks, one round
-    // each, many generations (20 x 8 heads x 1100-3900 tokens: 41.5 us per step, against
-    // 50.7 at 8 x 2 x 2 rounds); the 8-bit cache, half the bytes per block, keeps four blocks
-    // in flight for two rounds (43.8 us against 48.3).
-    p.nb = f8 ? 4 : 2;
-    bps = f8 ? 2 * p.waves * p.nb : p.waves * p.nb;
+    // Read volume far beyond one wave generation: pieces of 8 blocks over many generations of
+    // workgroups.  With d = 128 a piece is two wavefronts of one block for four rounds: the
+    // one-block kernel's 122 registers let four workgroups share a SIMD pair where the
+    // two-block kernel fits three (20 x 8 heads x 1100-3900 tokens, three full layers: 143.0
+    // us per step against 155.0 for four wavefronts of two blocks in one round, 165.8 for two
+    // rounds of 16-block pieces); the 8-bit cache, half the bytes per block, keeps four
+    // wavefronts of four blocks for two rounds (43.8 us against 48.3).
+    if (f8) {
+      p.nb = 4;
+      bps = 2 * p.waves * p.nb;
+    } else if (d == 128) {
+      p.waves = 2;
+      p.nb = 1;
+      bps = 4 * p.waves * p.nb;
+    } else {
+      p.nb = 2;
+      bps = p.waves * p.nb;
+    }
   } else if (total >= kBandwidthBlocks) {
     // Enough blocks for the read volume to set the time: eight wavefronts of two blocks in
     // flight, two rounds each (8 KV heads x 3000+ tokens, batch 4, per step: 4 waves x 4
@@ -741,7 +753,10 @@ static void launch_decode(const Plan& p, dim3 grid, size_t lds, hipStream_t st, 
       launch_one<D, 4, 2, F8>(p, grid, lds, st, q, kp, vp, num_blocks, tables, max_blocks, ctx, hq, hkv, c, nk, nv, o,
                               lse, ws, ex);
   } else {
-    if (p.waves == 4 && p.nb == 1)
+    if (p.waves == 2 && p.nb == 1)
+      launch_one<D, 2, 1, F8>(p, grid, lds, st, q, kp, vp, num_blocks, tables, max_blocks, ctx, hq, hkv, c, nk, nv, o,
+                              lse, ws, ex);
+    else if (p.waves == 4 && p.nb == 1)
       launch_one<D, 4, 1, F8>(p, grid, lds, st, q, kp, vp, num_blocks, tables, max_blocks, ctx, hq, hkv, c, nk, nv, o,
                               lse, ws, ex);
     else if (p.waves == 4 && p.nb == 2)

@@ -95,21 +95,17 @@ inline Plan choose_plan(int batch, int hq, int hkv, int d, int max_ctx, bool f8)
   if (total >= kManyBlocks) {
     // Read volume far beyond one wave generation: pieces of 8 blocks over many generations of
     // workgroups.  With d = 128 a piece is two wavefronts of one block for four rounds: the
-    // one-block kernel's 122 registers let four workgroups share a SIMD pair where the
-    // two-block kernel fits three (20 x 8 heads x 1100-3900 tokens, three full layers: 143.0
-    // us per step against 155.0 for four wavefronts of two blocks in one round, 165.8 for two
-    // rounds of 16-block pieces); the 8-bit cache, half the bytes per block, keeps four
-    // wavefronts of four blocks for two rounds (43.8 us against 48.3).
-    if (f8) {
-      p.nb = 4;
-      bps = 2 * p.waves * p.nb;
-    } else if (d == 128) {
+    // one-block kernel's registers (122, 160 for the 8-bit cache) let more workgroups share a
+    // SIMD pair than the wider kernels (20 x 8 heads x 1100-3900 tokens, three full layers per
+    // step: 143.0 us against 155.0 for four wavefronts of two blocks in one round; 8-bit cache
+    // 103 us against 138 for four wavefronts of four blocks in two rounds).
+    if (d == 128) {
       p.waves = 2;
       p.nb = 1;
       bps = 4 * p.waves * p.nb;
     } else {
-      p.nb = 2;
-      bps = p.waves * p.nb;
+      p.nb = f8 ? 4 : 2;
+      bps = f8 ? 2 * p.waves * p.nb : p.waves * p.nb;
     }
   } else if (total >= kBandwidthBlocks) {
     // Enough blocks for the read volume to set the time: eight wavefronts of two blocks in

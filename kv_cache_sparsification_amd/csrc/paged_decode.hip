@@ -505,19 +505,20 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
 
 // Merge of the split partials.  Each thread folds its output channel over the splits 16 at a
 // time, issuing all loads of a chunk (its channel plus the (max, sum) pair, shared with its
-// neighbours through L1) before using any: one memory round trip per 16 splits.  The loads
+// neighbours through L1) before using any: one memory round trip per 16 splits (kOne: the
+// caller knows there are at most 16, and the fold is a single straight pass).  The loads
 // cover every split the launch has (a bound known on the host), so they do not wait for the
 // context length; the splits past the sequence's last non-empty one (`used`) hold stale data
 // and are masked out afterwards.
 // Returns the running max M (log2 units), the sum l against it and the output numerator.
-template <int D>
+template <int D, bool kOne = false>
 __device__ __forceinline__ void merge_partials(const float* __restrict__ part, int splits, int used, int dd, float& M,
                                                float& l, float& acc) {
   constexpr int C = 16;
   M = -INFINITY;
   l = 0.f;
   acc = 0.f;
-  for (int sp0 = 0; sp0 < splits; sp0 += C) {
+  for (int sp0 = 0; kOne ? sp0 == 0 : sp0 < splits; sp0 += C) {
     float mv[C], lv[C], ov[C];
 #pragma unroll
     for (int i = 0; i < C; ++i) {
@@ -560,7 +561,11 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict
   const int used = min((nblk + bps - 1) / bps, splits);
   {
     float M, l, acc;
-    merge_partials<D>(ws + ((size_t)b * hq + h) * splits * (D + 2), splits, used, dd, M, l, acc);
+    const float* part = ws + ((size_t)b * hq + h) * splits * (D + 2);
+    if (splits <= 16)   // grid-uniform: one straight pass (7.40 against 7.50 us per batch-1 step)
+      merge_partials<D, true>(part, splits, used, dd, M, l, acc);
+    else
+      merge_partials<D>(part, splits, used, dd, M, l, acc);
     if (used <= 1) return;                    // written directly by the decode kernel
     o[((size_t)b * hq + h) * D + dd] = (uint16_t)f32_to_bf16_bits(acc / l);
     if (lse_out && dd == 0) lse_out[(size_t)b * hq + h] = (M + log2f(l)) * kLn2;

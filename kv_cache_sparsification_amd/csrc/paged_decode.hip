@@ -178,7 +178,7 @@ __device__ __forceinline__ int f8_kofs(int st, int grp) { return (st / 2) * 64 +
 // F8: the cache holds E4M3 codes with a fp32 scale per (slot, KV head) row; codes are widened
 // to bf16 (exact) for the same MFMAs, the K scale multiplies the slot's score and the V scale
 // its probability (before the bf16 rounding of P), and the appended token is quantized here.
-template <int D, int W, int kNB, bool F8, bool kOne = false>
+template <int D, int W, int kNB, bool F8, bool kOne = false, bool kScored = false>
 __global__ __launch_bounds__(W * kWave) void decode_kernel(
     const uint16_t* __restrict__ q, void* __restrict__ k_pool_v, void* __restrict__ v_pool_v, int num_blocks,
     const int32_t* __restrict__ tables, int max_blocks, const int32_t* __restrict__ ctx_lens, int hq, int hkv,
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
     qf[st] = __builtin_bit_cast(bf16x8, x);
   }
 
-  const int dst = ex.dst_slots ? ex.dst_slots[b * hkv + g] : L - 1;   // slot of the new token
+  const int dst = (kScored && ex.dst_slots) ? ex.dst_slots[b * hkv + g] : L - 1;   // slot of the new token
   const int last_blk = dst / kBlock, last_slot = dst % kBlock;
   const bool append = new_k != nullptr && new_v != nullptr && dst >= 0 && dst < L;   // else nothing is written
   const uint16_t* nk = new_k + ((size_t)b * hkv + g) * D;
@@ -425,7 +425,7 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
         const float si = F8 ? sc[i] * f8[j].sk[i] : sc[i];
         x[i] = t < L ? si * c_log2 : -INFINITY;
       }
-      if (ex.logits) {   // scored decode only (uniform branch)
+      if (kScored && ex.logits) {   // scored decode only (uniform branch)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int t = bi * kBlock + grp * 4 + i;
@@ -508,7 +508,7 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
       acc += s_o[((size_t)v * G + c) * D + dd] * wgt;
     }
     const int h = g * G + c;
-    if (used == 1 && !ex.force_partials) {
+    if (used == 1 && !(kScored && ex.force_partials)) {
       o[((size_t)b * hq + h) * D + dd] = (uint16_t)f32_to_bf16_bits(acc / l);
       if (lse_out && dd == 0) lse_out[(size_t)b * hq + h] = (m + log2f(l)) * kLn2;
     } else {
@@ -752,15 +752,19 @@ static void launch_one(const Plan& p, dim3 grid, size_t lds, hipStream_t st, con
                        int num_blocks, const int32_t* tables, int max_blocks, const int32_t* ctx, int hq, int hkv,
                        float c, const uint16_t* nk, const uint16_t* nv, uint16_t* o, float* lse, float* ws,
                        const DecodeExtra& ex) {
+  // the scored decode's extras (slot choice, logits, partials for one split) as a separate build
+  const bool scored = ex.dst_slots || ex.logits || ex.force_partials;
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(W * kWave), lds, st, q, kp, vp, num_blocks, tables, max_blocks, ctx, hq, hkv,
+                       c, nk, nv, o, lse, ws, p.splits, p.bps, ex);
+  };
   if constexpr (W == 4 && NB == 1) {   // the few-block plan: pieces of one round
     if (p.bps <= W * NB) {
-      hipLaunchKernelGGL((decode_kernel<D, W, NB, F8, true>), grid, dim3(W * kWave), lds, st, q, kp, vp, num_blocks,
-                         tables, max_blocks, ctx, hq, hkv, c, nk, nv, o, lse, ws, p.splits, p.bps, ex);
+      scored ? go(decode_kernel<D, W, NB, F8, true, true>) : go(decode_kernel<D, W, NB, F8, true, false>);
       return;
     }
   }
-  hipLaunchKernelGGL((decode_kernel<D, W, NB, F8>), grid, dim3(W * kWave), lds, st, q, kp, vp, num_blocks, tables,
-                     max_blocks, ctx, hq, hkv, c, nk, nv, o, lse, ws, p.splits, p.bps, ex);
+  scored ? go(decode_kernel<D, W, NB, F8, false, true>) : go(decode_kernel<D, W, NB, F8, false, false>);
 }
 
 template <int D, bool F8>

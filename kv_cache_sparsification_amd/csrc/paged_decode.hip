@@ -76,10 +76,13 @@ inline Plan choose_plan(int batch, int hq, int hkv, int d, int max_ctx, bool f8)
   }
   // Short contexts in a batch wide enough for 1024+ wavefronts: one 8-wavefront workgroup per
   // pair walks its blocks in a few rounds, and the merge launch is saved (20 sequences x 8 KV
-  // heads x 528 tokens: 10.8 us per step, against 15.2-22 us for any split plan).
+  // heads x 528 tokens: 10.8 us per step, against 15.2-22 us for any split plan).  With d = 128
+  // a wavefront has one block in flight per round: the 29 such layers of the 32-layer step at
+  // concurrency 20 take 14.8 us less than with two (8-bit cache: 5 us less); 4, 6, 12 and 16
+  // wavefronts of one block, or 8 of three, were slower still.
   if (nblk <= kNoSplitBlocks && units * 8 >= 4 * kCUs) {
     p.waves = 8;
-    p.nb = 2;
+    p.nb = d == 128 ? 1 : 2;
     p.bps = nblk;
     p.splits = 1;
     return p;
@@ -108,12 +111,14 @@ inline Plan choose_plan(int batch, int hq, int hkv, int d, int max_ctx, bool f8)
       bps = f8 ? 2 * p.waves * p.nb : p.waves * p.nb;
     }
   } else if (total >= kBandwidthBlocks) {
-    // Enough blocks for the read volume to set the time: eight wavefronts of two blocks in
-    // flight, two rounds each (8 KV heads x 3000+ tokens, batch 4, per step: 4 waves x 4
-    // blocks x 1 round 15.2 us, 8 x 4 x 1 14.4, 8 x 2 x 2 13.7, 8 x 2 x 3 15.1, 8 x 2 x 4 18.0).
+    // Enough blocks for the read volume to set the time: pieces of 32 blocks for eight
+    // wavefronts (8 KV heads x 3000+ tokens, batch 4, per step: 4 waves x 4 blocks x 1 round
+    // 15.2 us, 8 x 4 x 1 14.4, 8 x 2 x 2 13.7, 8 x 2 x 3 15.1, 8 x 2 x 4 18.0; with d = 128
+    // one block in flight for four rounds 13.0 against 13.3 for 8 x 2 x 2, 8-bit cache 12.0
+    // against 12.3, while pieces of 16 or 24 blocks were slower).
     p.waves = 8;
-    p.nb = 2;
-    if (bps < 2 * p.waves * p.nb) bps = 2 * p.waves * p.nb;
+    p.nb = d == 128 ? 1 : 2;
+    if (bps < 32) bps = 32;
   }
   if ((nblk + bps - 1) / bps > kMaxSplitsMerge) bps = (nblk + kMaxSplitsMerge - 1) / kMaxSplitsMerge;
   p.bps = bps;
@@ -784,7 +789,10 @@ static void launch_decode(const Plan& p, dim3 grid, size_t lds, hipStream_t st, 
       launch_one<D, 4, 2, F8>(p, grid, lds, st, q, kp, vp, num_blocks, tables, max_blocks, ctx, hq, hkv, c, nk, nv, o,
                               lse, ws, ex);
   } else {
-    if (p.waves == 2 && p.nb == 1)
+    if (p.waves == 8 && p.nb == 1)
+      launch_one<D, 8, 1, F8>(p, grid, lds, st, q, kp, vp, num_blocks, tables, max_blocks, ctx, hq, hkv, c, nk, nv, o,
+                              lse, ws, ex);
+    else if (p.waves == 2 && p.nb == 1)
       launch_one<D, 2, 1, F8>(p, grid, lds, st, q, kp, vp, num_blocks, tables, max_blocks, ctx, hq, hkv, c, nk, nv, o,
                               lse, ws, ex);
     else if (p.waves == 4 && p.nb == 1)

@@ -268,7 +268,12 @@ def test_compaction_offsets_keep_all_and_partial_blocks():
 @pytest.mark.parametrize("d,hq,hkv,lens", [(128, 32, 8, [5000, 1, 17, 900]), (64, 4, 2, [3, 2000]),
                                            (128, 8, 8, [16, 32, 48]), (64, 16, 2, [700, 5]),
                                            (64, 16, 1, [300, 2500]), (128, 16, 1, [1200, 7]),
-                                           (128, 32, 8, [100000, 3])])   # 6250 blocks: the split count is capped
+                                           (128, 32, 8, [100000, 3]),    # 6250 blocks: the split count is capped
+                                           # wide batches of short contexts (one workgroup per sequence
+                                           # and head, several rounds) and a mid-size split plan
+                                           (128, 32, 8, list(range(400, 700, 15))),
+                                           (128, 32, 8, list(range(250, 390, 7))),
+                                           (128, 32, 8, [3000 + 33 * i for i in range(4)])])
 def test_decode_batch_splits_and_merge(d, hq, hkv, lens):
     """Full-cache decode over several contexts, with and without append; long contexts split and merge."""
     _say(f"decode batch d={d} hq={hq} hkv={hkv} lens={lens}")

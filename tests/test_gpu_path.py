@@ -432,6 +432,33 @@ def test_prefill_without_statistics_writes_only_o():
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
 
 
+@pytest.mark.parametrize("n,d", [(1000, 128), (20, 64), (777, 64)])
+def test_single_prompt_matches_batched_form(n, d):
+    """A prompt alone and the same prompt followed by an empty one (a different grid and work
+    mapping): prefill, window score and top-k give the same bits."""
+    hq, hkv, alpha, kb = 8, 2, 32, 200
+    _say(f"single prompt against the batched form: n={n} d={d}")
+    r = np.random.default_rng(n + d)
+    qb = wl.f32_to_bf16_bits(r.standard_normal((n, hq, d), dtype=np.float32))
+    kk = wl.f32_to_bf16_bits(r.standard_normal((n, hkv, d), dtype=np.float32))
+    vb = wl.f32_to_bf16_bits(r.standard_normal((n, hkv, d), dtype=np.float32))
+    q, k, v = to_dev_bf16(qb), to_dev_bf16(kk), to_dev_bf16(vb)
+    ke = min(kb, n)
+    outs = []
+    for cu, koff in (([0, n], [0, ke]), ([0, n, n], [0, ke, ke])):
+        o, lse = kvs.kvs_prefill_attn_lse(q, k, v, i32(cu), n)
+        S = kvs.kvs_window_score(q, k, lse, i32(cu), n, alpha)
+        keep = kvs.kvs_topk_select(S, i32(cu), n, alpha, kb, i32(koff), total_keep=ke)
+        torch.cuda.synchronize()
+        outs.append((bf16_bits(o), lse.cpu().numpy().view(np.uint32), S.cpu().numpy().view(np.uint32),
+                     keep.cpu().numpy()))
+    for what, a, b in zip(("O", "LSE", "S", "keep"), outs[0], outs[1]):
+        np.testing.assert_array_equal(a, b, err_msg=f"{what}: one prompt against the batched form")
+    O_ref, lse_ref, _, _ = oracle.causal_attention(_f64(qb), _f64(kk), _f64(vb))
+    assert_rows_close(bf16_to_f64(torch.from_numpy(outs[0][0].view(np.int16)).view(torch.bfloat16)), O_ref)
+    assert_lse_close(outs[0][1].view(np.float32), lse_ref)
+
+
 def test_empty_prompts_in_a_ragged_batch():
     """Prompts of length 0 between real ones (repeated cu_seqlens entries): they produce no
     rows, scores, kept indices or blocks, and the prompts around them match the oracle."""

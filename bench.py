@@ -12,8 +12,8 @@ One step = the whole hot path once: prefill attention with LSE, window score, to
 compaction into blocks, then 500 decode steps with append.  Every kernel is launched on
 torch's current stream and bracketed by HIP events, so per-kernel durations come from the
 GPU clock of the timed steps.  The printed JSON line carries:
-  value        prefill+compress throughput: prompt tokens / GPU time of the four
-               prefill-side kernels (attention, score, top-k, compaction)
+  value        prefill+compress throughput: prompt tokens / GPU time of the prefill-side
+               kernels (attention, score, top-k fused with compaction)
   decode       paged-decode throughput: generated tokens / GPU time of the 500 decode calls
   ms_per_step  wall time of one full step (host clock, synchronised on both sides)
   roofline     the kernel with the largest share of the step's GPU time, against MI355X's
@@ -61,8 +61,16 @@ def parse():
 
 
 def kernel_source_hash(name: str) -> str:
-    path = os.path.join(ROOT, "kv_cache_sparsification_amd", "csrc", name)
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    """Hash of a kernel source and of the local headers it includes (kvs_common.h aside), so a
+    counter record goes stale when any code the kernel is built from changes."""
+    import re
+    csrc = os.path.join(ROOT, "kv_cache_sparsification_amd", "csrc")
+    text = open(os.path.join(csrc, name), "rb").read()
+    h = hashlib.sha256(text)
+    for inc in re.findall(rb'#include "([a-z_]+\.h)"', text):
+        if inc != b"kvs_common.h" and os.path.exists(os.path.join(csrc, inc.decode())):
+            h.update(open(os.path.join(csrc, inc.decode()), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel_key: str, source: str):
@@ -172,9 +180,9 @@ def main():
         mark("prefill_end")
         kvs.kvs_window_score(q, k, lse, cu_d, n, alpha, scores=S)
         mark("score_end")
-        kvs.kvs_topk_select(S, cu_d, n, alpha, kb, keep_off, keep_idx=keep)
-        mark("topk_end")
-        kvs.kvs_compact_paged(k, v, cu_d, keep, keep_off, k_eff, k_pool, v_pool, tbl)
+        # top-k and compaction in one launch (one workgroup per (head, block), each repeating
+        # the selection); kvs_topk_select and kvs_compact_paged are timed alone below as well
+        kvs.kvs_topk_compact(S, k, v, cu_d, n, alpha, kb, keep_off, k_pool, v_pool, tbl, keep_idx=keep)
         mark("compact_end")
 
     graph = pre_graph = None
@@ -244,6 +252,8 @@ def main():
     launches = {
         "prefill_attn_lse": lambda: kvs.kvs_prefill_attn_lse(q, k, v, cu_d, n, o=o, lse=lse),
         "window_score": lambda: kvs.kvs_window_score(q, k, lse, cu_d, n, alpha, scores=S),
+        "topk_compact": lambda: kvs.kvs_topk_compact(S, k, v, cu_d, n, alpha, kb, keep_off, k_pool, v_pool, tbl,
+                                                     keep_idx=keep),
         "topk_select": lambda: kvs.kvs_topk_select(S, cu_d, n, alpha, kb, keep_off, keep_idx=keep),
         "compact_paged": lambda: kvs.kvs_compact_paged(k, v, cu_d, keep, keep_off, k_eff, k_pool, v_pool, tbl),
     }
@@ -268,7 +278,9 @@ def main():
         pre_phase.append(span(rec, "prefill_begin", "compact_end"))
         dec_phase.append(rec["compact_end"][0].elapsed_time(de[-1]))
     avg_ms = {kname: float(np.mean(v)) for kname, v in dur.items()}
-    per_step_ms = {kname: avg_ms[kname] * (steps_dec if kname == "paged_decode" else 1) for kname in avg_ms}
+    # the step's kernels (the separate top-k and compaction calls are timed for reference only)
+    step_kernels = ("prefill_attn_lse", "window_score", "topk_compact", "paged_decode")
+    per_step_ms = {kname: avg_ms[kname] * (steps_dec if kname == "paged_decode" else 1) for kname in step_kernels}
 
     # ---- algorithmic work per launch
     P = sum(j + 1 for j in range(n - min(alpha, n), n))        # visited (window row, key) pairs
@@ -278,6 +290,8 @@ def main():
                              "prefill_attn.hip"),
         "window_score": ("hbm", n * hkv * d * 2 + min(alpha, n) * hq * (2 * d + 4) + 4 * hkv * n, "GB/s",
                          HBM_PEAK_GBS, "window_score.hip"),
+        "topk_compact": ("hbm", 4 * hkv * n + 4 * hkv * k_eff + 8 * k_eff * hkv * d, "GB/s", HBM_PEAK_GBS,
+                         "topk_select.hip"),
         "topk_select": ("hbm", 4 * hkv * n + 4 * hkv * k_eff, "GB/s", HBM_PEAK_GBS, "topk_select.hip"),
         "compact_paged": ("hbm", 8 * k_eff * hkv * d, "GB/s", HBM_PEAK_GBS, "compact_paged.hip"),
         "paged_decode": ("hbm", decode_bytes(mean_L, hq, hkv, d), "GB/s", HBM_PEAK_GBS, "paged_decode.hip"),
@@ -294,7 +308,9 @@ def main():
                             "timed_as": ("one decode call (decode kernel, plus the merge kernel when the "
                                          "context is split) inside the 500-step graph of the timed steps"
                                          if kname == "paged_decode" else
-                                         "graph of back-to-back launches of this kernel alone")}
+                                         "graph of back-to-back launches of this kernel alone"
+                                         + ("; a separate call, not in the timed step (which runs topk_compact)"
+                                            if kname in ("topk_select", "compact_paged") else ""))}
         if bound == "mfma":
             rooflines[kname]["counters"] = measured_mfma(kname, src)
     dominant = max(per_step_ms, key=per_step_ms.get)
@@ -893,7 +909,7 @@ def decode_32_layers(kvs, torch, wl, steps, fp8=False):
 def prefix_reuse(kvs, torch, wl, w, q, k, v, reps=10):
     """The bench layer when the first 2048 prompt tokens are found in the cache (block-hash
     match): their K/V come back from the blocks (gather) and only rows 2048-3999 are prefilled
-    against all 4000 keys, then window score, top-k and compaction as usual, captured as one
+    against all 4000 keys, then window score and top-k with compaction as usual, captured as one
     graph and timed with clock stamps between the launches (as the timed step's prompt phase)."""
     import numpy as np
     dev = torch.device("cuda:0")
@@ -916,7 +932,7 @@ def prefix_reuse(kvs, torch, wl, w, q, k, v, reps=10):
     ctbl = torch.arange(nblk_p, nblk_p + (-(-k_eff // 16)), dtype=torch.int32, device=dev).reshape(1, -1)
     counts = torch.tensor([P], dtype=torch.int32, device=dev)
     start = torch.tensor([0], dtype=torch.int32, device=dev)
-    marks = ["gather", "prefill_chunk", "window", "topk", "compact"]
+    marks = ["gather", "prefill_chunk", "window", "topk_compact"]
     o_c = torch.empty_like(q_rows)
     lse_c = torch.empty(hq, n - P, dtype=torch.float32, device=dev)
     S_c = torch.empty(hkv, n, dtype=torch.float32, device=dev)
@@ -931,10 +947,8 @@ def prefix_reuse(kvs, torch, wl, w, q, k, v, reps=10):
         kvs.kvs_probe_timestamp(stamps[2:3])
         kvs.kvs_window_score_chunk(q_rows, k_all, lse_c, cu_q, cu_full, n, alpha, scores=S_c)
         kvs.kvs_probe_timestamp(stamps[3:4])
-        kvs.kvs_topk_select(S_c, cu_full, n, alpha, kb, keep_off, keep_idx=keep_c)
+        kvs.kvs_topk_compact(S_c, k_all, v_all, cu_full, n, alpha, kb, keep_off, k_pool, v_pool, ctbl, keep_idx=keep_c)
         kvs.kvs_probe_timestamp(stamps[4:5])
-        kvs.kvs_compact_paged(k_all, v_all, cu_full, keep_c, keep_off, k_eff, k_pool, v_pool, ctbl)
-        kvs.kvs_probe_timestamp(stamps[5:6])
 
     # one captured graph, a clock stamp before each launch and after the last: each stage's span
     # is its kernel plus one in-graph launch boundary; the graph's start latency is outside
@@ -959,7 +973,7 @@ def prefix_reuse(kvs, torch, wl, w, q, k, v, reps=10):
     total = sum(per.values())
     flops = 2.0 * d * hq * sum(2 * (i + 1) for i in range(P, n))
     return {"workload": f"bench layer n={n} with the first {P} tokens reused from the cache: gather, prefill of "
-                        f"rows {P}-{n - 1} against {n} keys, window score, top-k, compaction",
+                        f"rows {P}-{n - 1} against {n} keys, window score, top-k with compaction (one launch)",
             "us": {m: round(v_, 2) for m, v_ in per.items()}, "total_us": round(total, 2),
             "prefill_chunk_TFLOPs": round(flops / (per["prefill_chunk"] * 1e-6) / 1e12, 1),
             "prompt_tok_s": round(n / (total * 1e-6), 1)}

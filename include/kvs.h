@@ -193,6 +193,27 @@ int kvs_compact_paged(const void* k_src, const void* v_src, const int32_t* cu_se
                       const int32_t* dst_slot_offset, void* stream);
 
 /*
+ * kvs_topk_compact - kvs_topk_select followed by kvs_compact_paged of the kept rows, in one
+ * launch (same results, bit for bit).
+ *   [KVS] Key techniques, 2: the k_l highest-scoring tokens of every head are kept, the rest
+ *   dropped; [PAG] "How paging works": the kept rows go to 16-token blocks through the
+ *   sequence's block table.
+ * Arguments as in the two calls: scores, cu_seqlens, max_seqlen, alpha, k_budget,
+ * keep_offsets and keep_idx (written, the kvs_topk_select layout) as in kvs_topk_select;
+ * k_src, v_src [total_tokens][hkv][d] bf16, pools, block tables and dst_slot_offset (NULL: 0)
+ * as in kvs_compact_paged with max_keep = min(k_budget, max_seqlen).  One workgroup per
+ * (prompt, KV head, block) repeats the selection and writes its block; when that would be
+ * more than 512 workgroups, or max_seqlen exceeds 16384, the two kernels run one after the
+ * other instead (a small batch gains a launch and the compaction's metadata round trips; a
+ * wide one would repeat the selection too often).
+ * Errors: as the two calls; source and pools must not overlap.
+ */
+int kvs_topk_compact(const float* scores, const void* k_src, const void* v_src, const int32_t* cu_seqlens,
+                     int num_seqs, int total_tokens, int max_seqlen, int hkv, int d, int alpha, int k_budget,
+                     const int32_t* keep_offsets, int32_t* keep_idx, void* k_pool, void* v_pool, int num_blocks,
+                     const int32_t* block_tables, int max_blocks, const int32_t* dst_slot_offset, void* stream);
+
+/*
  * kvs_paged_decode - attention of one new token per sequence over its paged cache.
  *   [PAG] "How paging works": the attention kernel follows the request's block table to
  *   read keys and values block by block.  [KVS] Key techniques, 2: PagedAttention does

@@ -1,13 +1,14 @@
 """KV-cache sparsification on MI355X: the prefill-and-compress path behind libkvs.
 
     kvs_prefill_attn_lse -> kvs_window_score -> kvs_topk_select -> kvs_compact_paged -> kvs_paged_decode
+    (kvs_topk_compact: the selection and the compaction in one launch)
 
 Every step runs in hand-written HIP kernels for gfx950 (libkvs.so, built in-tree with
 ``python kv_cache_sparsification_amd/build.py``).  This package only marshals torch tensors
 into the C ABI declared in include/kvs.h; importing it fails if the library is not built.
 """
 from ._lib import lib, KvsError, BLOCK_SIZE, LIB_PATH
-from .ops import (kvs_prefill_attn_lse, kvs_window_score, kvs_topk_select, kvs_compact_paged,
+from .ops import (kvs_prefill_attn_lse, kvs_window_score, kvs_topk_select, kvs_compact_paged, kvs_topk_compact,
                   kvs_paged_decode, kvs_paged_decode_workspace_size, kvs_copy_blocks, new_pools,
                   kvs_slot_init, kvs_decode_select_slot, kvs_paged_decode_scored,
                   kvs_paged_decode_scored_workspace_size, new_pools_fp8, kvs_compact_paged_fp8,
@@ -22,7 +23,7 @@ from .prefix_cache import BlockHashIndex, chained_block_keys
 
 __all__ = [
     "lib", "KvsError", "BLOCK_SIZE", "LIB_PATH",
-    "kvs_prefill_attn_lse", "kvs_window_score", "kvs_topk_select", "kvs_compact_paged",
+    "kvs_prefill_attn_lse", "kvs_window_score", "kvs_topk_select", "kvs_compact_paged", "kvs_topk_compact",
     "kvs_paged_decode", "kvs_paged_decode_workspace_size", "kvs_copy_blocks", "new_pools",
     "kvs_slot_init", "kvs_decode_select_slot", "kvs_paged_decode_scored", "kvs_paged_decode_scored_workspace_size",
     "new_pools_fp8", "kvs_compact_paged_fp8", "kvs_paged_decode_fp8", "kvs_copy_blocks_fp8",

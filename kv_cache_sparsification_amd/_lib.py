@@ -24,6 +24,8 @@ SIGNATURES = {
     "kvs_window_score": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                   _c_float, _vp, _vp]),
     "kvs_topk_select": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
+    "kvs_topk_compact": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp,
+                                  _vp, _vp, _vp, _c_int, _vp, _c_int, _vp, _vp]),
     "kvs_compact_paged": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _c_int, _vp, _vp, _c_int, _vp,
                                    _c_int, _vp, _vp]),
     "kvs_paged_decode_workspace_size": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),

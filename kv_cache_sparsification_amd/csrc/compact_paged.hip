@@ -10,10 +10,10 @@
 //
 // Pool layouts (bf16): K [num_blocks][hkv][16][d] (token rows), V [num_blocks][hkv][d][16]
 // (each channel's 16 slots contiguous, the operand order the decode kernel's P.V product
-// wants).  One wavefront fills one (destination block, head) pair: for K it moves whole
-// token rows with 16-byte lanes, for V each lane owns a pair of channels, reads them for all
-// 16 slots (every read instruction covers one contiguous source row) and writes two
-// contiguous 32-byte channel runs, so both sides stay coalesced with no LDS round trip.
+// wants).  One wavefront fills one (destination block, head) pair (copy_kv_block: K as whole
+// token rows with 16-byte lanes, V as two contiguous 32-byte channel runs per lane), so both
+// sides stay coalesced with no LDS round trip.
+#include "compact_block.h"
 #include "kvs_common.h"
 
 namespace kvs {
@@ -48,7 +48,6 @@ __global__ __launch_bounds__(kWavesPerWG * kWave) void compact_kernel(
   if (k_eff <= 0 || p0 >= off + k_eff || tbl_pos >= max_blocks) return;
   const int32_t* keep = keep_all ? nullptr : keep_idx + (size_t)hkv * ko0 + (size_t)g * k_eff;
   const int t0 = p0 - off;                         // rank written to slot 0 (may be negative)
-  const bool full = t0 >= 0 && t0 + kBlock <= k_eff;
   // Source rows of the 16 slots (wave-uniform addresses); -1 marks a slot this block does not fill.
   int srcrow[kBlock];
 #pragma unroll
@@ -61,61 +60,7 @@ __global__ __launch_bounds__(kWavesPerWG * kWave) void compact_kernel(
   for (int j = 0; j < kBlock; ++j)
     if (t0 + j < 0 || t0 + j >= k_eff) srcrow[j] = -1;
   if (blk < 0 || blk >= num_blocks) return;
-
-  // ---- K: row-major slots, 16-byte lanes
-  constexpr int kLanesPerRow = D * 2 / 16;         // 16 (d=128) or 8 (d=64)
-  constexpr int kRowsPerIter = kWave / kLanesPerRow;
-  constexpr int kIters = kBlock / kRowsPerIter;
-  uint16_t* kdst = k_pool + ((size_t)blk * hkv + g) * kBlock * D;
-  {
-    const int c = lane % kLanesPerRow;
-    u32x4 val[kIters];
-#pragma unroll
-    for (int it = 0; it < kIters; ++it) {
-      const int j = it * kRowsPerIter + lane / kLanesPerRow;
-      int src = srcrow[0];
-#pragma unroll
-      for (int jj = 1; jj < kBlock; ++jj) src = j == jj ? srcrow[jj] : src;   // select, no dynamic indexing
-      val[it] = u32x4{0u, 0u, 0u, 0u};
-      if (src >= 0) val[it] = *reinterpret_cast<const u32x4*>(k_src + ((size_t)(base + src) * hkv + g) * D + c * 8);
-    }
-#pragma unroll
-    for (int it = 0; it < kIters; ++it) {
-      const int j = it * kRowsPerIter + lane / kLanesPerRow;
-      if (t0 + j >= 0 && t0 + j < k_eff) *reinterpret_cast<u32x4*>(kdst + j * D + c * 8) = val[it];
-    }
-  }
-
-  // ---- V: channel-major slots; lane owns channels 2*lane and 2*lane + 1
-  constexpr int kPairs = D / 2;
-  if (lane >= kPairs) return;
-  uint16_t* vdst = v_pool + ((size_t)blk * hkv + g) * D * kBlock;
-  if (full) {
-    uint32_t pair[kBlock];
-#pragma unroll
-    for (int j = 0; j < kBlock; ++j)
-      pair[j] = *reinterpret_cast<const uint32_t*>(v_src + ((size_t)(base + srcrow[j]) * hkv + g) * D + 2 * lane);
-    u32x4 lo[2], hi[2];   // channel 2*lane (low halves) and 2*lane + 1 (high halves), 16 slots each
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      // slot 2q in the low half-word, slot 2q + 1 in the high one
-      lo[q / 4][q % 4] = (pair[2 * q] & 0xffffu) | (pair[2 * q + 1] << 16);
-      hi[q / 4][q % 4] = (pair[2 * q] >> 16) | (pair[2 * q + 1] & 0xffff0000u);
-    }
-    u32x4* d0 = reinterpret_cast<u32x4*>(vdst + (size_t)(2 * lane) * kBlock);
-    u32x4* d1 = reinterpret_cast<u32x4*>(vdst + (size_t)(2 * lane + 1) * kBlock);
-    d0[0] = lo[0]; d0[1] = lo[1];
-    d1[0] = hi[0]; d1[1] = hi[1];
-  } else {
-#pragma unroll
-    for (int j = 0; j < kBlock; ++j) {
-      const int src = srcrow[j];
-      if (src < 0) continue;
-      const uint32_t x = *reinterpret_cast<const uint32_t*>(v_src + ((size_t)(base + src) * hkv + g) * D + 2 * lane);
-      vdst[(size_t)(2 * lane) * kBlock + j] = (uint16_t)(x & 0xffffu);
-      vdst[(size_t)(2 * lane + 1) * kBlock + j] = (uint16_t)(x >> 16);
-    }
-  }
+  copy_kv_block<D>(k_src, v_src, base, hkv, g, srcrow, k_pool, v_pool, blk, lane);
 }
 
 // Gather: tokens 0..count-1 of a sequence read back through its block table into contiguous

@@ -110,6 +110,32 @@ def kvs_compact_paged(k_src, v_src, cu_seqlens, keep_idx, keep_offsets, max_keep
                                 _ptr(dst_slot_offset), _stream(stream)))
 
 
+def kvs_topk_compact(scores, k_src, v_src, cu_seqlens, max_seqlen: int, alpha: int, k_budget: int, keep_offsets,
+                     k_pool, v_pool, block_tables, keep_idx=None, total_keep: Optional[int] = None,
+                     dst_slot_offset=None, stream=None):
+    """kvs_topk_select then kvs_compact_paged of the kept rows, in one launch; returns keep_idx."""
+    _dev(scores, torch.float32, "scores"); _dev(cu_seqlens, torch.int32, "cu_seqlens")
+    _dev(keep_offsets, torch.int32, "keep_offsets")
+    _dev(k_src, torch.bfloat16, "k_src"); _dev(v_src, torch.bfloat16, "v_src")
+    _dev(k_pool, torch.bfloat16, "k_pool"); _dev(v_pool, torch.bfloat16, "v_pool")
+    _dev(block_tables, torch.int32, "block_tables")
+    if dst_slot_offset is not None:
+        _dev(dst_slot_offset, torch.int32, "dst_slot_offset")
+    hkv, T = scores.shape
+    if keep_idx is None:
+        if total_keep is None:
+            raise ValueError("total_keep (host value of keep_offsets[-1]) is needed to size keep_idx")
+        keep_idx = torch.empty(hkv * int(total_keep), device=scores.device, dtype=torch.int32)
+    _dev(keep_idx, torch.int32, "keep_idx")
+    d = k_src.shape[2]
+    check(lib.kvs_topk_compact(scores.data_ptr(), k_src.data_ptr(), v_src.data_ptr(), cu_seqlens.data_ptr(),
+                               cu_seqlens.numel() - 1, T, int(max_seqlen), hkv, d, int(alpha), int(k_budget),
+                               keep_offsets.data_ptr(), keep_idx.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                               k_pool.shape[0], block_tables.data_ptr(), block_tables.shape[1],
+                               _ptr(dst_slot_offset), _stream(stream)))
+    return keep_idx
+
+
 def kvs_paged_decode_workspace_size(batch: int, hq: int, hkv: int, d: int, max_ctx: int) -> int:
     return int(lib.kvs_paged_decode_workspace_size(batch, hq, hkv, d, max_ctx))
 

@@ -67,10 +67,8 @@ def prefill_compress_layer(q, k, v, cu_seqlens, lengths: Sequence[int], alpha: i
         for c in kept:
             keep_off.append(keep_off[-1] + c)
         keep_off_dev = torch.tensor(keep_off, dtype=torch.int32).to(dev)
-        keep_idx = ops.kvs_topk_select(scores, cu_seqlens, max_n, alpha, k_budget, keep_off_dev,
-                                       total_keep=keep_off[-1], stream=stream)
-        ops.kvs_compact_paged(k, v, cu_seqlens, keep_idx, keep_off_dev, max(kept), k_pool, v_pool, tbl_dev,
-                              stream=stream)
+        keep_idx = ops.kvs_topk_compact(scores, k, v, cu_seqlens, max_n, alpha, k_budget, keep_off_dev, k_pool,
+                                        v_pool, tbl_dev, total_keep=keep_off[-1], stream=stream)
     return dict(o=o, lse=lse, scores=scores, keep_idx=keep_idx, keep_offsets=keep_off_dev, kept=kept,
                 tables=tables, tables_dev=tbl_dev)
 
@@ -137,9 +135,8 @@ def prefill_compress_layer_chunked(q, k, v, cu_q, cu_k, q_lengths: Sequence[int]
         for c in kept:
             keep_off.append(keep_off[-1] + c)
         keep_off_dev = torch.tensor(keep_off, dtype=torch.int32).to(dev)
-        keep_idx = ops.kvs_topk_select(scores, cu_k, max_k, alpha, k_budget, keep_off_dev, total_keep=keep_off[-1],
-                                       stream=stream)
-        ops.kvs_compact_paged(k, v, cu_k, keep_idx, keep_off_dev, max(kept), k_pool, v_pool, tbl_dev, stream=stream)
+        keep_idx = ops.kvs_topk_compact(scores, k, v, cu_k, max_k, alpha, k_budget, keep_off_dev, k_pool, v_pool,
+                                        tbl_dev, total_keep=keep_off[-1], stream=stream)
     return dict(o=o, lse=lse, scores=scores, keep_idx=keep_idx, keep_offsets=keep_off_dev, kept=kept,
                 tables_dev=tbl_dev)
 
@@ -242,9 +239,7 @@ def prefill_compress_admission(cache, layer: int, seqs: Sequence, plans, q, k, v
         for c in kept:
             keep_off.append(keep_off[-1] + c)
         keep_off_dev = i32(keep_off)
-        keep_idx = ops.kvs_topk_select(scores, cu_k_dev, max_n, alpha, budget, keep_off_dev, total_keep=keep_off[-1],
-                                       stream=stream)
-        ops.kvs_compact_paged(k, v, cu_k_dev, keep_idx, keep_off_dev, max(kept), k_pool, v_pool, tbl_dev,
-                              stream=stream)
+        keep_idx = ops.kvs_topk_compact(scores, k, v, cu_k_dev, max_n, alpha, budget, keep_off_dev, k_pool, v_pool,
+                                        tbl_dev, total_keep=keep_off[-1], stream=stream)
     return dict(o=o, lse=lse, scores=scores, keep_idx=keep_idx, keep_offsets=keep_off_dev, kept=kept, first=first,
                 cu_q=cu_q, cu_k=cu_k, tables_dev=tbl_dev)

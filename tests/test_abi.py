@@ -47,6 +47,14 @@ def test_host_validation_rejects_before_launch():
     assert L.kvs_topk_select(fake, fake, 1, 10, 10, 2, 8, 4, fake, fake, None) == -1      # k < alpha
     assert b"alpha" in L.kvs_last_error()
     assert L.kvs_compact_paged(fake, fake, fake, 1, 2, 100, None, None, 8, fake, fake, 4, fake, 4, None, None) == -1
+    # fused selection and compaction: k < alpha, a bad head size, a NULL pool
+    tc = dict(scores=fake, k_src=fake, v_src=fake, cu=fake, num_seqs=1, total=10, max_seqlen=10, hkv=2, d=128,
+              alpha=8, k=16, koff=fake, keep=fake, kp=fake, vp=fake, nb=4, tbl=fake, max_blocks=4, dst=None,
+              stream=None)
+    assert L.kvs_topk_compact(*dict(tc, k=4).values()) == -1 and b"alpha" in L.kvs_last_error()
+    assert L.kvs_topk_compact(*dict(tc, d=96).values()) == -1 and b"bad shape" in L.kvs_last_error()
+    assert L.kvs_topk_compact(*dict(tc, kp=None).values()) == -1 and b"NULL" in L.kvs_last_error()
+    assert L.kvs_topk_compact(*dict(tc, num_seqs=0, total=0).values()) == 0     # nothing to do
     assert L.kvs_copy_blocks(fake, fake, 4, 2, 128, None, 3, None) == -1
     ws = L.kvs_paged_decode_workspace_size(1, 32, 8, 128, 30000)
     assert ws > 0

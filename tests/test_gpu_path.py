@@ -316,6 +316,67 @@ def test_decode_batch_splits_and_merge(d, hq, hkv, lens):
             assert_lse_close(lg[b], l_ref, what=f"decode lse b={b} append={append}")
 
 
+@pytest.mark.parametrize("lens,hkv,d,alpha,kb,offs,ties", [
+    ([4000], 8, 128, 32, 400, None, False),                    # the 8B layer's shape
+    ([300, 17, 1000, 5, 0, 64], 2, 64, 16, 64, [3, 0, 17, 9, 0, 15], False),   # ragged, keep-all, empty, offsets
+    ([900, 33], 4, 128, 32, 32, None, False),                   # the budget is the window
+    ([2000, 1500], 2, 128, 8, 300, [5, 16], True),              # many equal scores
+    ([16000], 1, 64, 32, 700, None, False),                     # the most candidates the fused form takes
+    ([600] * 20, 2, 128, 32, 512, None, False),                 # wide batch: the two kernels run instead
+    ([20000], 2, 64, 32, 700, None, False),                     # candidates beyond the LDS: two kernels
+    ([20000], 1, 64, 32, 17000, [7], False)])                   # kept list beyond the LDS: two kernels
+def test_topk_compact_matches_separate_calls(lens, hkv, d, alpha, kb, offs, ties):
+    """The fused selection-and-compaction call against kvs_topk_select followed by
+    kvs_compact_paged: the same kept indices and the same pools, bit for bit (pools poisoned
+    with NaN first, so a slot written by one and not the other shows)."""
+    _say(f"topk_compact lens={lens} hkv={hkv} d={d} alpha={alpha} k={kb} offs={offs} ties={ties}")
+    r = np.random.default_rng(sum(lens) + kb)
+    T = sum(lens)
+    S = r.random((hkv, T), dtype=np.float32)
+    if ties:
+        S = np.round(S * 8) / 8                  # 9 distinct values
+    kk = wl.f32_to_bf16_bits(r.standard_normal((T, hkv, d), dtype=np.float32))
+    vv = wl.f32_to_bf16_bits(r.standard_normal((T, hkv, d), dtype=np.float32))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    kept = [min(kb, n) for n in lens]
+    koff = np.concatenate([[0], np.cumsum(kept)]).astype(np.int32)
+    o = offs or [0] * len(lens)
+    nbs = [-(-(o[i] + kept[i]) // 16) for i in range(len(lens))]
+    nb = sum(nbs) + 3
+    perm = r.permutation(nb)
+    tbl = np.full((len(lens), max(max(nbs), 1)), -1, np.int32)
+    at = 0
+    for i, c in enumerate(nbs):
+        tbl[i, :c] = perm[at:at + c]
+        at += c
+    S_d, k_d, v_d = torch.from_numpy(S).cuda(), to_dev_bf16(kk), to_dev_bf16(vv)
+    cu_d, koff_d, tbl_d = i32(cu), i32(koff), i32(tbl)
+    off_d = i32(offs) if offs is not None else None
+    res = []
+    for fused in (False, True):
+        kp, vp = kvs.new_pools(nb, hkv, d)
+        kp.view(torch.int16).fill_(0x7FC0)
+        vp.view(torch.int16).fill_(0x7FC0)
+        if fused:
+            keep = kvs.kvs_topk_compact(S_d, k_d, v_d, cu_d, max(lens), alpha, kb, koff_d, kp, vp, tbl_d,
+                                        total_keep=int(koff[-1]), dst_slot_offset=off_d)
+        else:
+            keep = kvs.kvs_topk_select(S_d, cu_d, max(lens), alpha, kb, koff_d, total_keep=int(koff[-1]))
+            kvs.kvs_compact_paged(k_d, v_d, cu_d, keep, koff_d, max(kept), kp, vp, tbl_d, dst_slot_offset=off_d)
+        torch.cuda.synchronize()
+        res.append((keep.cpu().numpy(), bf16_bits(kp), bf16_bits(vp)))
+    for what, a, b in zip(("keep_idx", "K pool", "V pool"), res[0], res[1]):
+        np.testing.assert_array_equal(b, a, err_msg=f"{what}: fused against separate calls")
+    # and the kept sets are the oracle's (ties to the lower index)
+    for s_, n in enumerate(lens):
+        for g in range(hkv):
+            if n == 0:
+                continue
+            got = res[1][0][hkv * koff[s_] + g * kept[s_]: hkv * koff[s_] + (g + 1) * kept[s_]]
+            ref = oracle.select_keep(S[g, cu[s_]:cu[s_ + 1]].astype(np.float64), n, alpha, kb)
+            np.testing.assert_array_equal(got, ref, err_msg=f"keep prompt {s_} head {g}")
+
+
 def test_copy_blocks_for_copy_on_write():
     _say("copy_blocks")
     hkv, d, nb = 2, 128, 10

@@ -94,6 +94,16 @@ def run_full_path(w: wl.Workload, layer: int, check_decode_steps, decode_steps: 
     for g in range(w.hkv):
         np.testing.assert_array_equal(gk[:, g], kb[keep_g[g], g])
         np.testing.assert_array_equal(gv[:, g], vb[keep_g[g], g])
+    # the fused call (what the pipeline makes) leaves the same indices and pools
+    k_pool2, v_pool2 = kvs.new_pools(num_blocks, w.hkv, d)
+    k_pool2.view(torch.int16).fill_(0x7FC0)
+    v_pool2.view(torch.int16).fill_(0x7FC0)
+    keep2 = kvs.kvs_topk_compact(S, k, v, cu_d, n, alpha, k_budget, keep_off, k_pool2, v_pool2, i32(tbl),
+                                 total_keep=k_eff)
+    np.testing.assert_array_equal(keep2.cpu().numpy().reshape(w.hkv, k_eff), keep_g)
+    assert torch.equal(k_pool2.view(torch.int16), k_pool.view(torch.int16))
+    assert torch.equal(v_pool2.view(torch.int16), v_pool.view(torch.int16))
+    del k_pool2, v_pool2
 
     # ---- step 5: decode steps with append (write-then-attend)
     cache_k = [kf[keep_g[g], g] for g in range(w.hkv)]

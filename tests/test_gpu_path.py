@@ -218,9 +218,15 @@ def test_topk_exact_with_ties_and_budgets():
                 np.testing.assert_array_equal(seg[g], ref, err_msg=f"seq {s} head {g} alpha {alpha} k {kb}")
 
 
-def test_topk_threshold_bin_taken_whole():
-    """The kept candidates are exactly the members of one radix bin (the top 11 bits, or the top
-    22) above everything else: the search stops at that pass and must keep the same set."""
+@pytest.mark.parametrize("fused", [False, True])
+def test_topk_over_score_ranges(fused):
+XX
+    differing only in their low bits (one pass), a few distinct values, zeros beside tiny
+    positives, and the full spread of exponents (three passes); kept sets as the oracle's."""Scores over very different ranges: all equal, differing only in their low bits, a few
+    distinct values, zeros beside tiny positives, every exponent, and one binade (like the
+    bench layer's non-sink scores); kept sets as the oracle's, for both entry points."""The kept candidates are exactly the members of one narrow score range above everything
+    else, so a pass can find its threshold bin taken whole and stop early (after the first or
+    the second pass): the kept set must be the same as a full search's."""
     r = np.random.default_rng(31)
     for n, alpha, kb in ((300, 8, 40), (4000, 32, 400), (20000, 16, 700)):
         kk = kb - alpha

@@ -220,13 +220,37 @@ def test_topk_exact_with_ties_and_budgets():
 
 @pytest.mark.parametrize("fused", [False, True])
 def test_topk_over_score_ranges(fused):
-XX
-    differing only in their low bits (one pass), a few distinct values, zeros beside tiny
-    positives, and the full spread of exponents (three passes); kept sets as the oracle's."""Scores over very different ranges: all equal, differing only in their low bits, a few
+    """Scores over very different ranges: all equal, differing only in their low bits, a few
     distinct values, zeros beside tiny positives, every exponent, and one binade (like the
-    bench layer's non-sink scores); kept sets as the oracle's, for both entry points."""The kept candidates are exactly the members of one narrow score range above everything
-    else, so a pass can find its threshold bin taken whole and stop early (after the first or
-    the second pass): the kept set must be the same as a full search's."""
+    bench layer's non-sink scores); kept sets as the oracle's, for both entry points."""
+    r = np.random.default_rng(41)
+    n, alpha, kb, hkv = 3000, 16, 300, 6
+    S = np.empty((hkv, n), np.float32)
+    S[0] = 0.37                                                             # every score equal
+    S[1] = (np.uint32(0x3D000000) | r.integers(0, 1 << 9, n).astype(np.uint32)).view(np.float32)   # 9 low bits
+    S[2] = (r.integers(0, 5, n) * 0.125 + 1.0).astype(np.float32)           # five values
+    S[3] = np.where(r.random(n) < 0.5, 0.0, r.random(n) * 1e-30).astype(np.float32)   # zeros and tiny ones
+    S[4] = (2.0 ** r.uniform(-126, 6, n)).astype(np.float32)                # every exponent
+    S[5] = (0.05 * (1 + 0.1 * r.standard_normal(n))).astype(np.float32)     # one binade
+    _say(f"topk over score ranges, fused={fused}")
+    S_d = torch.from_numpy(S).cuda()
+    cu, off = i32([0, n]), i32([0, kb])
+    if fused:
+        k_src = torch.zeros(n, hkv, 64, device="cuda", dtype=torch.bfloat16)
+        kp, vp = kvs.new_pools(-(-kb // 16), hkv, 64)
+        tbl = i32([list(range(-(-kb // 16)))])
+        keep = kvs.kvs_topk_compact(S_d, k_src, k_src, cu, n, alpha, kb, off, kp, vp, tbl, total_keep=kb)
+    else:
+        keep = kvs.kvs_topk_select(S_d, cu, n, alpha, kb, off, total_keep=kb)
+    keep = keep.cpu().numpy().reshape(hkv, kb)
+    for g in range(hkv):
+        np.testing.assert_array_equal(keep[g], oracle.select_keep(S[g].astype(np.float64), n, alpha, kb),
+                                      err_msg=f"head {g}")
+
+
+def test_topk_threshold_bin_taken_whole():
+    """The kept candidates are exactly the members of one radix bin (the top 11 bits, or the top
+    22) above everything else: the search stops at that pass and must keep the same set."""
     r = np.random.default_rng(31)
     for n, alpha, kb in ((300, 8, 40), (4000, 32, 400), (20000, 16, 700)):
         kk = kb - alpha

@@ -81,10 +81,11 @@ def test_noalloc_decode_matches_the_workspace_decode(calls):
 
 
 def test_noalloc_rejects_shapes_beyond_the_scratch():
-    B, hq, hkv, d, max_ctx = 60, 32, 8, 128, 100000
+    # 9 sequences of 16000 tokens: 125 pieces of 8 blocks per (sequence, head), 17.9 MiB of partials
+    B, hq, hkv, d, max_ctx = 9, 32, 8, 128, 16000
     assert kvs.kvs_paged_decode_workspace_size(B, hq, hkv, d, max_ctx) > 16 << 20
     fake = 0x1000    # never dereferenced: the size check comes first
-    rc = kvs.lib.kvs_paged_decode_noalloc(fake, fake, fake, 10000, fake, 6250, fake, B, max_ctx, hq, hkv, d, 0.1,
+    rc = kvs.lib.kvs_paged_decode_noalloc(fake, fake, fake, 10000, fake, 1000, fake, B, max_ctx, hq, hkv, d, 0.1,
                                           None, None, fake, None, None)
     assert rc == kvs._lib.KVS_E_INVAL
     assert b"scratch" in kvs.lib.kvs_last_error()

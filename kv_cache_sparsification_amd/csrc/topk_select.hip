@@ -20,6 +20,10 @@
 // contiguous per-thread chunks keeps every score above T plus the first `ties` copies of T
 // (lowest index first), placing them with two block scans, and writes the window after them.
 // No sort, no device-wide traffic.
+//
+// The same selection also runs fused with the compaction of the kept rows ([PAG] "How paging
+// works": the rows go to 16-token blocks through the block table): one workgroup per
+// (prompt, KV head, destination block) repeats it and copies its block (topk_compact_kernel).
 #include "compact_block.h"
 #include "kvs_common.h"
 

@@ -367,19 +367,40 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void prefill_kernel(
 
   // ---- epilogue: O = acc / l, LSE = ln 2 * (m_ref + log2 l)
   const float l = half_sum(l_lane);   // sum of exp2(x - m_ref)
-  if (row >= 0) {   // rows before the prompt belong to no query (every row is < m)
-    const float inv = 1.f / l;
-    uint16_t* orow = o + ((size_t)(base + row) * hq + h) * D;
+  // O goes out through LDS: a lane holds half the channels of one row in 4-channel pieces, so
+  // stored directly every instruction would write 8 bytes into each of 32 rows; staged as
+  // row-major rows (stride D + 8, 16-byte aligned), 16 lanes write one row's 2D bytes as
+  // whole lines (bench layer: 134.5 us without any O store against 144 with the direct one).
+  // The tile buffers are free once every wavefront has passed the last product; two
+  // wavefronts' strips fit one buffer.
+  constexpr int OSTR = D + 8;
+  __syncthreads();
+  uint16_t* stage = (w < 2 ? ks0 : w < 4 ? ks1 : w < 6 ? ks2 : vs0) + (w & 1) * (kRowsPerWave * OSTR);
+  {
+    const float inv = 1.f / l;   // rows before the prompt (row < 0) are staged but never stored
 #pragma unroll
     for (int mt = 0; mt < MT2; ++mt)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        // acc_o[mt][4*i4 + 0..3] are channels mt*32 + 8*i4 + 4*half + 0..3
+        // acc_o[mt][4*i4 + 0..3] are channels mt*32 + 8*i4 + 4*half + 0..3 of row `col`
         u32x2 x;
         x[0] = pack_bf16x2(acc_o[mt][4 * i4 + 0] * inv, acc_o[mt][4 * i4 + 1] * inv);
         x[1] = pack_bf16x2(acc_o[mt][4 * i4 + 2] * inv, acc_o[mt][4 * i4 + 3] * inv);
-        *reinterpret_cast<u32x2*>(orow + mt * 32 + 8 * i4 + 4 * half) = x;
+        *reinterpret_cast<u32x2*>(&stage[col * OSTR + mt * 32 + 8 * i4 + 4 * half]) = x;
       }
+  }
+  __syncthreads();
+  {
+    constexpr int kChunks = D / 8;                  // 16-byte pieces of a row
+    constexpr int kRowsPerIt = kWave / kChunks;
+#pragma unroll
+    for (int it = 0; it < kRowsPerWave / kRowsPerIt; ++it) {
+      const int rr = it * kRowsPerIt + lane / kChunks, cc = lane % kChunks;
+      const u32x4 x = *reinterpret_cast<const u32x4*>(&stage[rr * OSTR + cc * 8]);
+      if (R + rr >= 0) *reinterpret_cast<u32x4*>(o + ((size_t)(base + R + rr) * hq + h) * D + cc * 8) = x;
+    }
+  }
+  if (row >= 0) {   // rows before the prompt belong to no query (every row is < m)
     if (half == 0) {
       const size_t li = (size_t)h * total_tokens + base + row;
       if (lse) lse[li] = (m_ref + log2f(l)) * kLn2;

@@ -242,6 +242,12 @@ def test_fp8_decode_long_context_batch():
     _decode_case("long context", 32, 8, 128, [3000, 2950, 3001, 2990], 3, seed=3, prompt_extra=200)
 
 
+def test_fp8_decode_long_contexts():
+    """Two sequences of 17000-20000 cached tokens: the long-context plan (equal pieces over
+    8-wavefront workgroups, the piece count chosen to fill the CUs)."""
+    _decode_case("long contexts", 32, 8, 128, [20000, 17001], 2, seed=9, prompt_extra=16)
+
+
 @pytest.mark.parametrize("hq,hkv,d,k_effs", [(16, 2, 64, [700, 5]), (16, 1, 64, [300, 2500]),
                                              (16, 1, 128, [1200, 7])])
 def test_fp8_decode_wide_groups(hq, hkv, d, k_effs):

@@ -313,7 +313,8 @@ def test_compaction_offsets_keep_all_and_partial_blocks():
                                            # and head, several rounds) and a mid-size split plan
                                            (128, 32, 8, list(range(400, 700, 15))),
                                            (128, 32, 8, list(range(250, 390, 7))),
-                                           (128, 32, 8, [3000 + 33 * i for i in range(4)])])
+                                           (128, 32, 8, [3000 + 33 * i for i in range(4)]),
+                                           (128, 32, 8, [16400, 16399, 17000, 16384])])   # the long-context plan
 def test_decode_batch_splits_and_merge(d, hq, hkv, lens):
     """Full-cache decode over several contexts, with and without append; long contexts split and merge."""
     _say(f"decode batch d={d} hq={hq} hkv={hkv} lens={lens}")

@@ -51,7 +51,7 @@ def parse():
                    help="only run a plain device copy of MIB mebibytes three times (reference for the "
                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
     p.add_argument("--decode-mode", choices=("graph", "loop"), default="graph",
-                   help="graph: the four prompt-side kernels replay as one captured HIP graph and the 500 "
+                   help="graph: the prompt-side kernels replay as one captured HIP graph and the 500 "
                         "decode steps as another (the launch mode of a serving loop); loop: one host launch "
                         "per kernel")
     p.add_argument("--sections", default="all",
@@ -192,7 +192,7 @@ def main():
     stamp_hist = torch.zeros(max(args.steps, 1), 4, dtype=torch.int64, device=dev)
     if args.decode_mode == "graph":
         # Both phases captured as HIP graphs, the way a serving loop launches a fixed sequence:
-        # the four prompt-side kernels as one graph, the 500 decode steps as another.
+        # the prompt-side kernels as one graph, the 500 decode steps as another.
         # Compaction first so the captured steps see a filled cache; capture records launches.
         prefill_compress(lambda key: None)
         torch.cuda.synchronize()

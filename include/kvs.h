@@ -203,9 +203,9 @@ int kvs_compact_paged(const void* k_src, const void* v_src, const int32_t* cu_se
  * k_src, v_src [total_tokens][hkv][d] bf16, pools, block tables and dst_slot_offset (NULL: 0)
  * as in kvs_compact_paged with max_keep = min(k_budget, max_seqlen).  One workgroup per
  * (prompt, KV head, block) repeats the selection and writes its block; when that would be
- * more than 512 workgroups, or max_seqlen exceeds 16384, the two kernels run one after the
- * other instead (a small batch gains a launch and the compaction's metadata round trips; a
- * wide one would repeat the selection too often).
+ * more than 256 workgroups (one per CU), or max_seqlen exceeds 16384, the two kernels run one
+ * after the other instead (a small batch gains a launch and the compaction's metadata round
+ * trips; a wide one would run the repeated selections one after another).
  * Errors: as the two calls; source and pools must not overlap.
  */
 int kvs_topk_compact(const float* scores, const void* k_src, const void* v_src, const int32_t* cu_seqlens,

@@ -35,7 +35,9 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kLdsCap = 16384;   // candidates held in LDS (64 KB); longer prompts read L2 each pass
 constexpr int kCopies = 4;       // copies of every histogram bin: lane l counts into copy l % 4
 constexpr int kKeptCap = 2 * 2048 * kCopies;   // kept indices the fused kernel holds in the histograms' LDS
-constexpr long long kFusedMaxWGs = 512;          // (prompt, head, block) workgroups of a fused launch at most
+// (prompt, head, block) workgroups of a fused launch at most: one per CU (a 1024-thread workgroup
+// of this kernel's registers fits a CU once), so the repeated selections run side by side
+constexpr long long kFusedMaxWGs = 256;
 
 // Inclusive scan across the 64 lanes with DPP moves (no LDS): prefix sums within rows of 16
 // lanes by shifts of 1, 2, 4 and 8, then row 0's total into rows 1 and 3 (row_bcast:15) and
@@ -372,8 +374,9 @@ extern "C" int kvs_topk_compact(const float* scores, const void* k_src, const vo
   // on as many CUs as there are blocks, one round trip after the selection.  On the 8B layer
   // (8 heads, k = 400: 200 workgroups) 10.2 us against 11.4 for the two kernels; one workgroup
   // per 16, 8, 4 or 2 blocks took 12.5, 11.0, 10.5 and 10.2 us, the copy being bound by the
-  // bytes each CU moves.  Wider launches would repeat the selection too often and candidates
-  // beyond the LDS would be re-read by every replica: there the two kernels run instead.
+  // bytes each CU moves.  Wider launches would run the repeated selections one generation
+  // after another, and candidates beyond the LDS would be re-read by every replica: there the
+  // two kernels run instead.
   const int blocks = (max_keep + kBlock - 1) / kBlock + (dst_slot_offset ? 1 : 0);
   if (max_keep > kKeptCap || max_seqlen > kLdsCap || (long long)hkv * num_seqs * blocks > kFusedMaxWGs) {
     const int rc = kvs_topk_select(scores, cu_seqlens, num_seqs, total_tokens, max_seqlen, hkv, alpha, k_budget,

@@ -1,6 +1,7 @@
 """A multi-layer decode step captured as one HIP graph (next row f4) gives the eager results on
 every replay, with the program's own eager work and synchronisations between replays; the
-eager results themselves match the fp64 oracle.
+eager results themselves match the fp64 oracle.  The prompt-side chain the bench captures
+(prefill, window score, top-k fused with compaction) replays bit for bit as well.
 
 Three layers of different shapes (a full layer of ragged contexts, a compressed layer, an
 8-bit compressed layer) and four batched decode steps with append per replay.  Appends are
@@ -158,3 +159,62 @@ def test_clock_stamps_time_the_work_between_them():
         assert t1 > t0 > 0
         assert 0.9 * ev_ms <= span_ms <= 1.01 * ev_ms + 0.005
     assert int(sink.abs().sum()) == 0       # the zero buffer folds to 0, never the probe's key
+
+
+def test_prompt_side_graph_replays_match_eager():
+    """The prompt-side chain the bench captures (prefill with LSE, window score, top-k fused with
+    compaction into blocks) replayed as one graph, with eager work and synchronisations between
+    replays: outputs, scores, kept indices and pools bit for bit as the eager launches left them."""
+    w = wl.WORKLOADS[2]
+    n, hq, hkv, d, alpha, kb = 2000, w.hq, w.hkv, w.d, w.alpha, w.budgets[0]
+    _say(f"prompt-side graph: n={n} hq={hq} hkv={hkv} d={d} alpha={alpha} k={kb}")
+    qb, kbits, vb, cu = wl.prefill_batch(w, 0, [n])
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+    q, k, v, cu_d = up(qb), up(kbits), up(vb), i32(cu)
+    o = torch.empty_like(q)
+    lse = torch.empty(hq, n, dtype=torch.float32, device="cuda")
+    S = torch.empty(hkv, n, dtype=torch.float32, device="cuda")
+    keep = torch.empty(hkv * kb, dtype=torch.int32, device="cuda")
+    koff = i32([0, kb])
+    nblk = -(-kb // 16)
+    k_pool, v_pool = kvs.new_pools(nblk + 3, hkv, d)
+    tbl = i32([list(np.random.default_rng(7).permutation(nblk + 3)[:nblk])])
+
+    def chain():
+        kvs.kvs_prefill_attn_lse(q, k, v, cu_d, n, o=o, lse=lse)
+        kvs.kvs_window_score(q, k, lse, cu_d, n, alpha, scores=S)
+        kvs.kvs_topk_compact(S, k, v, cu_d, n, alpha, kb, koff, k_pool, v_pool, tbl, keep_idx=keep)
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return [t.clone() for t in (o.view(torch.int16), lse, S, keep, k_pool.view(torch.int16),
+                                    v_pool.view(torch.int16))]
+
+    k_pool.view(torch.int16).fill_(0x7FC0)          # blocks the table does not name stay as filled
+    v_pool.view(torch.int16).fill_(0x7FC0)
+    chain()
+    eager = snapshot()
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        chain()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        chain()
+    for rep in range(3):
+        for t in (o, lse, S):                       # eager work between replays: clobber the outputs
+            t.view(torch.int32 if t.dtype == torch.float32 else torch.int16).fill_(-1)
+        keep.fill_(-1)
+        k_pool.view(torch.int16).fill_(0x7FC0)
+        v_pool.view(torch.int16).fill_(0x7FC0)
+        torch.cuda.synchronize()
+        graph.replay()
+        got = snapshot()
+        for name, a, b in zip(("O", "LSE", "S", "keep", "K pool", "V pool"), eager, got):
+            assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager run"

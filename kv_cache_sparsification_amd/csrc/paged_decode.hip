@@ -547,16 +547,15 @@ __global__ __launch_bounds__(W * kWave) void decode_kernel(
 
 // Merge of the split partials.  Each thread folds its output channel over the splits 16 at a
 // time, issuing all loads of a chunk (its channel plus the (max, sum) pair, shared with its
-// neighbours through L1) before using any: one memory round trip per 16 splits (kOne: the
-// caller knows there are at most 16, and the fold is a single straight pass).  The loads
+// neighbours through L1) before using any: one memory round trip per C splits (kOne: the
+// caller knows there are at most C, and the fold is a single straight pass).  The loads
 // cover every split the launch has (a bound known on the host), so they do not wait for the
 // context length; the splits past the sequence's last non-empty one (`used`) hold stale data
 // and are masked out afterwards.
 // Returns the running max M (log2 units), the sum l against it and the output numerator.
-template <int D, bool kOne = false>
+template <int D, bool kOne = false, int C = 16>
 __device__ __forceinline__ void merge_partials(const float* __restrict__ part, int splits, int used, int dd, float& M,
                                                float& l, float& acc) {
-  constexpr int C = 16;
   M = -INFINITY;
   l = 0.f;
   acc = 0.f;
@@ -592,7 +591,7 @@ __device__ __forceinline__ void merge_partials(const float* __restrict__ part, i
   }
 }
 
-template <int D>
+template <int D, int C>
 __global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict__ ws,
                                                          const int32_t* __restrict__ ctx_lens, int hq, int hkv,
                                                          int max_blocks, int splits, int bps,
@@ -604,23 +603,22 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict
   {
     float M, l, acc;
     const float* part = ws + ((size_t)b * hq + h) * splits * (D + 2);
-    if (splits <= 16)   // grid-uniform: one straight pass (7.40 against 7.50 us per batch-1 step)
-      merge_partials<D, true>(part, splits, used, dd, M, l, acc);
+    if (splits <= C)   // grid-uniform: one straight pass
+      merge_partials<D, true, C>(part, splits, used, dd, M, l, acc);
     else
-      merge_partials<D>(part, splits, used, dd, M, l, acc);
+      merge_partials<D, false, C>(part, splits, used, dd, M, l, acc);
     if (used <= 1) return;                    // written directly by the decode kernel
     o[((size_t)b * hq + h) * D + dd] = (uint16_t)f32_to_bf16_bits(acc / l);
     if (lse_out && dd == 0) lse_out[(size_t)b * hq + h] = (M + log2f(l)) * kLn2;
   }
 }
 
-// The merge of two (query head, channel) outputs at once, all loads of a chunk of 16 splits for
+// The merge of two (query head, channel) outputs at once, all loads of a chunk of C splits for
 // both issued before either is folded (one memory round trip per chunk for the pair).
-template <int D>
+template <int D, int C = 16>
 __device__ __forceinline__ void merge_partials_pair(const float* __restrict__ part0, const float* __restrict__ part1,
                                                     bool has1, int splits, int used, int dd0, int dd1, float (&M)[2],
                                                     float (&l)[2], float (&acc)[2]) {
-  constexpr int C = 16;
   for (int k = 0; k < 2; ++k) {
     M[k] = -INFINITY;
     l[k] = 0.f;
@@ -676,7 +674,7 @@ __device__ __forceinline__ void merge_partials_pair(const float* __restrict__ pa
 // registers, they are fetched at the start, in the same round trip as the partials and the
 // context length, and the choice is made from the registers; otherwise the slots are read after
 // the merge.  Either way every slot is updated and chosen by the same arithmetic.
-template <int D>
+template <int D, int C>
 __global__ __launch_bounds__(kSelectThreads) void decode_merge_score_kernel(
     const float* __restrict__ ws, const float* __restrict__ logits, int logit_stride,
     const int32_t* __restrict__ ctx_lens, int hq, int hkv, int max_blocks, int splits, int bps,
@@ -713,7 +711,7 @@ __global__ __launch_bounds__(kSelectThreads) void decode_merge_score_kernel(
     const int c0 = e / D, dd0 = e % D, c1 = has1 ? e1 / D : c0, dd1 = has1 ? e1 % D : dd0;
     const int h0 = g * G + c0, h1 = g * G + c1;
     float M[2], l[2], acc[2];
-    merge_partials_pair<D>(ws + ((size_t)b * hq + h0) * splits * (D + 2), ws + ((size_t)b * hq + h1) * splits * (D + 2),
+    merge_partials_pair<D, C>(ws + ((size_t)b * hq + h0) * splits * (D + 2), ws + ((size_t)b * hq + h1) * splits * (D + 2),
                            has1, splits, used, dd0, dd1, M, l, acc);
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
@@ -768,6 +766,31 @@ extern "C" size_t kvs_paged_decode_workspace_size(int batch, int hq, int hkv, in
   const int splits = p.splits > p8.splits ? p.splits : p8.splits;
   if (splits <= 1) return 0;
   return (size_t)batch * hq * splits * (d + 2) * sizeof(float);
+}
+
+// Splits fetched per round trip by the merge kernels: the fewest of 4, 8, 12 or 16 that cover
+// the launch's split count, so that a short split list issues no loads for splits it does not
+// have (16 per round, and more than one round, past 16 splits).
+static int merge_width(int splits) { return splits <= 4 ? 4 : splits <= 8 ? 8 : splits <= 12 ? 12 : 16; }
+
+template <int D>
+static void launch_merge(int cw, int batch, hipStream_t st, const float* ws, const int32_t* ctx_lens, int hq, int hkv,
+                         int max_blocks, int splits, int bps, uint16_t* o, float* lse) {
+  auto k = cw == 4 ? decode_merge_kernel<D, 4> : cw == 8 ? decode_merge_kernel<D, 8>
+           : cw == 12 ? decode_merge_kernel<D, 12> : decode_merge_kernel<D, 16>;
+  hipLaunchKernelGGL(k, dim3(hq, batch), dim3(D), 0, st, ws, ctx_lens, hq, hkv, max_blocks, splits, bps, o, lse);
+}
+
+template <int D>
+static void launch_merge_score(int cw, int batch, hipStream_t st, const float* ws, const float* logits, int max_ctx,
+                               const int32_t* ctx_lens, int hq, int hkv, int max_blocks, int splits, int bps,
+                               uint16_t* o, float* lse, float* slot_scores, int slot_stride, int32_t* slot_pos,
+                               int cap, int alpha, const int32_t* next_pos, int32_t* next_dst) {
+  auto k = cw == 4 ? decode_merge_score_kernel<D, 4> : cw == 8 ? decode_merge_score_kernel<D, 8>
+           : cw == 12 ? decode_merge_score_kernel<D, 12> : decode_merge_score_kernel<D, 16>;
+  hipLaunchKernelGGL(k, dim3(hkv, batch), dim3(kSelectThreads), 0, st, ws, logits, max_ctx, ctx_lens, hq, hkv,
+                     max_blocks, splits, bps, o, lse, slot_scores, slot_stride, slot_pos, cap, alpha, next_pos,
+                     next_dst);
 }
 
 template <int D, int W, int NB, bool F8>
@@ -877,11 +900,9 @@ static int run_decode(const char* name, const void* q, void* k_pool, void* v_poo
   int rc = launch_status(name);
   if (rc != KVS_OK || p.splits == 1) return rc;
   if (d == 128)
-    hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(hq, batch), dim3(128), 0, st, ws, ctx_lens, hq, hkv, max_blocks,
-                       p.splits, p.bps, oo, lse_opt);
+    launch_merge<128>(merge_width(p.splits), batch, st, ws, ctx_lens, hq, hkv, max_blocks, p.splits, p.bps, oo, lse_opt);
   else
-    hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(hq, batch), dim3(64), 0, st, ws, ctx_lens, hq, hkv, max_blocks,
-                       p.splits, p.bps, oo, lse_opt);
+    launch_merge<64>(merge_width(p.splits), batch, st, ws, ctx_lens, hq, hkv, max_blocks, p.splits, p.bps, oo, lse_opt);
   return launch_status(name);
 }
 
@@ -1030,14 +1051,13 @@ static int run_scored(const char* name, const void* q, void* k_pool, void* v_poo
   }
   int rc = launch_status(name);
   if (rc != KVS_OK) return rc;
+  const int cw = merge_width(p.splits);
   if (d == 128)
-    hipLaunchKernelGGL(decode_merge_score_kernel<128>, dim3(hkv, batch), dim3(kSelectThreads), 0, st, ws, logits,
-                       max_ctx, ctx_lens, hq, hkv, max_blocks, p.splits, p.bps, oo, lse_opt, slot_scores, slot_stride,
-                       slot_pos, cap, alpha, next_pos, next_dst);
+    launch_merge_score<128>(cw, batch, st, ws, logits, max_ctx, ctx_lens, hq, hkv, max_blocks, p.splits, p.bps, oo,
+                            lse_opt, slot_scores, slot_stride, slot_pos, cap, alpha, next_pos, next_dst);
   else
-    hipLaunchKernelGGL(decode_merge_score_kernel<64>, dim3(hkv, batch), dim3(kSelectThreads), 0, st, ws, logits,
-                       max_ctx, ctx_lens, hq, hkv, max_blocks, p.splits, p.bps, oo, lse_opt, slot_scores, slot_stride,
-                       slot_pos, cap, alpha, next_pos, next_dst);
+    launch_merge_score<64>(cw, batch, st, ws, logits, max_ctx, ctx_lens, hq, hkv, max_blocks, p.splits, p.bps, oo,
+                           lse_opt, slot_scores, slot_stride, slot_pos, cap, alpha, next_pos, next_dst);
   return launch_status(name);
 }
 

@@ -121,10 +121,12 @@ def test_eviction_wide_groups(hq, hkv, d):
     assert c.n == c.cap
 
 
-def test_eviction_budget_beyond_register_slots():
-    """A budget of 600 slots: more than the merge-and-score kernel keeps in registers (512 per
-    workgroup), so the slots are read after the merge and the choice made from memory."""
-    w = dataclasses.replace(wl.WORKLOADS[1], hq=8, hkv=2, d=64, alpha=16, budgets=(600,), fixed_len=700,
+@pytest.mark.parametrize("budget,n,d", [(600, 700, 64), (1100, 1200, 128)])
+def test_eviction_budget_beyond_register_slots(budget, n, d):
+    """Budgets of 600 and 1100 slots: more than the merge-and-score kernel keeps in registers
+    (512 per workgroup), so the slots are read after the merge and the choice made from memory;
+    at 1100 slots the decode has more than 16 splits, which the merge folds in two rounds."""
+    w = dataclasses.replace(wl.WORKLOADS[1], hq=8, hkv=2, d=d, alpha=16, budgets=(budget,), fixed_len=n,
                             decode_steps=12)
     c = _run(w, steps=12, check_every=4)
     assert c.n == c.cap

@@ -357,6 +357,31 @@ def test_decode_batch_splits_and_merge(d, hq, hkv, lens):
             assert_lse_close(lg[b], l_ref, what=f"decode lse b={b} append={append}")
 
 
+def _contexts_by_split_count(batch, hq, hkv, d, wanted, limit):
+    """For each wanted split count, the shortest context (up to limit) whose launch plan has it,
+    read back through the workspace size (batch * hq * splits * (d + 2) fp32 partials)."""
+    found = {}
+    for L in range(1, limit + 1):
+        ws = kvs.kvs_paged_decode_workspace_size(batch, hq, hkv, d, L)
+        s = ws // (batch * hq * (d + 2) * 4) if ws else 1
+        if s in wanted and s not in found:
+            found[s] = L
+    return found
+
+
+@pytest.mark.parametrize("d,hq,hkv", [(128, 32, 8), (64, 16, 2)])
+def test_decode_merge_fetch_widths(d, hq, hkv):
+    """The merge kernel fetches 4, 8, 12 or 16 splits per round trip, the fewest covering the
+    launch's split count, and loops past 16: contexts at both sides of every width's edge."""
+    wanted = {2, 3, 4, 5, 8, 9, 12, 13, 16, 17, 33}
+    found = _contexts_by_split_count(1, hq, hkv, d, wanted, 6000)
+    _say(f"merge widths d={d}: split count -> context {sorted(found.items())}")
+    assert {4, 5, 8, 9, 12, 13, 16, 17} <= set(found), found
+    for s, L in sorted(found.items()):
+        test_decode_batch_splits_and_merge(d, hq, hkv, [L])
+        test_decode_batch_splits_and_merge(d, hq, hkv, [L, max(1, L // 3)])   # a shorter second context
+
+
 @pytest.mark.parametrize("lens,hkv,d,alpha,kb,offs,ties", [
     ([4000], 8, 128, 32, 400, None, False),                    # the 8B layer's shape
     ([300, 17, 1000, 5, 0, 64], 2, 64, 16, 64, [3, 0, 17, 9, 0, 15], False),   # ragged, keep-all, empty, offsets
